@@ -1,0 +1,542 @@
+"""Pins for the oracle: checks against facts the pages and the mathematics fix,
+not against the oracle itself.
+
+* golden fixtures (tests/golden), each citing the page item it restates;
+* hand-worked folds with the arithmetic written out in the fixture;
+* closed forms (one-hot rank-1 fold), special cases that reduce to a textbook
+  formula (the one-entry router route is dense LoRA, checked through the merged
+  weight ``scale * B @ A``), and invariants (B = 0, linearity in the scale,
+  grouped == gather on permuted rows, window splits, skip rules);
+* mutation checks: plausible mistakes planted in copies of the oracle must each
+  fail at least one of these pins.
+"""
+from __future__ import annotations
+
+import json
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from tests.common import OracleView, golden_json, golden_lines
+from workloads import make_gather_case, make_grouped_case
+
+# ---------------------------------------------------------------------------
+# host integer functions
+# ---------------------------------------------------------------------------
+
+
+def test_route_truth_table():
+    for line in golden_lines("route_truth_table.txt"):
+        slot, active, has, want = line.split()
+        assert oracle.resolve_moe_lora_route(int(slot), int(active), bool(int(has))) == want, line
+
+
+def test_ensure_decode_route_servable():
+    oracle.ensure_decode_route_servable(oracle.FOLD)
+    oracle.ensure_decode_route_servable(oracle.SKIP)
+    with pytest.raises(oracle.RefuseError, match="one adapter per batch"):
+        oracle.ensure_decode_route_servable(oracle.REFUSE)
+
+
+def test_row_adapter_host_golden():
+    for line in golden_lines("row_adapter_host.txt"):
+        c = json.loads(line)
+        assert oracle.build_moe_row_adapter_host(c["cu"], c["slots"]) == c["expect"], line
+
+
+def test_row_adapter_decode_golden():
+    for line in golden_lines("row_adapter_decode.txt"):
+        c = json.loads(line)
+        got = oracle.build_moe_row_adapter_decode(c["slots"], c["padded_n"], c["active"], c["has"])
+        assert got == c["expect"], line
+
+
+def test_pack_golden():
+    for line in golden_lines("pack_expert_tables.txt"):
+        c = json.loads(line)
+        got = oracle.pack_expert_tables([tuple(e) for e in c["entries"]])
+        if c["expect"] is None:
+            assert got is None
+            continue
+        a, b, s, n = got
+        assert (a, b, s, n) == (c["expect"]["a"], c["expect"]["b"], c["expect"]["s"],
+                                c["expect"]["n"]), line
+
+
+def test_pack_rejects_bad_ids():
+    with pytest.raises(ValueError):
+        oracle.pack_expert_tables([(-1, 1, 2, 1.0)])
+    with pytest.raises(ValueError):
+        oracle.pack_expert_tables([(oracle.MAX_EXPERT_ID + 1, 1, 2, 1.0)])
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 40), st.integers(0, 2**64 - 1),
+                          st.integers(0, 2**64 - 1), st.floats(-4, 4, width=32)),
+                min_size=1, max_size=30))
+def test_pack_properties(entries):
+    a, b, s, n = oracle.pack_expert_tables(entries)
+    assert n == max(e for e, *_ in entries) + 1
+    assert len(a) == len(b) == len(s) == n
+    last = {}
+    for e, aa, bb, sc in entries:
+        last[e] = (aa, bb, sc)
+    for i in range(n):
+        assert (a[i], b[i], s[i]) == last.get(i, (0, 0, 0.0))
+
+
+def test_windows_and_wc_golden():
+    for line in golden_lines("windows.txt"):
+        c = json.loads(line)
+        if "wc" in c:
+            off, end, mt = c["wc"]
+            assert oracle.grouped_down_wc(off, end, mt) == c["expect"], line
+        elif c["expect"] == "error":
+            with pytest.raises(ValueError):
+                oracle.grouped_down_windows(c["total"], c["cap"])
+        else:
+            got = oracle.grouped_down_windows(c["total"], c["cap"])
+            assert [list(w) for w in got] == c["expect"], line
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.integers(0, 5000), st.integers(1, 700))
+def test_windows_cover_exactly(total, cap):
+    w = oracle.grouped_down_windows(total, cap)
+    covered = []
+    for s, e in w:
+        assert 0 < e - s <= cap
+        covered.extend(range(s, e))
+    assert covered == list(range(total))
+    # greedy: every window but the last is full
+    assert all(e - s == cap for s, e in w[:-1])
+
+
+def test_row_token():
+    assert oracle.gather_row_token(0, 8) == 0
+    assert oracle.gather_row_token(7, 8) == 0
+    assert oracle.gather_row_token(8, 8) == 1
+    assert oracle.gather_row_token(639, 8) == 79
+    assert oracle.gather_row_token(5, 1) == 5
+
+
+# ---------------------------------------------------------------------------
+# fold pins, written against a pluggable implementation so the mutation test
+# can run them on mistaken copies of the oracle
+# ---------------------------------------------------------------------------
+
+
+def _hand():
+    g = golden_json("fold_hand.json")
+    x = np.array(g["x"], dtype=np.float64)
+    mats = {}
+    for name, m in g["A"].items():
+        mats[100 + int(name)] = np.array(m, dtype=np.float64)
+    for name, m in g["B"].items():
+        mats[200 + int(name)] = np.array(m, dtype=np.float64)
+    entries = []
+    for e, a, b, s in g["entries"]:
+        entries.append((e, 0 if a is None else 100 + int(a[1:]),
+                        0 if b is None else 200 + int(b[1:]), s))
+    a_t, b_t, s_t, _ = oracle.pack_expert_tables(entries)
+    return g, x, mats, a_t, b_t, s_t, np.array(g["base"], dtype=np.float64)
+
+
+def pin_gather_hand(gather):
+    g, x, mats, a_t, b_t, s_t, base = _hand()
+    for c in g["gather"]:
+        got = gather(x, a_t, b_t, s_t, mats, base, c["indices"], c["row_adapter"], g["top_k"])
+        if not np.array_equal(got, np.array(c["expect"], dtype=np.float64)):
+            return False
+    return True
+
+
+def pin_grouped_hand(grouped):
+    g, x, mats, a_t, b_t, s_t, base = _hand()
+    for c in g["grouped"]:
+        lo, hi = c["window"]
+        got = grouped(x, a_t, b_t, s_t, mats, base, c["expert_offsets"], c["sorted_ids"],
+                      c["row_adapter"], g["top_k"], lo, hi)
+        if not np.array_equal(got, np.array(c["expect"], dtype=np.float64)):
+            return False
+    return True
+
+
+def _small_gather(seed=11, **kw):
+    args = dict(n_seq=6, padded_n=8, top_k=3, n_route=7, k_in=5, n_out=4, max_rank=2,
+                dtype="f32", n_adapted=5, skip_seqs=1)
+    args.update(kw)
+    return OracleView(make_gather_case(seed, **args))
+
+
+def pin_gather_b_zero(gather):
+    v = _small_gather()
+    mats = {k: (np.zeros_like(m) if m.shape == (4, 2) else m) for k, m in v.mats.items()}
+    base = np.random.default_rng(0).standard_normal((v.case.n_rows, 4))
+    got = gather(v.x, v.a_table, v.b_table, v.scale_table, mats, base, v.case.indices,
+                 v.row_adapter, v.case.top_k)
+    return bool(np.all(got == base))
+
+
+def pin_gather_rank1_onehot(gather):
+    """One-hot token rows and rank 1: the delta of a row with token t, expert e
+    and x[t] = unit vector i is scale_e * A_e[0, i] * B_e[:, 0]."""
+    rng = np.random.default_rng(5)
+    top_k, n_tok, k_in, n_out, n_exp = 2, 4, 6, 3, 3
+    x = np.zeros((n_tok, k_in))
+    hot = [4, 0, 2, 5]
+    for t, i in enumerate(hot):
+        x[t, i] = 1.0
+    mats, entries = {}, []
+    for e in range(n_exp):
+        mats[10 + e] = rng.standard_normal((1, k_in))
+        mats[20 + e] = rng.standard_normal((n_out, 1))
+        entries.append((e, 10 + e, 20 + e, float(e + 1) * 0.75))
+    a_t, b_t, s_t, _ = oracle.pack_expert_tables(entries)
+    idx = [0, 2, 1, 1, 2, 0, 0, 1]
+    base = np.zeros((len(idx), n_out))
+    got = gather(x, a_t, b_t, s_t, mats, base, idx, [1] * n_tok, top_k)
+    for row, e in enumerate(idx):
+        t = row // top_k
+        want = s_t[e] * mats[10 + e][0, hot[t]] * mats[20 + e][:, 0]
+        if not np.allclose(got[row], want, rtol=1e-14, atol=0.0):
+            return False
+    return True
+
+
+def pin_gather_scale_linear(gather):
+    """Doubling every scale doubles every delta exactly (base 0)."""
+    v = _small_gather(seed=12)
+    base = np.zeros((v.case.n_rows, 4))
+    d1 = gather(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base, v.case.indices,
+                v.row_adapter, v.case.top_k)
+    s2 = [2.0 * s for s in v.scale_table]
+    d2 = gather(v.x, v.a_table, v.b_table, s2, v.mats, base, v.case.indices,
+                v.row_adapter, v.case.top_k)
+    return bool(np.array_equal(d2, 2.0 * d1)) and bool(np.any(d1 != 0))
+
+
+def pin_router_dense_lora(gather):
+    """A one-entry route with top_k = 1 and every row on expert 0 is dense LoRA;
+    checked through the merged weight delta_W = scale * B @ A."""
+    rng = np.random.default_rng(9)
+    t, k_in, n_out, r = 9, 7, 5, 3
+    x = rng.standard_normal((t, k_in))
+    a = rng.standard_normal((r, k_in))
+    b = rng.standard_normal((n_out, r))
+    s = 1.25
+    base = rng.standard_normal((t, n_out))
+    a_t, b_t, s_t, _ = oracle.pack_expert_tables([(0, 1, 2, s)])
+    got = gather(x, a_t, b_t, s_t, {1: a, 2: b}, base, [0] * t, [0] * t, 1)
+    w_delta = s * (b @ a)               # [n_out, k_in]
+    want = base + x @ w_delta.T
+    return bool(np.allclose(got, want, rtol=1e-12, atol=1e-12))
+
+
+def pin_gather_integer_bruteforce(gather):
+    """Small integer inputs: exact rational brute force (every product and sum
+    written out) equals the fp64 result bit for bit."""
+    rng = np.random.default_rng(21)
+    top_k, n_tok, k_in, n_out, r, n_exp = 2, 3, 4, 3, 2, 3
+    x = rng.integers(-2, 3, (n_tok, k_in)).astype(np.float64)
+    mats, entries = {}, []
+    for e in range(n_exp):
+        mats[10 + e] = rng.integers(-2, 3, (r, k_in)).astype(np.float64)
+        mats[20 + e] = rng.integers(-2, 3, (n_out, r)).astype(np.float64)
+        entries.append((e, 10 + e, 20 + e, [0.5, 1.0, 2.0][e]))
+    a_t, b_t, s_t, _ = oracle.pack_expert_tables(entries)
+    idx = [2, 0, 1, 2, 0, 1]
+    ra = [1, -1, 1]
+    base = rng.integers(-3, 4, (len(idx), n_out)).astype(np.float64)
+    got = gather(x, a_t, b_t, s_t, mats, base, idx, ra, top_k)
+    for row, e in enumerate(idx):
+        t = row // top_k
+        for n in range(n_out):
+            acc = Fraction(int(base[row, n]))
+            if ra[t] >= 0:
+                for j in range(r):
+                    h = sum(Fraction(int(mats[10 + e][j, k])) * Fraction(int(x[t, k]))
+                            for k in range(k_in))
+                    acc += Fraction(s_t[e]) * Fraction(int(mats[20 + e][n, j])) * h
+            if Fraction(got[row, n]) != acc:
+                return False
+    return True
+
+
+def pin_gather_skips(gather):
+    """Rows with a negative map entry, a null cell (a only, b only, both), an id
+    at/after the table length or a negative id are returned bit for bit; a
+    live row on the same tables changes."""
+    rng = np.random.default_rng(3)
+    k_in, n_out, r, top_k = 4, 3, 2, 1
+    x = rng.standard_normal((7, k_in))
+    # address 0 holds junk: an implementation that reads a null cell uses it
+    mats = {0: rng.standard_normal((n_out, r)), 1: rng.standard_normal((r, k_in)),
+            2: rng.standard_normal((n_out, r))}
+    entries = [(0, 1, 2, 1.0), (1, 0, 2, 1.0), (2, 1, 0, 1.0), (3, 0, 0, 0.0), (4, 1, 2, 1.0)]
+    a_t, b_t, s_t, _ = oracle.pack_expert_tables(entries)
+    idx = [1, 2, 3, 5, -1, 0, 4]
+    ra = [0, 0, 0, 0, 0, -1, 0]
+    base = rng.standard_normal((7, n_out))
+    got = gather(x, a_t, b_t, s_t, mats, base, idx, ra, top_k)
+    untouched = got[:6].view(np.uint64) == base[:6].view(np.uint64)
+    return bool(np.all(untouched)) and bool(np.all(got[6] != base[6]))
+
+
+def pin_gather_scalar_equals_vectorized(gather):
+    v = _small_gather(seed=13, wild_index_frac=0.2)
+    base = np.random.default_rng(1).standard_normal((v.case.n_rows, 4))
+    got = gather(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base, v.case.indices,
+                 v.row_adapter, v.case.top_k)
+    ref = oracle.fold_gather_scalar(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base,
+                                    v.case.indices, v.row_adapter, v.case.top_k)
+    return bool(np.allclose(got, ref, rtol=1e-12, atol=1e-12))
+
+
+GATHER_PINS = [pin_gather_hand, pin_gather_b_zero, pin_gather_rank1_onehot,
+               pin_gather_scale_linear, pin_router_dense_lora, pin_gather_integer_bruteforce,
+               pin_gather_skips, pin_gather_scalar_equals_vectorized]
+
+
+def _small_grouped(seed=31, **kw):
+    args = dict(stream_lens=[5, 0, 7, 4], top_k=3, n_route=6, k_in=5, n_out=4, max_rank=2,
+                dtype="f32", n_unadapted=2, dup_frac=0.3, cap=7,
+                stream_slot_values=[1, 1, -1, 1])
+    args.update(kw)
+    return OracleView(make_grouped_case(seed, **args))
+
+
+def pin_grouped_equals_gather_permuted(grouped):
+    """Grouped row r equals gather row sorted_ids[r] on the same inputs."""
+    v = _small_grouped()
+    c = v.case
+    base_flat = np.random.default_rng(2).standard_normal((c.n_rows, 4))
+    base_sorted = base_flat[c.sorted_ids]
+    out_g = grouped(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base_sorted,
+                    c.expert_offsets, c.sorted_ids, v.row_adapter, c.top_k, 0, c.n_rows)
+    out_flat = oracle.fold_gather(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base_flat,
+                                  c.notes["indices_flat"], v.row_adapter, c.top_k)
+    return bool(np.allclose(out_g, out_flat[c.sorted_ids], rtol=1e-12, atol=1e-12))
+
+
+def pin_grouped_windows(grouped):
+    """Folding window after window equals folding one window over all rows, and
+    rows outside a window stay as given."""
+    v = _small_grouped(seed=32)
+    c = v.case
+    base = np.random.default_rng(4).standard_normal((c.n_rows, 4))
+    whole = grouped(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base, c.expert_offsets,
+                    c.sorted_ids, v.row_adapter, c.top_k, 0, c.n_rows)
+    out = base.copy()
+    for s, e in oracle.grouped_down_windows(c.n_rows, 5):
+        nxt = grouped(v.x, v.a_table, v.b_table, v.scale_table, v.mats, out, c.expert_offsets,
+                      c.sorted_ids, v.row_adapter, c.top_k, s, e)
+        outside = np.ones(c.n_rows, dtype=bool)
+        outside[s:e] = False
+        if not np.array_equal(nxt[outside], out[outside]):
+            return False
+        out = nxt
+    return bool(np.allclose(out, whole, rtol=1e-12, atol=1e-12))
+
+
+def pin_grouped_spans(grouped):
+    """Rows before the first span start or after the last span end fold nothing;
+    rows of an empty span's neighbours use the neighbour's expert."""
+    g, x, mats, a_t, b_t, s_t, base = _hand()
+    got = grouped(x, a_t, b_t, s_t, mats, base, [1, 1, 3, 3], [1, 0, 3, 2], [1, 1], 2, 0, 4)
+    want = np.array(g["grouped"][3]["expect"], dtype=np.float64)
+    return bool(np.array_equal(got, want))
+
+
+GROUPED_PINS = [pin_grouped_hand, pin_grouped_equals_gather_permuted, pin_grouped_windows,
+                pin_grouped_spans]
+
+
+@pytest.mark.parametrize("pin", GATHER_PINS, ids=lambda f: f.__name__)
+def test_gather_pins(pin):
+    assert pin(oracle.fold_gather)
+    assert pin(oracle.fold_gather_scalar)
+
+
+@pytest.mark.parametrize("pin", GROUPED_PINS, ids=lambda f: f.__name__)
+def test_grouped_pins(pin):
+    assert pin(oracle.fold_grouped)
+    assert pin(oracle.fold_grouped_scalar)
+
+
+def test_grouped_scalar_equals_vectorized():
+    v = _small_grouped(seed=33)
+    c = v.case
+    base = np.random.default_rng(6).standard_normal((c.n_rows, 4))
+    for s, e in [(0, c.n_rows), (3, 11), (c.n_rows, c.n_rows)]:
+        a = oracle.fold_grouped(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base,
+                                c.expert_offsets, c.sorted_ids, v.row_adapter, c.top_k, s, e)
+        b = oracle.fold_grouped_scalar(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base,
+                                       c.expert_offsets, c.sorted_ids, v.row_adapter, c.top_k,
+                                       s, e)
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_decoy_entries_lose():
+    """With duplicate ids packed decoy-first, the fold equals the fold of the
+    real entries alone (the last duplicate wins)."""
+    v = _small_grouped(seed=34, dup_frac=0.5)
+    c = v.case
+    seen, real = set(), []
+    for ent in reversed(v.entries):
+        if ent[0] not in seen:
+            seen.add(ent[0])
+            real.append(ent)
+    a2, b2, s2, _ = oracle.pack_expert_tables(list(reversed(real)))
+    assert len(real) < len(v.entries)
+    base = np.random.default_rng(7).standard_normal((c.n_rows, 4))
+    x1 = oracle.fold_grouped(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base,
+                             c.expert_offsets, c.sorted_ids, v.row_adapter, c.top_k, 0, c.n_rows)
+    x2 = oracle.fold_grouped(v.x, a2, b2, s2, v.mats, base, c.expert_offsets, c.sorted_ids,
+                             v.row_adapter, c.top_k, 0, c.n_rows)
+    assert np.array_equal(x1, x2)
+
+
+# ---------------------------------------------------------------------------
+# mutation checks: each planted mistake must fail at least one pin
+# ---------------------------------------------------------------------------
+
+
+def _gather_mutant(kind):
+    def f(x, a_table, b_table, scale_table, mats, base, indices, row_adapter, top_k):
+        out = np.array(base, dtype=np.float64, copy=True)
+        n = len(a_table)
+        for row in range(len(indices)):
+            t = row if kind == "token_is_row" else row // top_k
+            t = min(t, x.shape[0] - 1)
+            gate = row_adapter[min(row, len(row_adapter) - 1)] if kind == "map_by_row" \
+                else row_adapter[t]
+            if kind != "no_map_check" and gate < 0:
+                continue
+            e = int(indices[row])
+            if kind == "no_b_cell_check":
+                ok = 0 <= e < n and a_table[e] != 0
+            elif kind == "signed_only_upper":
+                ok = e < n and a_table[e] != 0 and b_table[e] != 0
+            else:
+                ok = 0 <= e < n and a_table[e] != 0 and b_table[e] != 0
+            if not ok:
+                continue
+            a = mats[a_table[e]]
+            b = mats[b_table[e]]
+            if kind == "a_transposed_use":
+                h = (x[t] @ a.T[:, :]) if a.shape[1] == x.shape[1] else None
+                h = a[:, ::-1] @ x[t]
+            else:
+                h = a @ x[t]
+            s = 1.0 if kind == "no_scale" else float(scale_table[e])
+            delta = s * (b @ h)
+            if kind == "minus":
+                delta = -delta
+            if kind == "square_h":
+                delta = s * (b @ (h * h))
+            out[row] = base[row] + delta
+        return out
+    return f
+
+
+GATHER_MUTANTS = ["token_is_row", "map_by_row", "no_map_check", "no_b_cell_check",
+                  "signed_only_upper", "a_transposed_use", "no_scale", "minus", "square_h"]
+
+
+@pytest.mark.parametrize("kind", GATHER_MUTANTS)
+def test_gather_mutant_is_caught(kind):
+    mut = _gather_mutant(kind)
+    results = []
+    for pin in GATHER_PINS:
+        try:
+            results.append(pin(mut))
+        except Exception:
+            results.append(False)
+    assert not all(results), f"mutant {kind} passed every pin"
+
+
+def _grouped_mutant(kind):
+    def f(x, a_table, b_table, scale_table, mats, base, expert_offsets, sorted_ids,
+          row_adapter, top_k, row_offset, row_end):
+        out = np.array(base, dtype=np.float64, copy=True)
+        off = [int(v) for v in expert_offsets]
+        hi = row_end + 1 if kind == "window_inclusive" else row_end
+        for r in range(row_offset, min(hi, len(base))):
+            owner = -1
+            for e in range(len(off) - 1):
+                inside = off[e] <= r <= off[e + 1] if kind == "closed_span" \
+                    else off[e] <= r < off[e + 1]
+                if inside:
+                    owner = e
+                    break
+            if owner < 0:
+                if kind == "orphan_to_zero":
+                    owner = 0
+                else:
+                    continue
+            if kind == "token_is_sorted_row":
+                t = r // top_k
+            elif kind == "token_is_id":
+                t = min(int(sorted_ids[r]), x.shape[0] - 1)
+            else:
+                t = int(sorted_ids[r]) // top_k
+            if row_adapter[t] < 0:
+                continue
+            e = owner
+            if not (0 <= e < len(a_table) and a_table[e] != 0 and b_table[e] != 0):
+                continue
+            a, b = mats[a_table[e]], mats[b_table[e]]
+            out[r] = base[r] + float(scale_table[e]) * (b @ (a @ x[t]))
+        return out
+    return f
+
+
+GROUPED_MUTANTS = ["window_inclusive", "closed_span", "orphan_to_zero", "token_is_sorted_row",
+                   "token_is_id"]
+
+
+@pytest.mark.parametrize("kind", GROUPED_MUTANTS)
+def test_grouped_mutant_is_caught(kind):
+    mut = _grouped_mutant(kind)
+    results = []
+    for pin in GROUPED_PINS:
+        try:
+            results.append(pin(mut))
+        except Exception:
+            results.append(False)
+    assert not all(results), f"mutant {kind} passed every pin"
+
+
+def test_pack_mutants_are_caught():
+    """First-duplicate-wins and table length = max id both fail the golden file."""
+    def first_wins(entries):
+        if not entries:
+            return None
+        n = max(e for e, *_ in entries) + 1
+        a, b, s = [0] * n, [0] * n, [0.0] * n
+        for e, aa, bb, sc in reversed(list(entries)):
+            a[e], b[e], s[e] = aa, bb, sc
+        return a, b, s, n
+
+    def short_table(entries):
+        if not entries:
+            return None
+        n = max(e for e, *_ in entries)
+        a, b, s = [0] * (n + 1), [0] * (n + 1), [0.0] * (n + 1)
+        for e, aa, bb, sc in entries:
+            a[e], b[e], s[e] = aa, bb, sc
+        return a, b, s, n
+
+    for mut in (first_wins, short_table):
+        ok = True
+        for line in golden_lines("pack_expert_tables.txt"):
+            c = json.loads(line)
+            got = mut([tuple(e) for e in c["entries"]])
+            want = None if c["expect"] is None else (
+                c["expect"]["a"], c["expect"]["b"], c["expect"]["s"], c["expect"]["n"])
+            ok &= got == want
+        assert not ok
