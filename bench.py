@@ -1,0 +1,349 @@
+"""Benchmark of the MoE expert-LoRA fold on one MI355X.
+
+One step = one pass of the fold over one synthetic batch: for the decode
+workloads one mlora_gather_bgmv call, for the prefill workloads one
+mlora_grouped_down call per window of grouped_down_windows. The host-side
+integer work (tables, maps, windows) is done once before timing, as an engine
+does at adapter install / batch setup; its cost is reported separately.
+
+Inputs are resident in HBM before timing starts. The step cycles through
+`copies` independent copies of x, A, B, base_out and the tables, so each step
+reads data that no recent step touched (more bytes than L2 + MALL hold):
+the figures are cold-cache HBM figures.
+
+Prints ONE JSON line (rank 0, N = 1):
+  value      rows folded per second (rows covered by the calls / wall time)
+  roofline   algorithmic bytes per launch / mean launch duration (HIP events)
+             against the 8 TB/s HBM peak; traffic = counter-measured HBM bytes
+             from the committed rocprofv3 summary when the kernel source still
+             matches it, else null
+  cpu_baseline  the fp64 CPU oracle timed on the host on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-LoRA fold rows/s + achieved HBM GB/s (decode gather, prefill grouped)"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "cfg2"
+KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_lora_amd", "csrc", "mlora_fold.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+WORKLOAD_TEXT = {
+    "cfg1": "tiny gather fold f32: 4 tokens x top-2 of 4 experts, k_in 64, n_out 32, rank 8",
+    "cfg2": "Qwen3-MoE-like decode down-proj gather: 64 seqs x top-8 (640 rows padded), "
+            "128 experts (96 adapted), k_in 768, n_out 2048, rank 16, bf16",
+    "cfg3": "prefill grouped down fold: 4096 tokens x top-8 (32768 sorted rows), Zipf(1.1) "
+            "over 128 experts, k_in 768, n_out 2048, rank 32, bf16, windows of 8192",
+    "cfg4": "gate/up gather: 256 seqs x top-8 (2048 rows), 128 experts, k_in 2048, "
+            "n_out 768, rank 64, bf16",
+    "cfg5a": "router fold one-entry route: 8192 token rows, top_k 1, k_in 2048, n_out 128, "
+             "rank 16, bf16",
+    "cfg5b": "mixed prefill grouped fold: 16384 sorted rows, 256 experts (77 unadapted, "
+             "duplicate ids), k_in 1536, n_out 4096, rank 16, bf16, windows of 8192",
+}
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes: what the fold must move, counted from the inputs
+# ---------------------------------------------------------------------------
+
+def algorithmic_traffic(case, tables, row_adapter):
+    """(bytes, flops, rows, folded_rows) per step, summed over launches.
+
+    bytes = unique tokens * k_in * 2 + unique experts * (r*k_in + n_out*r) * 2
+          + folded rows * n_out * 2 * 2 (base_out read + write)
+          + 4 * rows (indices / sorted_ids) + 4 * tokens (map)
+          + 4 * (n_route + 1) (offsets, grouped) + 20 * n_experts (tables)
+    """
+    at, bt, _, n_exp = tables
+    elt = 2 if case.dtype == "bf16" else 4
+    K, N, R = case.k_in, case.n_out, case.max_rank
+    live_cell = np.zeros(max(n_exp, 1), dtype=bool)
+    if n_exp:
+        live_cell[:n_exp] = (at != 0) & (bt != 0)
+    ra = np.asarray(row_adapter)
+
+    def cell_ok(e):
+        return (e >= 0) & (e < n_exp) & live_cell[np.clip(e, 0, max(n_exp - 1, 0))]
+
+    launches = []
+    if case.path == "gather":
+        rows = np.arange(case.n_rows)
+        tok = rows // case.top_k
+        e = case.indices.astype(np.int64)
+        live = (ra[tok] >= 0) & cell_ok(e)
+        launches.append((case.n_rows, tok[live], e[live], 0))
+    else:
+        off = case.expert_offsets.astype(np.int64)
+        owner = np.searchsorted(off, np.arange(case.n_rows), side="right") - 1
+        tok_all = case.sorted_ids.astype(np.int64) // case.top_k
+        inside = (owner >= 0) & (owner < len(off) - 1)
+        import moe_expert_lora_amd as ml
+        for (s, t) in ml.mlora_grouped_down_windows(case.n_rows, case.cap):
+            o = owner[s:t]
+            tk = tok_all[s:t]
+            live = inside[s:t] & cell_ok(o) & (ra[np.clip(tk, 0, len(ra) - 1)] >= 0)
+            launches.append((t - s, tk[live], o[live], case.n_route + 1))
+    total_b = 0
+    flops = 0
+    folded = 0
+    rows_total = 0
+    for (rows, toks, exps, n_off) in launches:
+        f = toks.shape[0]
+        b = (np.unique(toks).size * K * elt + np.unique(exps).size * (R * K + N * R) * elt
+             + f * N * elt * 2 + 4 * rows + 4 * case.n_tokens + 4 * n_off + 20 * n_exp)
+        total_b += int(b)
+        flops += 2 * f * R * (K + N)
+        folded += f
+        rows_total += rows
+    return total_b, flops, rows_total, folded, len(launches)
+
+
+# ---------------------------------------------------------------------------
+# device staging with rotating copies
+# ---------------------------------------------------------------------------
+
+class Staged:
+    def __init__(self, case, copies, device="cuda"):
+        import torch
+        from tests.device import DeviceCase
+        self.case = case
+        self.primary = DeviceCase(case, device)
+        self.copies = [self.primary]
+        for _ in range(copies - 1):
+            self.copies.append(self.primary_clone(device))
+        self.bases = [c.base0.clone() for c in self.copies]
+        torch.cuda.synchronize()
+
+    def primary_clone(self, device):
+        """Same data at new addresses (weights, x, base_out and the tables)."""
+        import copy
+        import moe_expert_lora_amd as ml
+        from tests.device import u64_to_device
+        p = self.primary
+        c = copy.copy(p)
+        c.x = p.x.clone()
+        c.a_pool = p.a_pool.clone()
+        c.b_pool = p.b_pool.clone()
+        c.base0 = p.base0.clone()
+        at, bt, st, n = p.tables_host
+        da = c.a_pool.data_ptr() - p.a_pool.data_ptr()
+        db = c.b_pool.data_ptr() - p.b_pool.data_ptr()
+        at2 = np.where(at != 0, at + np.uint64(da % (1 << 64)), 0).astype(np.uint64)
+        bt2 = np.where(bt != 0, bt + np.uint64(db % (1 << 64)), 0).astype(np.uint64)
+        c.a_table = u64_to_device(np.concatenate([at2, [0]]), device)
+        c.b_table = u64_to_device(np.concatenate([bt2, [0]]), device)
+        c.scale_table = p.scale_table.clone()
+        c.route = ml.make_route(c.a_table, c.b_table, c.scale_table, n, self.case.k_in,
+                                self.case.n_out, self.case.max_rank, p.tdtype)
+        return c
+
+    def step(self, i):
+        k = i % len(self.copies)
+        self.copies[k].fold(self.bases[k])
+
+
+def copy_bytes(case):
+    elt = 2 if case.dtype == "bf16" else 4
+    return (case.x.size + case.a_pool.size + case.b_pool.size + case.base.size) * elt
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(case, budget_s=10.0):
+    from tests.common import OracleView
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    view = OracleView(case)
+    base64 = None
+    from tests.common import to_f64
+    base64 = to_f64(case.base, case.dtype)
+    import oracle
+
+    if case.path == "gather":
+        def run():
+            return oracle.fold_gather(view.x, view.a_table, view.b_table, view.scale_table,
+                                      view.mats, base64, case.indices, view.row_adapter,
+                                      case.top_k)
+        rows_per = case.n_rows
+        sample = f"full {case.name} fold ({rows_per} rows) repeated"
+    else:
+        # bounded sample: the first window
+        import moe_expert_lora_amd as ml
+        s, e = ml.mlora_grouped_down_windows(case.n_rows, case.cap)[0]
+
+        def run():
+            return oracle.fold_grouped(view.x, view.a_table, view.b_table, view.scale_table,
+                                       view.mats, base64, case.expert_offsets, case.sorted_ids,
+                                       view.row_adapter, case.top_k, s, e)
+        rows_per = e - s
+        sample = f"first window [{s}, {e}) of {case.name}, repeated"
+    run()  # warm-up
+    t0 = time.perf_counter()
+    iters = 0
+    while True:
+        run()
+        iters += 1
+        el = time.perf_counter() - t0
+        if (el >= budget_s and iters >= 3) or el >= 3 * budget_s:
+            break
+    return {"value": rows_per * iters / el, "unit": "rows/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{sample} {iters}x in {el:.1f} s (fp64 NumPy, "
+                                         "per-expert matmuls)"}
+
+
+# ---------------------------------------------------------------------------
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the fold needs no collective and this "
+              "build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_expert_lora_amd as ml
+    import workloads
+
+    ml.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    t_gen = time.perf_counter()
+    case = workloads.CONFIGS[args.workload]()
+    t_gen = time.perf_counter() - t_gen
+    cb = copy_bytes(case)
+    copies = args.copies or max(2, min(64, math.ceil(640e6 / cb)))
+    st = Staged(case, copies)
+    tables = st.primary.tables_host
+    ra = st.primary.row_adapter_host
+    alg_bytes, flops, rows, folded, launches = algorithmic_traffic(case, tables, ra)
+
+    # host-side integer work of one batch, timed for the record
+    t0 = time.perf_counter()
+    for _ in range(50):
+        if case.map_kind == "decode":
+            ml.mlora_build_moe_row_adapter_decode(case.adapter_slots, case.padded_n, case.active,
+                                                  case.has_moe_lora)
+        else:
+            ml.mlora_build_moe_row_adapter_host(case.cu_seqlens, case.stream_slots)
+        if case.path == "grouped":
+            ml.mlora_grouped_down_windows(case.n_rows, case.cap)
+    host_us = (time.perf_counter() - t0) / 50 * 1e6
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        st.step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, wall clock
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st.step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-step device duration with HIP events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        st.step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    dur_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    step_ms = float(np.mean(dur_ms))
+    per_launch_s = step_ms / 1e3 / launches
+
+    achieved = alg_bytes / launches / per_launch_s / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            rec = json.load(open(TRAFFIC_FILE)).get(args.workload)
+            if rec and rec.get("kernel_sha256_16") == kernel_hash():
+                traffic = rec.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    ms_per_step = wall / args.steps * 1e3
+    out = {
+        "metric": METRIC,
+        "value": rows * args.steps / wall,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded generators; random-init adapter weights)",
+        "config": {
+            "workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
+            "path": case.path,
+            "rows_per_step": rows,
+            "folded_rows_per_step": folded,
+            "launches_per_step": launches,
+            "rotating_copies": copies,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes / launches,
+            "flops_per_launch": flops / launches,
+            "launch_us_mean": per_launch_s * 1e6,
+            "step_us_p10_p50_p90": [float(np.percentile(dur_ms, q)) * 1e3 for q in (10, 50, 90)],
+        },
+        "cpu_baseline": cpu,
+        "host_setup_us": host_us,
+        "notes": "the pages quote no performance numbers; vs_baseline is null",
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

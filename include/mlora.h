@@ -1,0 +1,209 @@
+/*
+ * mlora.h - C ABI of libmlora.so: the MoE expert-LoRA fold on AMD Instinct
+ * MI355X (gfx950), and the host-side integer work around it.
+ *
+ * The fold adds, in place, each routed expert's low-rank delta onto the base
+ * projection output of a (token, slot) row:
+ *
+ *     base_out[row] += scale_e * ((x[token(row)] @ A_e^T) @ B_e^T)
+ *
+ * (the two fold items of the "moe_lora_grouped" launcher-module index page).
+ * Sources cited below:
+ *   [P1] the "moe_row_adapter.rs" source page (GPU-free MoE LoRA routing),
+ *   [P2] the "moe_lora_grouped" module index page (fold launchers, packing).
+ *
+ * Conventions shared by every entry point:
+ *   - Every buffer, host or device, belongs to the caller. The library never
+ *     allocates, frees or synchronises, and keeps no state except a
+ *     thread-local last-error message (mlora_last_error).
+ *   - Host outputs are written only when the call returns MLORA_OK (or, for
+ *     sizes, MLORA_ERR_CAPACITY, which writes only the needed size).
+ *   - The two fold calls enqueue kernels on the caller's stream and return at
+ *     once. The host never reads routing data, so a fold is capturable in a
+ *     HIP graph. A device-side fault surfaces at the caller's next sync.
+ *   - Layouts are row-major and contiguous. bf16 is stored as its 16 raw bits.
+ */
+#ifndef MLORA_H_
+#define MLORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+  MLORA_OK = 0,
+  MLORA_NONE = 1,           /* the pages' "None": nothing was written         */
+  MLORA_ERR_INVALID = -1,   /* bad arguments (also the pages' panic on cap 0) */
+  MLORA_ERR_REFUSE = -2,    /* a decode batch the single-active fold refuses  */
+  MLORA_ERR_CAPACITY = -3,  /* a host output is too small; size written       */
+  MLORA_ERR_HIP = -4        /* the HIP runtime rejected a launch              */
+};
+
+/* Per-request fold decision [P1 resolve_moe_lora_route; MoeLoraRoute]. */
+enum { MLORA_ROUTE_FOLD = 0, MLORA_ROUTE_SKIP = 1, MLORA_ROUTE_REFUSE = 2 };
+
+/* Element type of x, A_e, B_e and base_out. */
+enum { MLORA_F32 = 0, MLORA_BF16 = 1 };
+
+/* Rows per grouped-fold tile [P2 MLG_M_TILE]: the host grid
+ * (mlora_grouped_down_wc) and the kernel's tiles use this one value. */
+#define MLORA_MLG_M_TILE 64
+
+/*
+ * Device tables of one projection's expert LoRA pairs, indexed by expert id
+ * [P2 MoeExpertRoute]. a_table[e] / b_table[e] hold the device addresses of
+ * A_e [max_rank, k_in] and B_e [n_out, max_rank]; scale_table[e] is scale_e.
+ * A cell of 0 marks an unadapted expert. All experts share k_in, n_out and
+ * max_rank (a lower rank is zero-padded to max_rank). Every A_e / B_e address
+ * must be 16-byte aligned. The struct itself lives in host memory; the three
+ * table pointers are device pointers with n_experts entries.
+ */
+typedef struct mlora_expert_route {
+  const uint64_t* a_table;
+  const uint64_t* b_table;
+  const float* scale_table;
+  int32_t n_experts;
+  int32_t k_in;      /* multiple of 8, >= 8                        */
+  int32_t n_out;     /* multiple of 8, >= 8                        */
+  int32_t max_rank;  /* 1 .. 128                                   */
+  int32_t dtype;     /* MLORA_BF16 or MLORA_F32                    */
+} mlora_expert_route;
+
+/* ------------------------------------------------------------------------ */
+/* Host-side integer work (no GPU needed).                                   */
+/* ------------------------------------------------------------------------ */
+
+/* [P1 resolve_moe_lora_route] With has_moe_lora == 0 every request folds;
+ * otherwise a negative slot is Skip, slot == active is Fold, any other slot
+ * is Refuse. Returns an MLORA_ROUTE_* value. */
+int32_t mlora_resolve_moe_lora_route(int32_t adapter_slot, int32_t active,
+                                     int32_t has_moe_lora);
+
+/* [P1 ensure_decode_route_servable] MLORA_OK for Fold and Skip,
+ * MLORA_ERR_REFUSE (message names the one-adapter-per-batch rule) for Refuse,
+ * MLORA_ERR_INVALID for a value that is no route. */
+int32_t mlora_ensure_decode_route_servable(int32_t route);
+
+/* [P2 pack_expert_tables, ExpertTables] Pack n_entries entries
+ * (expert_ids[i], a_addrs[i], b_addrs[i], scales[i]) into host tables indexed
+ * by expert id, with n = max id + 1 cells, 0 / 0.0 at ids no entry names, and
+ * the last entry winning for a repeated id. Ids must lie in [0, 2^24).
+ *   n_entries == 0            -> MLORA_NONE, nothing written.
+ *   a negative / too large id -> MLORA_ERR_INVALID, nothing written.
+ *   table_cap < n             -> MLORA_ERR_CAPACITY, only *n_experts written.
+ * The three tables may be NULL together with table_cap == 0 to query n.
+ * Upload the tables to device memory to build an mlora_expert_route. */
+int32_t mlora_pack_expert_tables(const int32_t* expert_ids, const uint64_t* a_addrs,
+                                 const uint64_t* b_addrs, const float* scales,
+                                 int64_t n_entries, uint64_t* a_table, uint64_t* b_table,
+                                 float* scale_table, int64_t table_cap, int32_t* n_experts);
+
+/* [P1 build_moe_row_adapter_host] Per-token adapter map of a packed prefill
+ * batch: stream b's slot is copied unchanged onto tokens
+ * cu_seqlens[b] .. cu_seqlens[b+1] (n_cu = batch + 1).
+ *   MLORA_NONE (nothing written) when n_cu < 2, n_slots != n_cu - 1,
+ *   cu_seqlens[0] != 0, or a boundary is negative or below its predecessor.
+ *   MLORA_ERR_CAPACITY when out_cap < total (only *total written).
+ * On MLORA_OK, out[0 .. total) holds the map and *total its length. The copy
+ * is literal: a slot >= 0 that is not the active one would fold the active
+ * adapter, so callers resolve routes first. */
+int32_t mlora_build_moe_row_adapter_host(const int32_t* cu_seqlens, int64_t n_cu,
+                                         const int32_t* adapter_slots, int64_t n_slots,
+                                         int32_t* out, int64_t out_cap, int64_t* total);
+
+/* [P1 build_moe_row_adapter_decode] Per-sequence adapter map of a decode batch:
+ * out[i] (i < padded_n) is `active` when sequence i exists (i < n_slots) and
+ * resolves to Fold, else -1 (Skip, Refuse and padding). Slots past padded_n
+ * are ignored. out must hold padded_n entries. MLORA_ERR_INVALID for a
+ * negative size or a NULL pointer that is needed. */
+int32_t mlora_build_moe_row_adapter_decode(const int32_t* adapter_slots, int64_t n_slots,
+                                           int64_t padded_n, int32_t active,
+                                           int32_t has_moe_lora, int32_t* out);
+
+/* [P2 grouped_down_windows] Contiguous [start, end) windows of at most cap
+ * rows covering 0 .. total_rows, all full except the last; zero rows give no
+ * window. cap <= 0 or total_rows < 0 -> MLORA_ERR_INVALID.
+ * out_cap < count -> MLORA_ERR_CAPACITY (only *n_windows written). */
+int32_t mlora_grouped_down_windows(int64_t total_rows, int64_t cap, int64_t* starts,
+                                   int64_t* ends, int64_t out_cap, int64_t* n_windows);
+
+/* [P2 grouped_down_wc] Row tiles of the window [row_offset, row_end):
+ * ceil((row_end - row_offset) / MLORA_MLG_M_TILE), at least 1. */
+uint32_t mlora_grouped_down_wc(int64_t row_offset, int64_t row_end);
+
+/* [P2 gather_row_token] The token that owns flat (token, slot) row `row`:
+ * row / top_k. Returns -1 when row < 0 or top_k <= 0. */
+int32_t mlora_gather_row_token(int32_t row, int32_t top_k);
+
+/* The grouped-fold tile rows (MLORA_MLG_M_TILE), for callers that cannot see
+ * the macro. */
+int32_t mlora_m_tile(void);
+
+/* Message of the last failing call on this thread ("" if none). The string
+ * stays valid until the next call on the same thread. */
+const char* mlora_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Device folds (enqueue on `stream`, a hipStream_t; NULL = default stream).  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [P2 moe_lora_gather_bgmv] Decode fold over flat (token, slot) rows.
+ * For every row in [0, n_slots): token = row / top_k; the row is skipped when
+ * row_adapter[token] < 0 [P1 build_moe_row_adapter_decode], when
+ * e = indices[row] is negative or >= n_experts, or when a_table[e] or
+ * b_table[e] is 0 [P2 module invariant]. Otherwise
+ *     base_out[row, :] = round(base_out[row, :] + scale_e * B_e (A_e x[token]))
+ * with fp32 accumulation and, for bf16, one round-to-nearest-even store.
+ * Skipped rows are not written at all.
+ *
+ * Device arguments:
+ *   x           [n_tokens, k_in]   dtype (bf16 or f32), read only
+ *   base_out    [n_slots, n_out]   dtype, updated in place
+ *   indices     [n_slots]          int32 expert id per row, read on device
+ *   row_adapter [n_tokens]         int32 per-token map, read on device
+ * n_tokens must be >= ceil(n_slots / top_k). x and base_out must be 16-byte
+ * aligned. n_slots == 0 or n_experts == 0 enqueues nothing.
+ * Returns MLORA_OK, MLORA_ERR_INVALID (arguments; nothing enqueued) or
+ * MLORA_ERR_HIP (launch rejected).
+ */
+int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void* x, int64_t n_tokens,
+                          void* base_out, const int32_t* indices, const int32_t* row_adapter,
+                          int64_t n_slots, int32_t top_k, void* stream);
+
+/*
+ * [P2 moe_lora_grouped_down] Prefill fold over expert-sorted rows in the
+ * window [row_offset, row_end) of a [n_rows, n_out] base_out.
+ * The expert of sorted row r is the e with expert_offsets[e] <= r <
+ * expert_offsets[e+1] (e < n_route; rows in no span are skipped). The row's
+ * token is sorted_ids[r] / top_k, sorted_ids holding each sorted row's flat
+ * (token, slot) id. Skip rules and arithmetic are those of mlora_gather_bgmv,
+ * with row_adapter indexed by that token; a token outside [0, n_tokens) is
+ * skipped. Rows outside the window are not touched. The device reads the
+ * routing; expert_offsets must be non-decreasing (other contents stay in
+ * bounds but fold unspecified rows of the window).
+ *
+ * Device arguments:
+ *   x              [n_tokens, k_in]  dtype
+ *   base_out       [n_rows, n_out]   dtype, updated in place
+ *   expert_offsets [n_route + 1]     int32
+ *   sorted_ids     [n_rows]          int32
+ *   row_adapter    [n_tokens]        int32
+ * 0 <= row_offset <= row_end <= n_rows. An empty window enqueues nothing.
+ * Returns MLORA_OK, MLORA_ERR_INVALID or MLORA_ERR_HIP.
+ */
+int32_t mlora_grouped_down(const mlora_expert_route* route, const void* x, int64_t n_tokens,
+                           void* base_out, int64_t n_rows, const int32_t* expert_offsets,
+                           int32_t n_route, const int32_t* sorted_ids,
+                           const int32_t* row_adapter, int32_t top_k, int64_t row_offset,
+                           int64_t row_end, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* MLORA_H_ */

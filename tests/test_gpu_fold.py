@@ -1,0 +1,341 @@
+"""GPU parity of the two folds against the fp64 oracle, through the C ABI.
+
+Bar (per fold call, over the whole base_out tensor): relative L2 <= 2e-3 and
+max abs <= 3e-2 against the unrounded fp64 oracle, on a random base (R run)
+and on a zero base (Z run, which measures the delta itself). Rows the fold
+must not touch are compared bit for bit; integer maps and tables bit for bit.
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+
+import workloads
+from tests.common import MAX_ABS_TOL, REL_L2_TOL, OracleView, max_abs, rel_l2, to_f64
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@functools.lru_cache(maxsize=None)
+def staged(name):
+    from tests.device import DeviceCase
+    case = workloads.CONFIGS[name]()
+    return case, OracleView(case), DeviceCase(case, DEV)
+
+
+def put_sentinel(base, rows, dtype):
+    """Fill `rows` of base with a signalling-NaN pattern (written through an
+    integer view); any arithmetic write would turn it into another pattern."""
+    if dtype == "bf16":
+        base.view(np.uint16)[rows] = 0x7F81
+    else:
+        base.view(np.uint32)[rows] = 0x7F800001
+
+
+def check(view, got, base, label):
+    ref = view.fold(base=base)
+    g = to_f64(got, view.case.dtype)
+    rel, mx = rel_l2(g, ref), max_abs(g, ref)
+    print(f"{label}: rel_l2={rel:.3e} max_abs={mx:.3e}", flush=True)
+    assert rel <= REL_L2_TOL, f"{label}: rel L2 {rel}"
+    assert mx <= MAX_ABS_TOL, f"{label}: max abs {mx}"
+    live = view.live_rows()
+    if (~live).any():
+        assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8)), \
+            f"{label}: a row that folds nothing was written"
+    return rel, mx
+
+
+ALL = ["cfg1", "cfg2", "cfg3", "cfg4", "cfg5a", "cfg5b"]
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_integer_maps_and_tables_bit_exact(name):
+    _need_gpu()
+    case, view, dev = staged(name)
+    assert dev.row_adapter_host.tolist() == view.row_adapter.tolist()
+    at, bt, st, n = dev.tables_host
+    assert n == view.n_experts
+    # same cells null / non-null, same scales bit for bit
+    assert [int(v != 0) for v in at] == [int(v != 0) for v in view.a_table]
+    assert [int(v != 0) for v in bt] == [int(v != 0) for v in view.b_table]
+    assert st.view(np.uint32).tolist() == np.asarray(view.scale_table, np.float32).view(np.uint32).tolist()
+    if case.path == "grouped":
+        import oracle
+        assert dev.windows == oracle.grouped_down_windows(case.n_rows, case.cap)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_parity_random_base(name):
+    _need_gpu()
+    case, view, dev = staged(name)
+    got = dev.run()
+    check(view, got, case.base, f"{name} R")
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_parity_zero_base(name):
+    _need_gpu()
+    case, view, dev = staged(name)
+    base = np.zeros_like(case.base)
+    got = dev.run(base)
+    check(view, got, base, f"{name} Z")
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_untouched_rows_sentinel(name):
+    _need_gpu()
+    case, view, dev = staged(name)
+    live = view.live_rows()
+    base = case.base.copy()
+    put_sentinel(base, ~live, case.dtype)
+    got = dev.run(base)
+    assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
+    assert not np.any(np.isnan(to_f64(got[live], case.dtype)))
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg5b"])
+def test_deterministic(name):
+    _need_gpu()
+    case, view, dev = staged(name)
+    a = dev.run()
+    b = dev.run()
+    assert np.array_equal(a, b)
+
+
+def test_grouped_equals_gather_permuted():
+    """Grouped row r equals gather row sorted_ids[r], bit for bit (same inputs)."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    g = workloads.make_grouped_case(71, stream_lens=[300, 97, 211], top_k=4, n_route=24,
+                                    k_in=256, n_out=512, max_rank=32, routing="zipf",
+                                    n_unadapted=4, cap=200, stream_slot_values=[1, -1, 1])
+    dg = DeviceCase(g, DEV)
+    out_g = dg.run()
+    flat = workloads.FoldCase(**{k: getattr(g, k) for k in g.__dataclass_fields__})
+    flat.path = "gather"
+    flat.indices = g.notes["indices_flat"]
+    inv = np.empty_like(g.sorted_ids)
+    inv[g.sorted_ids] = np.arange(g.sorted_ids.shape[0], dtype=g.sorted_ids.dtype)
+    flat.base = g.base[inv]  # flat row i holds the base of its sorted position
+    df = DeviceCase(flat, DEV)
+    out_f = df.run()
+    assert np.array_equal(out_g, out_f[g.sorted_ids])
+
+
+def test_windows_equal_single_window():
+    _need_gpu()
+    case, view, dev = staged("cfg3")
+    a = dev.run(windows=[(0, case.n_rows)])
+    b = dev.run()  # four windows of 8192
+    assert np.array_equal(a, b)
+    c = dev.run(windows=[(0, 1000), (1000, 1001), (1001, 20000), (20000, case.n_rows)])
+    assert np.array_equal(a, c)
+
+
+def test_scale_power_of_two_is_exact():
+    """Z run: scaling every scale by 4 scales every output by 4, bit for bit."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    c1 = workloads.make_gather_case(72, n_seq=40, padded_n=48, top_k=4, n_route=16, k_in=320,
+                                    n_out=384, max_rank=16, skip_seqs=3)
+    c1.base = np.zeros_like(c1.base)
+    c2 = workloads.FoldCase(**{k: getattr(c1, k) for k in c1.__dataclass_fields__})
+    c2.entries = [(e, a, b, s * 4.0) for (e, a, b, s) in c1.entries]
+    o1 = to_f64(DeviceCase(c1, DEV).run(), "bf16")
+    o2 = to_f64(DeviceCase(c2, DEV).run(), "bf16")
+    assert np.array_equal(o2, 4.0 * o1)
+    assert np.any(o1 != 0)
+
+
+def test_b_zero_leaves_base():
+    _need_gpu()
+    from tests.device import DeviceCase
+    c = workloads.make_grouped_case(73, stream_lens=[90, 70], top_k=2, n_route=8, k_in=128,
+                                    n_out=256, max_rank=16, cap=64)
+    c.b_pool = np.zeros_like(c.b_pool)
+    got = DeviceCase(c, DEV).run()
+    assert np.array_equal(to_f64(got, "bf16"), to_f64(c.base, "bf16"))
+
+
+def test_integer_inputs_bit_exact():
+    """Inputs in {-1, 0, 1}, scales in {1/2, 1, 2}: every partial sum is exact
+    in fp32 and bf16, so the device result equals the oracle exactly."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    rng = np.random.default_rng(74)
+    for path in ("gather", "grouped"):
+        if path == "gather":
+            c = workloads.make_gather_case(75, n_seq=30, padded_n=36, top_k=3, n_route=9,
+                                           k_in=96, n_out=136, max_rank=24, skip_seqs=4,
+                                           wild_index_frac=0.1)
+        else:
+            c = workloads.make_grouped_case(76, stream_lens=[50, 61], top_k=3, n_route=9,
+                                            k_in=96, n_out=136, max_rank=24, n_unadapted=2,
+                                            cap=70, dup_frac=0.3)
+        bits = {-1: 0xBF80, 0: 0x0000, 1: 0x3F80}
+
+        def tern(shape):
+            v = rng.integers(-1, 2, size=shape)
+            return np.vectorize(lambda t: bits[int(t)])(v).astype(np.uint16)
+
+        # two non-zeros per x row keep |h| <= 2 and every output within bf16's
+        # exact-integer range
+        x = np.zeros(c.x.shape, dtype=np.uint16)
+        for t in range(x.shape[0]):
+            cols = rng.choice(x.shape[1], size=2, replace=False)
+            x[t, cols] = [bits[int(v)] for v in rng.choice([-1, 1], size=2)]
+        c.x = x
+        c.a_pool = tern(c.a_pool.shape)
+        c.b_pool = tern(c.b_pool.shape)
+        c.base = tern(c.base.shape)
+        c.entries = [(e, a, b, [0.5, 1.0, 2.0][i % 3]) for i, (e, a, b, _) in enumerate(c.entries)]
+        view = OracleView(c)
+        ref = view.fold()
+        assert np.abs(ref).max() <= 256
+        got = to_f64(DeviceCase(c, DEV).run(), "bf16")
+        assert np.array_equal(got, ref), path
+
+
+def test_rank1_onehot_closed_form():
+    """One-hot x rows and rank 1: delta = scale * A[0, i] * B[:, 0]."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    c = workloads.make_gather_case(77, n_seq=20, padded_n=20, top_k=2, n_route=5, k_in=64,
+                                   n_out=96, max_rank=1)
+    hot = np.random.default_rng(78).integers(0, 64, size=c.x.shape[0])
+    x = np.zeros(c.x.shape, dtype=np.uint16)
+    x[np.arange(x.shape[0]), hot] = 0x3F80
+    c.x = x
+    c.base = np.zeros_like(c.base)
+    got = to_f64(DeviceCase(c, DEV).run(), "bf16")
+    view = OracleView(c)
+    for row in range(c.n_rows):
+        e = int(c.indices[row])
+        t = row // c.top_k
+        if not (0 <= e < view.n_experts and view.a_table[e] and view.b_table[e]):
+            continue
+        a = to_f64(c.a_pool[view_handle(c, e)], "bf16")
+        b = to_f64(c.b_pool[view_handle(c, e)], "bf16")
+        want = view.scale_table[e] * a[0, hot[t]] * b[:, 0]
+        assert np.allclose(got[row], want, rtol=8e-3, atol=1e-6)
+
+
+def view_handle(c, e):
+    h = None
+    for (ee, a, _, _) in c.entries:
+        if ee == e:
+            h = a
+    return h
+
+
+SMALL = [
+    # (label, builder kwargs)
+    ("gather_ragged_r8", dict(kind="gather", n_seq=13, padded_n=17, top_k=3, n_route=11,
+                              k_in=40, n_out=72, max_rank=8, skip_seqs=2, refuse_seqs=1,
+                              wild_index_frac=0.15, n_adapted=7)),
+    ("gather_r24_k72", dict(kind="gather", n_seq=50, padded_n=50, top_k=5, n_route=12,
+                            k_in=72, n_out=104, max_rank=24, n_adapted=10, dup_frac=0.3)),
+    ("gather_r48", dict(kind="gather", n_seq=64, padded_n=70, top_k=4, n_route=6, k_in=200,
+                        n_out=136, max_rank=48, skip_seqs=5)),
+    ("gather_r100", dict(kind="gather", n_seq=37, padded_n=40, top_k=2, n_route=5, k_in=264,
+                         n_out=520, max_rank=100)),
+    ("gather_r128", dict(kind="gather", n_seq=33, padded_n=33, top_k=3, n_route=4, k_in=128,
+                         n_out=96, max_rank=128)),
+    ("gather_r64_many_rows", dict(kind="gather", n_seq=700, padded_n=700, top_k=2, n_route=3,
+                                  k_in=512, n_out=264, max_rank=64)),
+    ("gather_topk1_one_expert", dict(kind="gather", n_seq=3000, padded_n=3000, top_k=1,
+                                     n_route=1, k_in=256, n_out=128, max_rank=16,
+                                     index_mode="zero", adapted=np.array([0]))),
+    ("gather_slots_not_multiple", dict(kind="gather", n_seq=10, padded_n=10, top_k=4,
+                                       n_route=7, k_in=64, n_out=64, max_rank=16,
+                                       n_slots=37)),
+    ("gather_all_skip", dict(kind="gather", n_seq=8, padded_n=8, top_k=2, n_route=4,
+                             k_in=64, n_out=64, max_rank=16, skip_seqs=8)),
+    ("gather_f32_r24", dict(kind="gather", n_seq=9, padded_n=11, top_k=3, n_route=6, k_in=48,
+                            n_out=40, max_rank=24, dtype="f32", skip_seqs=1,
+                            wild_index_frac=0.1)),
+    ("grouped_zipf_r32", dict(kind="grouped", stream_lens=[130, 0, 77, 300], top_k=6,
+                              n_route=20, k_in=192, n_out=320, max_rank=32, routing="zipf",
+                              n_unadapted=3, cap=100, stream_slot_values=[1, 1, -1, 1])),
+    ("grouped_r16_wide", dict(kind="grouped", stream_lens=[257], top_k=8, n_route=40,
+                              k_in=1536, n_out=1032, max_rank=16, n_unadapted=10,
+                              force_unadapted=(39,), dup_frac=0.2, cap=1000)),
+    ("grouped_r8_narrow", dict(kind="grouped", stream_lens=[33, 31], top_k=3, n_route=5,
+                               k_in=56, n_out=24, max_rank=8, cap=7)),
+    ("grouped_r64_r100", dict(kind="grouped", stream_lens=[211], top_k=2, n_route=9,
+                              k_in=320, n_out=200, max_rank=100, cap=150)),
+    ("grouped_r128", dict(kind="grouped", stream_lens=[100], top_k=2, n_route=3, k_in=128,
+                          n_out=256, max_rank=128, cap=64)),
+    ("grouped_f32", dict(kind="grouped", stream_lens=[20, 9], top_k=3, n_route=7, k_in=40,
+                         n_out=48, max_rank=12, dtype="f32", n_unadapted=2, cap=30)),
+]
+
+
+def build_small(label, kw):
+    kw = dict(kw)
+    kind = kw.pop("kind")
+    seed = 1000 + sum(map(ord, label))
+    if kind == "gather":
+        return workloads.make_gather_case(seed, name=label, **kw)
+    return workloads.make_grouped_case(seed, name=label, **kw)
+
+
+@pytest.mark.parametrize("label,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases(label, kw):
+    _need_gpu()
+    from tests.device import DeviceCase
+    c = build_small(label, kw)
+    view = OracleView(c)
+    dev = DeviceCase(c, DEV)
+    check(view, dev.run(), c.base, f"{label} R")
+    zero = np.zeros_like(c.base)
+    if view.live_rows().any():
+        check(view, dev.run(zero), zero, f"{label} Z")
+    live = view.live_rows()
+    base = c.base.copy()
+    put_sentinel(base, ~live, c.dtype)
+    got = dev.run(base)
+    assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
+
+
+def test_guard_bands_untouched():
+    """Fold into a slice of a larger buffer: the bytes around it stay as they were."""
+    _need_gpu()
+    from tests.device import DeviceCase, from_torch, to_torch
+    c = workloads.make_grouped_case(79, stream_lens=[120], top_k=4, n_route=10, k_in=128,
+                                    n_out=256, max_rank=32, cap=100)
+    dev = DeviceCase(c, DEV)
+    pad = 4096
+    flat = np.random.default_rng(80).integers(0, 1 << 16, size=c.base.size + 2 * pad,
+                                              dtype=np.uint64).astype(np.uint16)
+    flat[pad:pad + c.base.size] = c.base.reshape(-1)
+    buf = to_torch(flat, "bf16", DEV)
+    view = buf[pad:pad + c.base.size].view(c.base.shape)
+    dev.fold(view)
+    torch.cuda.synchronize()
+    after = from_torch(buf)
+    assert np.array_equal(after[:pad], flat[:pad])
+    assert np.array_equal(after[pad + c.base.size:], flat[pad + c.base.size:])
+    check(OracleView(c), after[pad:pad + c.base.size].reshape(c.base.shape), c.base, "guard")
+
+
+def test_empty_calls_enqueue_nothing():
+    _need_gpu()
+    from tests.device import DeviceCase
+    c = workloads.make_grouped_case(81, stream_lens=[40], top_k=2, n_route=4, k_in=64,
+                                    n_out=64, max_rank=16, cap=64)
+    dev = DeviceCase(c, DEV)
+    got = dev.run(windows=[(10, 10), (80, 80)])
+    assert np.array_equal(got, c.base)

@@ -1,0 +1,289 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and its host-side integer functions match the oracle bit for bit (golden
+fixtures plus randomized inputs, malformed ones included). Fold argument
+checks that fail before any device work are covered here too."""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import moe_expert_lora_amd as ml
+import oracle
+from tests.common import golden_lines
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+ROUTE_NAME = {ml.MLORA_ROUTE_FOLD: oracle.FOLD, ml.MLORA_ROUTE_SKIP: oracle.SKIP,
+              ml.MLORA_ROUTE_REFUSE: oracle.REFUSE}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ml.load()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mlora.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlora_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = declared_functions()
+    assert set(decl) == set(ml.EXPORTS), (decl, ml.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_m_tile_matches_header():
+    src = open(os.path.join(ROOT, "include", "mlora.h")).read()
+    m = re.search(r"#define\s+MLORA_MLG_M_TILE\s+(\d+)", src)
+    assert ml.mlora_m_tile() == int(m.group(1))
+
+
+def test_route_truth_table_golden():
+    for line in golden_lines("route_truth_table.txt"):
+        slot, active, has, want = line.split()
+        got = ml.mlora_resolve_moe_lora_route(int(slot), int(active), bool(int(has)))
+        assert ROUTE_NAME[got] == want, line
+
+
+def test_route_exhaustive_small():
+    for slot in range(-3, 5):
+        for active in range(-2, 4):
+            for has in (False, True):
+                got = ml.mlora_resolve_moe_lora_route(slot, active, has)
+                assert ROUTE_NAME[got] == oracle.resolve_moe_lora_route(slot, active, has)
+
+
+def test_ensure_decode_route_servable():
+    ml.mlora_ensure_decode_route_servable(ml.MLORA_ROUTE_FOLD)
+    ml.mlora_ensure_decode_route_servable(ml.MLORA_ROUTE_SKIP)
+    with pytest.raises(ml.MloraError) as ei:
+        ml.mlora_ensure_decode_route_servable(ml.MLORA_ROUTE_REFUSE)
+    assert ei.value.code == ml.MLORA_ERR_REFUSE
+    assert "one adapter per batch" in str(ei.value)
+    with pytest.raises(ml.MloraError) as ei:
+        ml.mlora_ensure_decode_route_servable(7)
+    assert ei.value.code == ml.MLORA_ERR_INVALID
+
+
+def _pack_both(entries):
+    ids = [e for e, *_ in entries]
+    a = [x for _, x, _, _ in entries]
+    b = [x for _, _, x, _ in entries]
+    s = [x for *_, x in entries]
+    got = ml.mlora_pack_expert_tables(ids, a, b, s)
+    want = oracle.pack_expert_tables(entries)
+    return got, want
+
+
+def _same_pack(got, want):
+    if want is None:
+        return got is None
+    at, bt, st_, n = got
+    wa, wb, ws, wn = want
+    return (n == wn and at.tolist() == wa and bt.tolist() == wb
+            and st_.view(np.uint32).tolist() == np.asarray(ws, np.float32).view(np.uint32).tolist())
+
+
+def test_pack_golden():
+    for line in golden_lines("pack_expert_tables.txt"):
+        c = json.loads(line)
+        got, want = _pack_both([tuple(e) for e in c["entries"]])
+        assert _same_pack(got, want), line
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 300), st.integers(0, 2**64 - 1),
+                          st.integers(0, 2**64 - 1),
+                          st.floats(allow_nan=False, width=32)), max_size=40))
+def test_pack_matches_oracle(entries):
+    got, want = _pack_both(entries)
+    assert _same_pack(got, want)
+
+
+def test_pack_rejects_bad_ids():
+    for bad in (-1, -100, oracle.MAX_EXPERT_ID + 1, 2**31 - 1):
+        with pytest.raises(ml.MloraError) as ei:
+            ml.mlora_pack_expert_tables([0, bad], [1, 2], [3, 4], [1.0, 1.0])
+        assert ei.value.code == ml.MLORA_ERR_INVALID
+    got = ml.mlora_pack_expert_tables([oracle.MAX_EXPERT_ID], [5], [6], [0.5])
+    assert got[3] == oracle.MAX_EXPERT_ID + 1 and got[0][-1] == 5
+
+
+def test_pack_capacity_leaves_tables(lib):
+    ids = np.array([3, 1], np.int32)
+    a = np.array([11, 12], np.uint64)
+    b = np.array([21, 22], np.uint64)
+    s = np.array([1.0, 2.0], np.float32)
+    at = np.full(2, 99, np.uint64)
+    bt = np.full(2, 99, np.uint64)
+    stt = np.full(2, 9.0, np.float32)
+    n = ctypes.c_int32(-5)
+    P = lambda arr, t: arr.ctypes.data_as(ctypes.POINTER(t))  # noqa: E731
+    rc = lib.mlora_pack_expert_tables(P(ids, ctypes.c_int32), P(a, ctypes.c_uint64),
+                                      P(b, ctypes.c_uint64), P(s, ctypes.c_float), 2,
+                                      P(at, ctypes.c_uint64), P(bt, ctypes.c_uint64),
+                                      P(stt, ctypes.c_float), 2, ctypes.byref(n))
+    assert rc == ml.MLORA_ERR_CAPACITY and n.value == 4
+    assert at.tolist() == [99, 99] and stt.tolist() == [9.0, 9.0]
+
+
+def test_row_adapter_host_golden():
+    for line in golden_lines("row_adapter_host.txt"):
+        c = json.loads(line)
+        got = ml.mlora_build_moe_row_adapter_host(c["cu"], c["slots"])
+        if c["expect"] is None:
+            assert got is None, line
+        else:
+            assert got is not None and got.tolist() == c["expect"], line
+
+
+@settings(max_examples=400, deadline=None)
+@given(st.lists(st.integers(-3, 40), max_size=8), st.lists(st.integers(-2, 5), max_size=8),
+       st.booleans())
+def test_row_adapter_host_matches_oracle(cu, slots, make_valid):
+    if make_valid and cu:
+        cu = [0] + sorted(abs(v) for v in cu)
+        slots = (slots + [1] * len(cu))[: len(cu) - 1]
+    got = ml.mlora_build_moe_row_adapter_host(cu, slots)
+    want = oracle.build_moe_row_adapter_host(cu, slots)
+    if want is None:
+        assert got is None
+    else:
+        assert got is not None and got.tolist() == want
+
+
+def test_row_adapter_host_none_writes_nothing(lib):
+    cu = np.array([0, 4, 2], np.int32)
+    sl = np.array([1, 1], np.int32)
+    out = np.full(8, 77, np.int32)
+    total = ctypes.c_int64(-9)
+    rc = lib.mlora_build_moe_row_adapter_host(
+        cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 3,
+        sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2,
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 8, ctypes.byref(total))
+    assert rc == ml.MLORA_NONE
+    assert out.tolist() == [77] * 8 and total.value == -9
+
+
+def test_row_adapter_decode_golden():
+    for line in golden_lines("row_adapter_decode.txt"):
+        c = json.loads(line)
+        got = ml.mlora_build_moe_row_adapter_decode(c["slots"], c["padded_n"], c["active"],
+                                                    c["has"])
+        assert got.tolist() == c["expect"], line
+
+
+@settings(max_examples=400, deadline=None)
+@given(st.lists(st.integers(-3, 6), max_size=12), st.integers(0, 16), st.integers(-2, 6),
+       st.booleans())
+def test_row_adapter_decode_matches_oracle(slots, padded_n, active, has):
+    got = ml.mlora_build_moe_row_adapter_decode(slots, padded_n, active, has)
+    assert got.tolist() == oracle.build_moe_row_adapter_decode(slots, padded_n, active, has)
+
+
+def test_windows_and_wc_golden():
+    for line in golden_lines("windows.txt"):
+        c = json.loads(line)
+        if "wc" in c:
+            off, end, mt = c["wc"]
+            if mt == ml.mlora_m_tile():
+                assert ml.mlora_grouped_down_wc(off, end) == c["expect"], line
+        elif c["expect"] == "error":
+            with pytest.raises(ml.MloraError) as ei:
+                ml.mlora_grouped_down_windows(c["total"], c["cap"])
+            assert ei.value.code == ml.MLORA_ERR_INVALID
+        else:
+            got = ml.mlora_grouped_down_windows(c["total"], c["cap"])
+            assert [list(w) for w in got] == c["expect"], line
+
+
+@settings(max_examples=400, deadline=None)
+@given(st.integers(0, 100000), st.integers(1, 20000))
+def test_windows_match_oracle(total, cap):
+    assert ml.mlora_grouped_down_windows(total, cap) == oracle.grouped_down_windows(total, cap)
+
+
+@settings(max_examples=400, deadline=None)
+@given(st.integers(0, 10**7), st.integers(-100, 10**5))
+def test_wc_matches_oracle(off, length):
+    m = ml.mlora_m_tile()
+    assert ml.mlora_grouped_down_wc(off, off + length) == oracle.grouped_down_wc(off, off + length, m)
+
+
+def test_windows_negative_cap():
+    for cap in (0, -1):
+        with pytest.raises(ml.MloraError):
+            ml.mlora_grouped_down_windows(10, cap)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.integers(0, 2**31 - 1), st.integers(1, 64))
+def test_row_token_matches_oracle(row, top_k):
+    assert ml.mlora_gather_row_token(row, top_k) == oracle.gather_row_token(row, top_k)
+
+
+def test_row_token_invalid():
+    assert ml.mlora_gather_row_token(3, 0) == -1
+    assert ml.mlora_gather_row_token(-1, 2) == -1
+
+
+# ---- fold argument checks that fail before any device work ----------------
+
+def _route(**kw):
+    f = dict(a_table=1 << 20, b_table=1 << 21, scale_table=1 << 22, n_experts=4, k_in=64,
+             n_out=32, max_rank=8, dtype=ml.MLORA_BF16)
+    f.update(kw)
+    return ml.ExpertRoute(f["a_table"], f["b_table"], f["scale_table"], f["n_experts"],
+                          f["k_in"], f["n_out"], f["max_rank"], f["dtype"])
+
+
+FAKE = 1 << 24  # never dereferenced: every call below is rejected before launch
+
+
+@pytest.mark.parametrize("kw", [dict(k_in=60), dict(n_out=0), dict(max_rank=0),
+                                dict(max_rank=129), dict(dtype=7), dict(n_experts=-1),
+                                dict(a_table=0)])
+def test_gather_rejects_bad_route(lib, kw):
+    r = _route(**kw)
+    rc = lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, 8, 2, None)
+    assert rc == ml.MLORA_ERR_INVALID
+    assert ml.load().mlora_last_error()
+
+
+def test_gather_rejects_bad_args(lib):
+    r = _route()
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, 8, 0, None) == -1
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 3, FAKE, FAKE, FAKE, 8, 2, None) == -1
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, -1, 2, None) == -1
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), None, 4, FAKE, FAKE, FAKE, 8, 2, None) == -1
+    # nothing to fold: accepted without touching the device
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 0, FAKE, FAKE, FAKE, 0, 2, None) == 0
+    r0 = _route(n_experts=0)
+    assert lib.mlora_gather_bgmv(ctypes.byref(r0), FAKE, 4, FAKE, FAKE, FAKE, 8, 2, None) == 0
+
+
+def test_grouped_rejects_bad_args(lib):
+    r = _route()
+    call = lambda **k: lib.mlora_grouped_down(  # noqa: E731
+        ctypes.byref(k.get("route", r)), FAKE, k.get("n_tok", 4), FAKE, k.get("n_rows", 8),
+        FAKE, k.get("n_route", 4), FAKE, FAKE, k.get("top_k", 2), k.get("off", 0),
+        k.get("end", 8), None)
+    assert call(top_k=0) == -1
+    assert call(off=5, end=4) == -1
+    assert call(end=9) == -1
+    assert call(off=-1) == -1
+    assert call(n_route=-1) == -1
+    assert call(n_tok=-1) == -1
+    assert call(route=_route(max_rank=200)) == -1
+    assert call(off=3, end=3) == 0          # empty window
+    assert call(n_route=0) == 0             # no spans
