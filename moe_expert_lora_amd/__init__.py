@@ -87,6 +87,12 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with "
                           "`python -m moe_expert_lora_amd.build`")
+    # PyTorch ships its own HIP runtime; load it first so that this library
+    # binds to the same runtime instance that owns the tensors and streams.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, u32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p
     sig = {

@@ -20,6 +20,10 @@
 //    of 8 consecutive output columns of one row, so base_out is read and
 //    written with 16-byte accesses, 64 contiguous bytes per row per
 //    instruction, and never staged through LDS.
+//  * Every operand moves through raw buffer loads/stores: 32-bit offsets, and
+//    a masked lane simply uses an offset past the buffer (its load returns 0,
+//    its store is dropped), so no access needs a branch. Loads are issued in
+//    batches and consumed after one wait.
 //  * Gather rows are grouped by expert on the device: each workgroup scans a
 //    slice of `indices` for its expert, so each A_e / B_e is streamed from HBM
 //    once per workgroup group and reused across that expert's rows.
@@ -43,14 +47,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTileRows = MLORA_MLG_M_TILE;
 constexpr int kColStep = 32;     // output columns per expand step of one wave
 constexpr int kScanMax = 2048;   // gather rows scanned by one workgroup
-constexpr int kMaxSegs = kTileRows;
 constexpr int kXcds = 8;
+// Largest buffer one resource may describe; every offset stays below it.
+constexpr uint32_t kMaxBufBytes = 0xFFFFFF00u;
+// An offset past every buffer: a load there returns 0, a store is dropped.
+constexpr uint32_t kOOB = 0xFFFFFFF0u;
 
 static_assert(kTileRows == 64, "grouped tiles are 64 rows (4 row blocks of 16)");
 
@@ -58,32 +66,68 @@ static_assert(kTileRows == 64, "grouped tiles are 64 rows (4 row blocks of 16)")
 // scalar helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 -> two bf16 in one word (low half = a), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-__device__ __forceinline__ u32x4 ld16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+// bf16 pair word -> its low / high value as fp32 (exact).
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// n / d for 0 <= n < 2^31 and d >= 1, with magic = floor((2^32 - 1) / d): the
+// high product is the quotient or one less, and one step corrects it.
+__device__ __forceinline__ uint32_t udiv(uint32_t n, uint32_t d, uint32_t magic) {
+  uint32_t q = __umulhi(n, magic);
+  if ((q + 1) * d <= n) q += 1;
+  return q;
 }
-__device__ __forceinline__ u32x2 ld8(const void* p) {
-  return *reinterpret_cast<const u32x2*>(p);
+
+// buffer resource (gfx9 family descriptor word 3: raw, 32-bit data format)
+__device__ __forceinline__ rsrc_t make_buf(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bld4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void bst16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
+}
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// A value every lane of the wave holds, moved to scalar registers. Buffer
+// descriptors built from scalar values need no per-lane handling, while one
+// built from a vector register makes the compiler loop over lanes per access.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+}
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Appends `val` pairs of the lanes whose `pred` is set to LDS lists, in one
-// LDS atomic per wave. Order across waves is unspecified; nothing downstream
+// Appends (v0, v1) of the lanes whose `pred` is set to LDS lists, in one LDS
+// atomic per wave. Order across waves is unspecified; nothing downstream
 // depends on it (every row is computed independently).
 __device__ __forceinline__ void wave_append(bool pred, int v0, int v1, int* cnt, int* l0,
                                             int* l1, int cap) {
@@ -103,15 +147,47 @@ __device__ __forceinline__ void wave_append(bool pred, int v0, int v1, int* cnt,
   }
 }
 
+// Workgroup barrier that orders LDS only. Every cross-wave exchange in these
+// kernels goes through LDS (each base_out element is read and written by one
+// lane), so outstanding global loads, such as prefetches, stay in flight
+// across it instead of being drained.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // the per-expert tile engine
 // ---------------------------------------------------------------------------
 
-// B_e fragment of one expand step: for each of the 2 column blocks, the lane's
-// 4*NB ranks (rank g*4NB .. g*4NB+4NB-1) of one B_e row, as 2*NB words.
+// Buffers of one fold_rows call.
+struct Bufs {
+  rsrc_t x;    // [n_tokens, K]
+  rsrc_t a;    // A_e [R, K]
+  rsrc_t b;    // B_e [N, R]
+  rsrc_t out;  // base_out rows addressed by this call
+};
+
+// Expand operands. After the shrink, lane group g of each row holds the 4*NB
+// consecutive ranks g*4NB .. g*4NB+4NB-1 (the rank permutation of the shrink
+// puts them there). The expand contracts over ranks in chunks: a chunk is the
+// 8 ranks (NB >= 2, one 16x16x32 MFMA) or 4 ranks (NB == 1, one 16x16x16
+// MFMA) a lane group holds at one position, so a lane's B_e words load
+// straight into an MFMA operand with no rearrangement, and hi and lo of H
+// each take one MFMA per chunk.
+template <int NB>
+struct Chunk {
+  static constexpr int kRanks = NB == 1 ? 4 : 8;       // ranks per lane per chunk
+  static constexpr int kCount = 4 * NB / kRanks;       // chunks per lane
+  static constexpr int kWords = kRanks / 2;            // bf16 pairs per chunk
+};
+
+// B_e fragment of one expand step: for each of the 2 column blocks and each
+// rank chunk, the lane's kRanks bf16 of one B_e row.
 template <int NB>
 struct BFrag {
-  uint32_t w[2][2 * NB];
+  uint32_t w[2][Chunk<NB>::kCount][Chunk<NB>::kWords];
 };
 
 // Output column (relative to the step start) of MFMA row `mi` in column block
@@ -122,106 +198,225 @@ __device__ __forceinline__ int col_of(int cb, int mi) {
 }
 
 template <int NB, bool FULL_R>
-__device__ __forceinline__ void load_bfrag(BFrag<NB>& f, const uint16_t* __restrict__ B, int R,
-                                           int c0, int n_hi, int li, int g) {
+__device__ __forceinline__ void load_bfrag(BFrag<NB>& f, rsrc_t rb, int R, int c0, int n_hi,
+                                           int li, int g) {
+  constexpr int CR = Chunk<NB>::kRanks, CC = Chunk<NB>::kCount, CW = Chunk<NB>::kWords;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int col = c0 + col_of(cb, li);
-    if (col < n_hi) {
-      const uint16_t* p = B + (size_t)col * R + g * 4 * NB;
-      if constexpr (FULL_R) {
-        if constexpr (NB == 1) {
-          const u32x2 v = ld8(p);
-          f.w[cb][0] = v.x;
-          f.w[cb][1] = v.y;
-        } else {
+    const bool ok = col < n_hi;
 #pragma unroll
-          for (int q = 0; q < NB / 2; ++q) {
-            const u32x4 v = ld16(p + 8 * q);
-            f.w[cb][4 * q + 0] = v.x;
-            f.w[cb][4 * q + 1] = v.y;
-            f.w[cb][4 * q + 2] = v.z;
-            f.w[cb][4 * q + 3] = v.w;
-          }
+    for (int q = 0; q < CC; ++q) {
+      const int r0 = g * 4 * NB + q * CR;  // first rank of the chunk
+      const uint32_t base = (uint32_t)(col * R + r0) * 2u;
+      if constexpr (FULL_R) {
+        if constexpr (CW == 2) {
+          const u32x2 v = bld8(rb, ok ? base : kOOB);
+          f.w[cb][q][0] = v.x;
+          f.w[cb][q][1] = v.y;
+        } else {
+          const u32x4 v = bld16(rb, ok ? base : kOOB);
+          f.w[cb][q][0] = v.x;
+          f.w[cb][q][1] = v.y;
+          f.w[cb][q][2] = v.z;
+          f.w[cb][q][3] = v.w;
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 2 * NB; ++q) {
-          const int r0 = g * 4 * NB + 2 * q;
-          const uint32_t lo = (r0 < R) ? p[2 * q] : 0u;
-          const uint32_t hi = (r0 + 1 < R) ? p[2 * q + 1] : 0u;
-          f.w[cb][q] = lo | (hi << 16);
+        for (int j = 0; j < CW; ++j) {
+          const int r = r0 + 2 * j;
+          const uint32_t lo = bld2(rb, (ok && r < R) ? base + 4u * j : kOOB);
+          const uint32_t hi = bld2(rb, (ok && r + 1 < R) ? base + 4u * j + 2u : kOOB);
+          f.w[cb][q][j] = (lo & 0xffffu) | (hi << 16);
         }
       }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 2 * NB; ++q) f.w[cb][q] = 0u;
     }
   }
 }
 
-// base_out fragment of one expand step: per row block, the lane's run of 8
-// columns (16 bytes).
-template <int MB>
-struct OutFrag {
-  u32x4 v[MB];
+// H operands of one row block: hi and lo halves of scale * H, per chunk.
+template <int NB>
+struct HOp {
+  uint32_t hi[Chunk<NB>::kCount][Chunk<NB>::kWords];
+  uint32_t lo[Chunk<NB>::kCount][Chunk<NB>::kWords];
 };
 
+// One chunk's MFMA: 16x16x32 for 8 ranks, 16x16x16 for 4.
+template <int CW>
+__device__ __forceinline__ f32x4 mfma_chunk(const uint32_t (&a)[CW], const uint32_t (&b)[CW],
+                                            f32x4 c) {
+  if constexpr (CW == 4) {
+    return mfma16x16x32(as_bf(u32x4{a[0], a[1], a[2], a[3]}),
+                        as_bf(u32x4{b[0], b[1], b[2], b[3]}), c);
+  } else {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        __builtin_bit_cast(s16x4, u32x2{a[0], a[1]}), __builtin_bit_cast(s16x4, u32x2{b[0], b[1]}),
+        c, 0, 0, 0);
+  }
+}
+
+// Loads are issued in batches: the k steps of one shrink batch (A_e and x
+// fragments) or the column steps of one expand batch (B_e and base_out
+// fragments) are requested together and consumed after a single wait. Two
+// batch buffers alternate, so the next batch is in flight while the current
+// one is multiplied: a wave always has memory requests outstanding. The batch
+// sizes bound the VGPRs a buffer holds.
+#ifndef MLORA_BATCH_VGPRS
+#define MLORA_BATCH_VGPRS 40
+#endif
+
+constexpr int cclamp(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+template <int NB, int MB>
+struct Batch {
+  static constexpr int US = cclamp(MLORA_BATCH_VGPRS / (4 * (NB + MB)), 1, 8);
+  static constexpr int UE = cclamp(MLORA_BATCH_VGPRS / (4 * (NB + MB)), 1, 8);
+};
+
+template <int NB, int MB, int US>
+struct ShrinkBatch {
+  u32x4 a[US][NB];
+  u32x4 x[US][MB];
+};
+
+template <int NB, int MB, int UE>
+struct ExpandBatch {
+  BFrag<NB> b[UE];
+  u32x4 o[UE][MB];
+};
+
+// Per-lane row state of one fold_rows call.
 template <int MB>
-__device__ __forceinline__ void load_out(OutFrag<MB>& f, const uint16_t* const (&orowp)[MB],
-                                         const bool (&valid)[MB], int nrb, int col, int n_hi) {
+struct Rows {
+  uint32_t xoff[MB];  // byte offset of the row's token in x
+  uint32_t ooff[MB];  // byte offset of the row in base_out
+  bool valid[MB];
+};
+
+template <int NB, int MB, int US>
+__device__ __forceinline__ void load_shrink(ShrinkBatch<NB, MB, US>& sb, const Bufs& bf, int K,
+                                            int R, const Rows<MB>& rw, int s0, int nks,
+                                            int li, int g) {
 #pragma unroll
-  for (int rb = 0; rb < MB; ++rb) {
-    if (rb < nrb) {
-      if (valid[rb] && col < n_hi)
-        f.v[rb] = ld16(orowp[rb] + col);
-      else
-        f.v[rb] = u32x4{0u, 0u, 0u, 0u};
+  for (int u = 0; u < US; ++u) {
+    const int s = s0 + u * kWaves;
+    const int k0 = s * 32 + g * 8;
+    const bool kin = s < nks && k0 < K;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
+      sb.a[u][b] = bld16(bf.a, (kin && rank < R) ? (uint32_t)(rank * K + k0) * 2u : kOOB);
+    }
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+      sb.x[u][rb] = bld16(bf.x, (kin && rw.valid[rb]) ? rw.xoff[rb] + 2u * k0 : kOOB);
+  }
+}
+
+template <int NB, int MB, int US>
+__device__ __forceinline__ void mma_shrink(f32x4 (&hacc)[MB][NB],
+                                           const ShrinkBatch<NB, MB, US>& sb, int nrb) {
+#pragma unroll
+  for (int u = 0; u < US; ++u) {
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      if (rb < nrb) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          hacc[rb][b] = mfma16x16x32(as_bf(sb.a[u][b]), as_bf(sb.x[u][rb]), hacc[rb][b]);
+      }
     }
   }
 }
 
-// Folds rows 0..nrows-1 (nrows <= 16*MB) of expert (A, B, scale) into columns
+template <int NB, int MB, int UE, bool FULL_R>
+__device__ __forceinline__ void load_expand(ExpandBatch<NB, MB, UE>& eb, const Bufs& bf, int R,
+                                            const Rows<MB>& rw, int cs0, int ncs, int n_lo,
+                                            int n_hi, int li, int g) {
+#pragma unroll
+  for (int u = 0; u < UE; ++u) {
+    const int cs = cs0 + u * kWaves;
+    const int c0 = n_lo + cs * kColStep;
+    load_bfrag<NB, FULL_R>(eb.b[u], bf.b, R, c0, cs < ncs ? n_hi : 0, li, g);
+    const int col = c0 + 8 * g;
+    const bool cok = cs < ncs && col < n_hi;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+      eb.o[u][rb] = bld16(bf.out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
+  }
+}
+
+// delta = B_e . (hi + lo) for the batch's columns, added to base_out, stored.
+template <int NB, int MB, int UE>
+__device__ __forceinline__ void mma_store_expand(const ExpandBatch<NB, MB, UE>& eb,
+                                                 const HOp<NB> (&hop)[MB], const Bufs& bf,
+                                                 const Rows<MB>& rw, int nrb, int cs0, int ncs,
+                                                 int n_lo, int n_hi, int g) {
+  constexpr int CC = Chunk<NB>::kCount;
+#pragma unroll
+  for (int u = 0; u < UE; ++u) {
+    const int cs = cs0 + u * kWaves;
+    const int col = n_lo + cs * kColStep + 8 * g;
+    const bool cok = cs < ncs && col < n_hi;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      if (rb < nrb) {
+        f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < CC; ++q) {
+          d0 = mfma_chunk(eb.b[u].w[0][q], hop[rb].hi[q], d0);
+          d1 = mfma_chunk(eb.b[u].w[1][q], hop[rb].hi[q], d1);
+          d0 = mfma_chunk(eb.b[u].w[0][q], hop[rb].lo[q], d0);
+          d1 = mfma_chunk(eb.b[u].w[1][q], hop[rb].lo[q], d1);
+        }
+        const u32x4 bq = eb.o[u][rb];
+        const uint32_t o0 = pack_bf16(lo_f(bq.x) + d0.x, hi_f(bq.x) + d0.y);
+        const uint32_t o1 = pack_bf16(lo_f(bq.y) + d0.z, hi_f(bq.y) + d0.w);
+        const uint32_t o2 = pack_bf16(lo_f(bq.z) + d1.x, hi_f(bq.z) + d1.y);
+        const uint32_t o3 = pack_bf16(lo_f(bq.w) + d1.z, hi_f(bq.w) + d1.w);
+        bst16(bf.out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB,
+              u32x4{o0, o1, o2, o3});
+      }
+    }
+  }
+}
+
+// Folds rows 0..nrows-1 (nrows <= 16*MB) of one expert into columns
 // [n_lo, n_hi) of base_out. Row m writes base_out row
-// (s_row ? s_row[m] : row_base + m) from token s_tok[m] (negative: dead row).
+// (s_row ? s_row[m] : row_base + m) of bf.out, from token s_tok[m]
+// (negative: a dead row, neither read nor written).
 // All threads of the workgroup must call it with the same arguments.
 template <int NB, int MB, bool FULL_R>
-__device__ void fold_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__ out, int K,
-                          int N, int R, const uint16_t* __restrict__ A,
-                          const uint16_t* __restrict__ B, float scale,
-                          const int* s_row, int64_t row_base, const int* s_tok, int nrows,
-                          int n_lo, int n_hi, float* s_part) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ void fold_rows(const Bufs& bf, int K, int N, int R, float scale, const int* s_row,
+                          int row_base, const int* s_tok, int nrows, int n_lo, int n_hi,
+                          float* s_part) {
+  constexpr int US = Batch<NB, MB>::US;
+  constexpr int UE = Batch<NB, MB>::UE;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
   const int nrb = (nrows + 15) >> 4;
 
-  const uint16_t* xrow[MB];
-  const uint16_t* orowp[MB];
-  bool valid[MB];
+  Rows<MB> rw;
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb) {
     const int m = rb * 16 + li;
-    int t = -1;
-    int64_t r = 0;
+    int t = -1, r = 0;
     if (m < nrows) {
       t = s_tok[m];
-      r = s_row ? (int64_t)s_row[m] : row_base + m;
+      r = s_row ? s_row[m] : row_base + m;
     }
-    valid[rb] = t >= 0;
-    xrow[rb] = x + (size_t)(t < 0 ? 0 : t) * K;
-    orowp[rb] = out + (size_t)r * N;
+    rw.valid[rb] = t >= 0;
+    rw.xoff[rb] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)K * 2u;
+    rw.ooff[rb] = (uint32_t)r * (uint32_t)N * 2u;
   }
 
-  // The first expand step's operands do not depend on the shrink: issue them
-  // now so their latency hides behind it.
+  // The first expand batch does not depend on the shrink: request it now so
+  // its latency hides behind the shrink.
   const int ncs = (n_hi - n_lo + kColStep - 1) / kColStep;
-  BFrag<NB> bcur;
-  OutFrag<MB> ocur;
-  if (wave < ncs) {
-    const int c0 = n_lo + wave * kColStep;
-    load_bfrag<NB, FULL_R>(bcur, B, R, c0, n_hi, li, g);
-    load_out<MB>(ocur, orowp, valid, nrb, c0 + 8 * g, n_hi);
-  }
+  ExpandBatch<NB, MB, UE> e0, e1;
+  load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, wave, ncs, n_lo, n_hi, li, g);
 
   // ---- shrink: H[rank][row] over this wave's k steps ----------------------
   f32x4 hacc[MB][NB];
@@ -231,23 +426,23 @@ __device__ void fold_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__
     for (int b = 0; b < NB; ++b) hacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nks = (K + 31) >> 5;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  for (int s = wave; s < nks; s += kWaves) {
-    const int k0 = s * 32 + g * 8;
-    const bool kin = k0 < K;
-    bf16x8 af[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
-      af[b] = as_bf((kin && rank < R) ? ld16(A + (size_t)rank * K + k0) : zero4);
-    }
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-      if (rb < nrb) {
-        const bf16x8 xf = as_bf((kin && valid[rb]) ? ld16(xrow[rb] + k0) : zero4);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) hacc[rb][b] = mfma16x16x32(af[b], xf, hacc[rb][b]);
-      }
+  {
+    constexpr int kStep = kWaves * US;
+    // The next batch is requested before the current one is used, without a
+    // condition: steps past the end load nothing (their offsets are out of
+    // range), and straight-line code keeps the wait counts exact.
+    ShrinkBatch<NB, MB, US> s0b, s1b;
+    int s0 = wave;
+    load_shrink<NB, MB, US>(s0b, bf, K, R, rw, s0, nks, li, g);
+    while (s0 < nks) {
+      const int s1 = s0 + kStep;
+      load_shrink<NB, MB, US>(s1b, bf, K, R, rw, s1, nks, li, g);
+      mma_shrink<NB, MB, US>(hacc, s0b, nrb);
+      if (s1 >= nks) break;
+      const int s2 = s1 + kStep;
+      load_shrink<NB, MB, US>(s0b, bf, K, R, rw, s2, nks, li, g);
+      mma_shrink<NB, MB, US>(hacc, s1b, nrb);
+      s0 = s2;
     }
   }
 
@@ -262,10 +457,10 @@ __device__ void fold_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__
         *reinterpret_cast<f32x4*>(dst + 4 * b) = hacc[rb][b];
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // H' operands: per row block and k step s, {hi[4s..4s+3], lo[4s..4s+3]}.
-  u32x4 hop[MB][NB];
+  // hi / lo operands of scale * H, chunk by chunk (4 ranks at a time here).
+  HOp<NB> hop[MB];
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb) {
     if (rb < nrb) {
@@ -277,63 +472,60 @@ __device__ void fold_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__
         for (int w = 1; w < kWaves; ++w)
           h += *reinterpret_cast<const f32x4*>(
               s_part + ((size_t)(w * MB + rb) * 64 + lane) * HW + 4 * s);
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v = scale * h[q];
-          hi[q] = f2bf(v);
-          lo[q] = f2bf(v - bf2f(hi[q]));
-        }
-        hop[rb][s] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                           lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+        const f32x4 v = scale * h;
+        const uint32_t hi01 = pack_bf16(v.x, v.y), hi23 = pack_bf16(v.z, v.w);
+        const uint32_t lo01 = pack_bf16(v.x - lo_f(hi01), v.y - hi_f(hi01));
+        const uint32_t lo23 = pack_bf16(v.z - lo_f(hi23), v.w - hi_f(hi23));
+        // ranks 4s .. 4s+3 of this lane: chunk (4s) / kRanks, word offset inside it
+        constexpr int CR = Chunk<NB>::kRanks;
+        const int q = (4 * s) / CR, w0 = ((4 * s) % CR) / 2;
+        hop[rb].hi[q][w0] = hi01;
+        hop[rb].hi[q][w0 + 1] = hi23;
+        hop[rb].lo[q][w0] = lo01;
+        hop[rb].lo[q][w0 + 1] = lo23;
       }
     }
   }
 
-  // ---- expand + read-modify-write ------------------------------------------
-  for (int cs = wave; cs < ncs; cs += kWaves) {
-    const int col = n_lo + cs * kColStep + 8 * g;
-    BFrag<NB> bnext;
-    OutFrag<MB> onext;
-    const bool more = cs + kWaves < ncs;
-    if (more) {
-      const int c1 = n_lo + (cs + kWaves) * kColStep;
-      load_bfrag<NB, FULL_R>(bnext, B, R, c1, n_hi, li, g);
-      load_out<MB>(onext, orowp, valid, nrb, c1 + 8 * g, n_hi);
-    }
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-      if (rb < nrb) {
-        f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NB; ++s) {
-          const bf16x8 hb = as_bf(hop[rb][s]);
-          const uint32_t a0 = bcur.w[0][2 * s], a1 = bcur.w[0][2 * s + 1];
-          const uint32_t b0 = bcur.w[1][2 * s], b1 = bcur.w[1][2 * s + 1];
-          d0 = mfma16x16x32(as_bf(u32x4{a0, a1, a0, a1}), hb, d0);
-          d1 = mfma16x16x32(as_bf(u32x4{b0, b1, b0, b1}), hb, d1);
-        }
-        if (valid[rb] && col < n_hi) {
-          const u32x4 bv = ocur.v[rb];
-          const uint32_t o0 = f2bf(bf2f(bv.x & 0xffffu) + d0.x) |
-                              (f2bf(bf2f(bv.x >> 16) + d0.y) << 16);
-          const uint32_t o1 = f2bf(bf2f(bv.y & 0xffffu) + d0.z) |
-                              (f2bf(bf2f(bv.y >> 16) + d0.w) << 16);
-          const uint32_t o2 = f2bf(bf2f(bv.z & 0xffffu) + d1.x) |
-                              (f2bf(bf2f(bv.z >> 16) + d1.y) << 16);
-          const uint32_t o3 = f2bf(bf2f(bv.w & 0xffffu) + d1.z) |
-                              (f2bf(bf2f(bv.w >> 16) + d1.w) << 16);
-          st16(const_cast<uint16_t*>(orowp[rb]) + col, u32x4{o0, o1, o2, o3});
-        }
-      }
-    }
-    if (more) {
-      bcur = bnext;
-      ocur = onext;
+  // ---- expand + read-modify-write, two batches in flight -------------------
+  {
+    constexpr int kStep = kWaves * UE;
+    int c0 = wave;
+    while (c0 < ncs) {
+      const int c1 = c0 + kStep;
+      load_expand<NB, MB, UE, FULL_R>(e1, bf, R, rw, c1, ncs, n_lo, n_hi, li, g);
+      mma_store_expand<NB, MB, UE>(e0, hop, bf, rw, nrb, c0, ncs, n_lo, n_hi, g);
+      if (c1 >= ncs) break;
+      const int c2 = c1 + kStep;
+      load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, c2, ncs, n_lo, n_hi, li, g);
+      mma_store_expand<NB, MB, UE>(e1, hop, bf, rw, nrb, c1, ncs, n_lo, n_hi, g);
+      c0 = c2;
     }
   }
   // s_part and the caller's row lists are reused by the next call.
-  __syncthreads();
+  lds_barrier();
+}
+
+// Requests the cache lines of `bytes` bytes of buffer `r` (one 4-byte load per
+// 128-byte line, NT lines per thread) so that HBM fetches of an expert's
+// weights start while the workgroup is still resolving its rows. Loads past
+// the buffer return 0 without touching memory. The loaded words are kept, and
+// consumed by an empty asm at the end of the kernel, only so the loads are not
+// removed; no wave waits for them earlier.
+template <int NT>
+__device__ __forceinline__ void touch_lines(rsrc_t r, uint32_t first_byte, uint32_t bytes,
+                                            uint32_t (&keep)[NT]) {
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const uint32_t off = ((uint32_t)i * kThreads + threadIdx.x) * 128u;
+    keep[i] = bld4(r, off < bytes ? first_byte + off : kOOB);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void consume(const uint32_t (&keep)[NT]) {
+#pragma unroll
+  for (int i = 0; i < NT; ++i) asm volatile("" ::"v"(keep[i]));
 }
 
 // ---------------------------------------------------------------------------
@@ -348,13 +540,15 @@ struct GatherArgs {
   const uint64_t* a_table;
   const uint64_t* b_table;
   const float* scale_table;
-  int32_t n_experts, K, N, R, n_slots, top_k;
-  int32_t rs_count;   // row slices per expert
-  int32_t ns_count;   // column slices per expert
-  int32_t scan_len;   // rows per row slice (<= kScanMax)
-  int32_t ns_cols;    // columns per column slice (multiple of kColStep)
-  int32_t units;      // n_experts * rs_count * ns_count
-  int32_t per_xcd;    // ceil(units / kXcds)
+  uint32_t x_bytes, out_bytes;
+  int32_t n_experts, K, N, R, n_slots, top_k, n_tokens;
+  uint32_t top_k_magic;  // floor((2^32 - 1) / top_k)
+  int32_t rs_count;      // row slices per expert
+  int32_t ns_count;      // column slices per expert
+  int32_t scan_len;      // rows per row slice (<= kScanMax)
+  int32_t ns_cols;       // columns per column slice (multiple of kColStep)
+  int32_t units;         // n_experts * rs_count * ns_count
+  int32_t per_xcd;       // ceil(units / kXcds)
 };
 
 template <int NB, int MB, bool FULL_R>
@@ -373,44 +567,60 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
   const int within = u - e * per_e;
   const int rs = within / p.ns_count, ns = within - rs * p.ns_count;
 
-  const uint64_t a_addr = p.a_table[e], b_addr = p.b_table[e];
-  if (a_addr == 0 || b_addr == 0) return;
-  const float scale = p.scale_table[e];
+  const uint64_t a_addr = uniform_u64(p.a_table[e]), b_addr = uniform_u64(p.b_table[e]);
+  const float scale = uniform_f32(p.scale_table[e]);
 
-  if (threadIdx.x == 0) s_cnt = 0;
-  __syncthreads();
-
-  // Rows of this slice routed to e with a live adapter map entry.
+  // This slice's routing, requested together with the table cells.
+  const rsrc_t r_idx = make_buf(p.indices, (uint32_t)p.n_slots * 4u);
+  const rsrc_t r_map = make_buf(p.row_adapter, (uint32_t)p.n_tokens * 4u);
   const int start = rs * p.scan_len;
   const int end = min(start + p.scan_len, p.n_slots);
   constexpr int kPer = kScanMax / kThreads;
+  const int rounds = (end - start + kThreads - 1) / kThreads;  // wave-uniform, <= kPer
   int iv[kPer], mv[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int row = start + i * kThreads + (int)threadIdx.x;
     iv[i] = -1;
     mv[i] = -1;
-    if (row < end) {
-      iv[i] = p.indices[row];
-      mv[i] = p.row_adapter[row / p.top_k];
+    if (i < rounds) {
+      const int row = start + i * kThreads + (int)threadIdx.x;
+      const bool in = row < end;
+      const uint32_t tok = udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
+      iv[i] = (int)bld4(r_idx, in ? (uint32_t)row * 4u : kOOB);
+      mv[i] = (int)bld4(r_map, in ? tok * 4u : kOOB);
     }
   }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int row = start + i * kThreads + (int)threadIdx.x;
-    const bool hit = row < end && iv[i] == e && mv[i] >= 0;
-    wave_append(hit, row, row / p.top_k, &s_cnt, s_rows, s_toks, kScanMax);
-  }
-  __syncthreads();
-  const int n = s_cnt;
+  if (a_addr == 0 || b_addr == 0) return;
 
   const int n_lo = ns * p.ns_cols;
   const int n_hi = min(n_lo + p.ns_cols, p.N);
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(a_addr);
-  const uint16_t* B = reinterpret_cast<const uint16_t*>(b_addr);
+  Bufs bf;
+  bf.x = make_buf(p.x, p.x_bytes);
+  bf.a = make_buf(reinterpret_cast<const void*>(a_addr), (uint32_t)(p.R * p.K) * 2u);
+  bf.b = make_buf(reinterpret_cast<const void*>(b_addr), (uint32_t)(p.N * p.R) * 2u);
+  bf.out = make_buf(p.out, p.out_bytes);
+  // Start the HBM fetch of this slice's weights while the rows are resolved.
+  uint32_t keep_a[2], keep_b[2];
+  touch_lines(bf.a, 0u, (uint32_t)(p.R * p.K) * 2u, keep_a);
+  touch_lines(bf.b, (uint32_t)(n_lo * p.R) * 2u, (uint32_t)((n_hi - n_lo) * p.R) * 2u, keep_b);
+
+  if (threadIdx.x == 0) s_cnt = 0;
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (i >= rounds) break;
+    const int row = start + i * kThreads + (int)threadIdx.x;
+    const bool hit = row < end && iv[i] == e && mv[i] >= 0;
+    const int tok = (int)udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
+    wave_append(hit, row, tok, &s_cnt, s_rows, s_toks, kScanMax);
+  }
+  lds_barrier();
+  const int n = __builtin_amdgcn_readfirstlane(s_cnt);
   for (int c = 0; c < n; c += 16 * MB)
-    fold_rows<NB, MB, FULL_R>(p.x, p.out, p.K, p.N, p.R, A, B, scale, s_rows + c, 0,
-                              s_toks + c, min(16 * MB, n - c), n_lo, n_hi, s_part);
+    fold_rows<NB, MB, FULL_R>(bf, p.K, p.N, p.R, scale, s_rows + c, 0, s_toks + c,
+                              min(16 * MB, n - c), n_lo, n_hi, s_part);
+  consume(keep_a);
+  consume(keep_b);
 }
 
 // ---------------------------------------------------------------------------
@@ -419,34 +629,42 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
 
 struct GroupedArgs {
   const uint16_t* x;
-  uint16_t* out;
+  uint16_t* out;  // base_out row row_offset (the window start)
   const int32_t* offsets;
   const int32_t* sorted_ids;
   const int32_t* row_adapter;
   const uint64_t* a_table;
   const uint64_t* b_table;
   const float* scale_table;
+  uint32_t x_bytes, out_bytes;
   int64_t row_offset, row_end;
   int32_t n_experts, K, N, R, n_route, top_k, n_tokens;
-  int32_t n_tiles, ns_count, ns_cols, units, per_xcd;
+  uint32_t top_k_magic;
+  int32_t n_tiles, ns_count, ns_cols, units, per_xcd;  // units = tiles * sub-tiles * ns
 };
 
+// One workgroup folds a sub-tile of 16*MB rows of one MLORA_MLG_M_TILE-row
+// tile (4 / MB sub-tiles per tile), over one column slice.
 template <int NB, int MB, bool FULL_R>
 __global__ __launch_bounds__(kThreads) void grouped_fold_kernel(GroupedArgs p) {
+  constexpr int kSub = kTileRows / (16 * MB);  // sub-tiles per tile
+  constexpr int kRows = 16 * MB;               // rows per sub-tile
   __shared__ float s_part[kWaves * MB * 64 * 4 * NB];
-  __shared__ int s_tok[kTileRows];
-  __shared__ int s_seg_e[kMaxSegs], s_seg_lo[kMaxSegs], s_seg_hi[kMaxSegs];
+  __shared__ int s_tok[kRows];
+  __shared__ int s_seg_e[kRows], s_seg_lo[kRows], s_seg_hi[kRows];
   __shared__ int s_nseg;
 
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int u = xcd * p.per_xcd + slot;
   if (u >= p.units) return;
-  const int t = u / p.ns_count, ns = u - t * p.ns_count;
-  const int64_t r0 = p.row_offset + (int64_t)t * kTileRows;
-  const int64_t r1 = min(r0 + kTileRows, p.row_end);
+  const int ns = u % p.ns_count;
+  const int ts = u / p.ns_count;  // sub-tile index within the window
+  const int64_t r0 = p.row_offset + (int64_t)(ts / kSub) * kTileRows + (ts % kSub) * kRows;
+  if (r0 >= p.row_end) return;
+  const int64_t r1 = min(r0 + kRows, p.row_end);
 
   if (threadIdx.x == 0) s_nseg = 0;
-  __syncthreads();
+  lds_barrier();
 
   // Expert spans that meet this tile, clipped to it.
   for (int e = threadIdx.x; e < p.n_route; e += kThreads) {
@@ -454,43 +672,50 @@ __global__ __launch_bounds__(kThreads) void grouped_fold_kernel(GroupedArgs p) {
     const int64_t hi = min((int64_t)p.offsets[e + 1], r1);
     if (lo < hi) {
       const int k = atomicAdd(&s_nseg, 1);
-      if (k < kMaxSegs) {
+      if (k < kRows) {
         s_seg_e[k] = e;
         s_seg_lo[k] = (int)(lo - r0);
         s_seg_hi[k] = (int)(hi - r0);
       }
     }
   }
-  // Token of each tile row, or -1 when the row folds nothing.
-  if (threadIdx.x < kTileRows) {
+  // Token of each sub-tile row, or -1 when the row folds nothing.
+  if (threadIdx.x < kRows) {
     const int64_t r = r0 + threadIdx.x;
     int tk = -1;
     if (r < r1) {
       const int id = p.sorted_ids[r];
       if (id >= 0) {
-        const int cand = id / p.top_k;
+        const int cand = (int)udiv((uint32_t)id, (uint32_t)p.top_k, p.top_k_magic);
         if (cand < p.n_tokens && p.row_adapter[cand] >= 0) tk = cand;
       }
     }
     s_tok[threadIdx.x] = tk;
   }
-  __syncthreads();
-  const int nseg = min(s_nseg, kMaxSegs);
+  lds_barrier();
+  const int nseg = min(__builtin_amdgcn_readfirstlane(s_nseg), kRows);
 
   const int n_lo = ns * p.ns_cols;
   const int n_hi = min(n_lo + p.ns_cols, p.N);
+  Bufs bf;
+  bf.x = make_buf(p.x, p.x_bytes);
+  bf.out = make_buf(p.out, p.out_bytes);
+  const int tile_row = (int)(r0 - p.row_offset);
   for (int sg = 0; sg < nseg; ++sg) {
-    const int e = s_seg_e[sg];
+    // LDS values are the same on every lane; say so, so that the expert's
+    // table cells and buffer descriptors live in scalar registers.
+    const int e = __builtin_amdgcn_readfirstlane(s_seg_e[sg]);
     if (e >= p.n_experts) continue;
-    const uint64_t a_addr = p.a_table[e], b_addr = p.b_table[e];
+    const uint64_t a_addr = uniform_u64(p.a_table[e]), b_addr = uniform_u64(p.b_table[e]);
     if (a_addr == 0 || b_addr == 0) continue;
-    const float scale = p.scale_table[e];
-    const int lo = s_seg_lo[sg], hi = s_seg_hi[sg];
+    const float scale = uniform_f32(p.scale_table[e]);
+    bf.a = make_buf(reinterpret_cast<const void*>(a_addr), (uint32_t)(p.R * p.K) * 2u);
+    bf.b = make_buf(reinterpret_cast<const void*>(b_addr), (uint32_t)(p.N * p.R) * 2u);
+    const int lo = __builtin_amdgcn_readfirstlane(s_seg_lo[sg]);
+    const int hi = __builtin_amdgcn_readfirstlane(s_seg_hi[sg]);
     for (int c = lo; c < hi; c += 16 * MB)
-      fold_rows<NB, MB, FULL_R>(p.x, p.out, p.K, p.N, p.R,
-                                reinterpret_cast<const uint16_t*>(a_addr),
-                                reinterpret_cast<const uint16_t*>(b_addr), scale, nullptr,
-                                r0 + c, s_tok + c, min(16 * MB, hi - c), n_lo, n_hi, s_part);
+      fold_rows<NB, MB, FULL_R>(bf, p.K, p.N, p.R, scale, nullptr, tile_row + c, s_tok + c,
+                                min(16 * MB, hi - c), n_lo, n_hi, s_part);
   }
 }
 
@@ -549,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void rowwise_f32_kernel(RowwiseArgs p) {
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (lane == 0) s_h[j] = acc;
   }
-  __syncthreads();
+  lds_barrier();
   float* orow = p.out + (size_t)row * p.N;
   for (int n = threadIdx.x; n < p.N; n += kThreads) {
     float acc = 0.f;
@@ -568,6 +793,8 @@ int env_int(const char* name, int dflt) {
   return std::atoi(v);
 }
 
+uint32_t magic_for(int32_t d) { return (uint32_t)(0xFFFFFFFFu / (uint32_t)d); }
+
 int32_t check_route(const mlora_expert_route* r, const char* who) {
   if (!r) return fail(MLORA_ERR_INVALID, "%s: NULL route", who);
   if (r->n_experts < 0) return fail(MLORA_ERR_INVALID, "%s: n_experts < 0", who);
@@ -580,6 +807,10 @@ int32_t check_route(const mlora_expert_route* r, const char* who) {
     return fail(MLORA_ERR_INVALID, "%s: max_rank=%d outside [1, 128]", who, r->max_rank);
   if (r->dtype != MLORA_BF16 && r->dtype != MLORA_F32)
     return fail(MLORA_ERR_INVALID, "%s: unknown dtype %d", who, r->dtype);
+  // one expert's matrices are addressed with 32-bit offsets
+  if ((int64_t)r->k_in * r->max_rank * 4 > (int64_t)kMaxBufBytes ||
+      (int64_t)r->n_out * r->max_rank * 4 > (int64_t)kMaxBufBytes)
+    return fail(MLORA_ERR_INVALID, "%s: an expert matrix exceeds 4 GiB", who);
   return MLORA_OK;
 }
 
@@ -599,34 +830,57 @@ int ns_cols_for(int N, int ns) {
   return (per + kColStep - 1) / kColStep * kColStep;
 }
 
-template <int NB, int MB, bool FULL_R>
+template <int NB, int MB>
 void launch_gather(const GatherArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gather_fold_kernel<NB, MB, FULL_R>), dim3(grid), dim3(kThreads), 0, s, a);
+  if (a.R == 16 * NB)
+    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, false>), dim3(grid), dim3(kThreads), 0, s, a);
 }
 
-template <int NB, int MB, bool FULL_R>
+// Rank blocks of 16 -> (NB, MB) instantiation. `small` picks one 16-row block
+// per chunk, for slices that hold few rows of their expert (decode).
+void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small) {
+  const int nb = (a.R + 15) / 16;
+  if (nb <= 1) {
+    if (small) launch_gather<1, 1>(a, grid, s); else launch_gather<1, 4>(a, grid, s);
+  } else if (nb <= 2) {
+    if (small) launch_gather<2, 1>(a, grid, s); else launch_gather<2, 4>(a, grid, s);
+  } else if (nb <= 4) {
+    if (small) launch_gather<4, 1>(a, grid, s); else launch_gather<4, 2>(a, grid, s);
+  } else {
+    launch_gather<8, 1>(a, grid, s);
+  }
+}
+
+template <int NB, int MB>
 void launch_grouped(const GroupedArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_fold_kernel<NB, MB, FULL_R>), dim3(grid), dim3(kThreads), 0, s, a);
+  if (a.R == 16 * NB)
+    hipLaunchKernelGGL((grouped_fold_kernel<NB, MB, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_fold_kernel<NB, MB, false>), dim3(grid), dim3(kThreads), 0, s, a);
 }
 
-// Rank blocks of 16 -> (NB, MB) instantiation.
-#define MLORA_DISPATCH(FN, ARGS, GRID, STREAM, R)                        \
-  do {                                                                   \
-    const int nb_ = ((R) + 15) / 16;                                     \
-    if (nb_ <= 1) {                                                      \
-      if ((R) == 16) FN<1, 4, true>(ARGS, GRID, STREAM);                 \
-      else FN<1, 4, false>(ARGS, GRID, STREAM);                          \
-    } else if (nb_ <= 2) {                                               \
-      if ((R) == 32) FN<2, 4, true>(ARGS, GRID, STREAM);                 \
-      else FN<2, 4, false>(ARGS, GRID, STREAM);                          \
-    } else if (nb_ <= 4) {                                               \
-      if ((R) == 64) FN<4, 2, true>(ARGS, GRID, STREAM);                 \
-      else FN<4, 2, false>(ARGS, GRID, STREAM);                          \
-    } else {                                                             \
-      if ((R) == 128) FN<8, 1, true>(ARGS, GRID, STREAM);                \
-      else FN<8, 1, false>(ARGS, GRID, STREAM);                          \
-    }                                                                    \
-  } while (0)
+// Largest rows-per-workgroup (16 * MB) that each rank width supports.
+int grouped_mb_max(int R) {
+  const int nb = (R + 15) / 16;
+  return nb <= 2 ? 4 : (nb <= 4 ? 2 : 1);
+}
+
+template <int NB>
+void dispatch_grouped_mb(const GroupedArgs& a, int grid, hipStream_t s, int mb) {
+  if (mb >= 4) launch_grouped<NB, 4>(a, grid, s);
+  else if (mb == 2) launch_grouped<NB, 2>(a, grid, s);
+  else launch_grouped<NB, 1>(a, grid, s);
+}
+
+void dispatch_grouped(const GroupedArgs& a, int grid, hipStream_t s, int mb) {
+  const int nb = (a.R + 15) / 16;
+  if (nb <= 1) dispatch_grouped_mb<1>(a, grid, s, mb);
+  else if (nb <= 2) dispatch_grouped_mb<2>(a, grid, s, mb);
+  else if (nb <= 4) { if (mb >= 2) launch_grouped<4, 2>(a, grid, s); else launch_grouped<4, 1>(a, grid, s); }
+  else launch_grouped<8, 1>(a, grid, s);
+}
 
 }  // namespace
 }  // namespace mlora
@@ -643,8 +897,8 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   if (n_slots < 0 || n_slots > (int64_t)0x7fffffff - kScanMax)
     return fail(MLORA_ERR_INVALID, "%s: n_slots=%lld out of range", who, (long long)n_slots);
   const int64_t need_tok = (n_slots + top_k - 1) / top_k;
-  if (n_tokens < need_tok)
-    return fail(MLORA_ERR_INVALID, "%s: n_tokens=%lld < ceil(n_slots/top_k)=%lld", who,
+  if (n_tokens < need_tok || n_tokens > 0x3fffffffll)
+    return fail(MLORA_ERR_INVALID, "%s: n_tokens=%lld (need >= ceil(n_slots/top_k)=%lld)", who,
                 (long long)n_tokens, (long long)need_tok);
   if (n_slots == 0 || route->n_experts == 0) {
     clear_error();
@@ -679,6 +933,9 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   if (!aligned16(x) || !aligned16(base_out))
     return fail(MLORA_ERR_INVALID, "%s: x and base_out must be 16-byte aligned", who);
   const int E = route->n_experts, K = route->k_in, N = route->n_out, R = route->max_rank;
+  const int64_t x_bytes = n_tokens * K * 2, out_bytes = n_slots * N * 2;
+  if (x_bytes > (int64_t)kMaxBufBytes || out_bytes > (int64_t)kMaxBufBytes)
+    return fail(MLORA_ERR_INVALID, "%s: x or base_out exceeds 4 GiB; split the call", who);
   const int ns_max = (N + kColStep - 1) / kColStep;
 
   // Launch shape. Row slices first (each slice scans at most kScanMax rows),
@@ -688,8 +945,7 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   int rs = (int)((n_slots + kScanMax - 1) / kScanMax);
   int ns = 1;
   const int64_t target = 512;
-  while ((int64_t)E * rs * ns < target && rows_per_e / (rs * 2) >= 32)
-    rs *= 2;
+  while ((int64_t)E * rs * ns < target && rows_per_e / (rs * 2) >= 32) rs *= 2;
   const double shrink_b = 2.0 * R * K + 2.0 * (double)rows_per_e / rs * K;
   const double expand_b = 2.0 * N * R + 4.0 * (double)rows_per_e / rs * N;
   while ((int64_t)E * rs * ns < target && ns * 2 <= ns_max &&
@@ -714,12 +970,16 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   a.a_table = route->a_table;
   a.b_table = route->b_table;
   a.scale_table = route->scale_table;
+  a.x_bytes = (uint32_t)x_bytes;
+  a.out_bytes = (uint32_t)out_bytes;
   a.n_experts = E;
   a.K = K;
   a.N = N;
   a.R = R;
   a.n_slots = (int32_t)n_slots;
   a.top_k = top_k;
+  a.n_tokens = (int32_t)n_tokens;
+  a.top_k_magic = magic_for(top_k);
   a.rs_count = rs;
   a.ns_count = ns;
   a.scan_len = scan;
@@ -730,7 +990,10 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   a.units = (int32_t)units;
   a.per_xcd = (int32_t)((units + kXcds - 1) / kXcds);
   const int grid = a.per_xcd * kXcds;
-  MLORA_DISPATCH(launch_gather, a, grid, s, R);
+  // one 16-row block per chunk when a slice is expected to hold few rows
+  const int64_t rows_per_slice = (n_slots + (int64_t)E * rs - 1) / ((int64_t)E * rs);
+  const int small = env_int("MLORA_GATHER_SMALL", rows_per_slice <= 16 ? 1 : 0);
+  dispatch_gather(a, grid, s, small != 0);
   return launched(who);
 }
 
@@ -744,7 +1007,7 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
   if (int32_t rc = check_route(route, who)) return rc;
   if (top_k <= 0) return fail(MLORA_ERR_INVALID, "%s: top_k=%d must be positive", who, top_k);
   if (n_route < 0) return fail(MLORA_ERR_INVALID, "%s: n_route < 0", who);
-  if (n_tokens < 0 || n_tokens > 0x7fffffffll)
+  if (n_tokens < 0 || n_tokens > 0x3fffffffll)
     return fail(MLORA_ERR_INVALID, "%s: n_tokens out of range", who);
   if (n_rows < 0 || row_offset < 0 || row_end < row_offset || row_end > n_rows)
     return fail(MLORA_ERR_INVALID, "%s: window [%lld, %lld) outside [0, %lld]", who,
@@ -786,30 +1049,43 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
   if (!aligned16(x) || !aligned16(base_out))
     return fail(MLORA_ERR_INVALID, "%s: x and base_out must be 16-byte aligned", who);
   const int N = route->n_out, K = route->k_in, R = route->max_rank;
+  const int64_t x_bytes = n_tokens * K * 2, out_bytes = (row_end - row_offset) * N * 2;
+  if (x_bytes > (int64_t)kMaxBufBytes || out_bytes > (int64_t)kMaxBufBytes)
+    return fail(MLORA_ERR_INVALID, "%s: x or the window of base_out exceeds 4 GiB", who);
   const int64_t tiles = mlora_grouped_down_wc(row_offset, row_end);
   const int ns_max = (N + kColStep - 1) / kColStep;
-  // Column slices while the grid is short of two workgroups per CU and the
-  // repeated shrink (x rows + A_e) stays below the expand bytes it splits.
+  // Split a tile's rows over workgroups first (no operand is read twice but
+  // A_e / B_e, which L2 serves), then columns while the grid is short of two
+  // workgroups per CU and the repeated shrink (x rows + A_e) stays below the
+  // expand bytes it splits.
+  int mb = grouped_mb_max(R);
+  while (mb > 1 && tiles * (4 / mb) < 512) mb /= 2;
   int ns = 1;
-  const double shrink_b = 2.0 * kTileRows * K + 2.0 * R * K;
-  const double expand_b = 4.0 * kTileRows * N + 2.0 * N * R;
-  while (tiles * ns < 512 && ns * 2 <= ns_max && (ns * 2) * shrink_b <= shrink_b + expand_b)
+  const double shrink_b = 2.0 * 16 * mb * K + 2.0 * R * K;
+  const double expand_b = 4.0 * 16 * mb * N + 2.0 * N * R;
+  while (tiles * (4 / mb) * ns < 512 && ns * 2 <= ns_max &&
+         (ns * 2) * shrink_b <= shrink_b + expand_b)
     ns *= 2;
+  mb = env_int("MLORA_GROUPED_MB", mb);
   ns = env_int("MLORA_GROUPED_NS", ns);
+  if (mb != 1 && mb != 2 && mb != 4) mb = 2;
+  if (mb > grouped_mb_max(R)) mb = grouped_mb_max(R);
   if (ns < 1) ns = 1;
   if (ns > ns_max) ns = ns_max;
-  const int64_t units = tiles * ns;
+  const int64_t units = tiles * (4 / mb) * ns;
   if (units > 0x7fffffffll / 2) return fail(MLORA_ERR_INVALID, "%s: window too large", who);
 
   GroupedArgs a{};
   a.x = static_cast<const uint16_t*>(x);
-  a.out = static_cast<uint16_t*>(base_out);
+  a.out = static_cast<uint16_t*>(base_out) + row_offset * N;
   a.offsets = expert_offsets;
   a.sorted_ids = sorted_ids;
   a.row_adapter = row_adapter;
   a.a_table = route->a_table;
   a.b_table = route->b_table;
   a.scale_table = route->scale_table;
+  a.x_bytes = (uint32_t)x_bytes;
+  a.out_bytes = (uint32_t)out_bytes;
   a.row_offset = row_offset;
   a.row_end = row_end;
   a.n_experts = route->n_experts;
@@ -819,12 +1095,13 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
   a.n_route = n_route;
   a.top_k = top_k;
   a.n_tokens = (int32_t)n_tokens;
+  a.top_k_magic = magic_for(top_k);
   a.n_tiles = (int32_t)tiles;
   a.ns_count = ns;
   a.ns_cols = ns_cols_for(N, ns);
   a.units = (int32_t)units;
   a.per_xcd = (int32_t)((units + kXcds - 1) / kXcds);
   const int grid = a.per_xcd * kXcds;
-  MLORA_DISPATCH(launch_grouped, a, grid, s, R);
+  dispatch_grouped(a, grid, s, mb);
   return launched(who);
 }

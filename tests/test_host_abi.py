@@ -287,3 +287,16 @@ def test_grouped_rejects_bad_args(lib):
     assert call(route=_route(max_rank=200)) == -1
     assert call(off=3, end=3) == 0          # empty window
     assert call(n_route=0) == 0             # no spans
+
+
+def test_single_hip_runtime_in_process():
+    """The library binds to the HIP runtime PyTorch loaded, not a second copy."""
+    import subprocess
+    import sys
+    code = ("import moe_expert_lora_amd as ml; ml.load(); "
+            "maps = open('/proc/self/maps').read(); "
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'amdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1"

@@ -540,3 +540,29 @@ def test_pack_mutants_are_caught():
                 c["expect"]["a"], c["expect"]["b"], c["expect"]["s"], c["expect"]["n"])
             ok &= got == want
         assert not ok
+
+
+# ---------------------------------------------------------------------------
+# the tolerance reading
+# ---------------------------------------------------------------------------
+
+
+def test_bf16_store_alone_breaks_literal_max_abs():
+    """The exact gate-up gather result, correctly rounded to bf16 (the best any
+    bf16 output can do), already misses a literal 3e-2 max-abs bound because
+    its outputs reach |v| >= 8 where half a bf16 ulp is 2**-5. It passes the
+    bound read as max(3e-2, one output ulp), and relative L2 <= 2e-3."""
+    import workloads
+    from tests.common import (MAX_ABS_TOL, REL_L2_TOL, max_abs, max_abs_excess, rel_l2,
+                              to_f64)
+    c = workloads.cfg4()
+    ref = OracleView(c).fold()
+    best = to_f64(workloads.bf16_from_f32(ref.astype(np.float32)), "bf16")
+    assert np.abs(ref).max() >= 8.0
+    assert max_abs(best, ref) > MAX_ABS_TOL
+    assert max_abs_excess(best, ref, "bf16") <= 0.5 + 1e-9
+    assert rel_l2(best, ref) <= REL_L2_TOL
+    # one more ulp of slack than the correctly rounded answer needs: a device
+    # result may round the other way when its fp32 sum sits near a midpoint
+    near = best + 0.9 * np.sign(ref - best) * np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+    assert max_abs_excess(near, ref, "bf16") <= 1.0
