@@ -5,6 +5,9 @@ workloads one mlora_gather_bgmv call, for the prefill workloads one
 mlora_grouped_down call per window of grouped_down_windows. The host-side
 integer work (tables, maps, windows) is done once before timing, as an engine
 does at adapter install / batch setup; its cost is reported separately.
+Steps are captured in a HIP graph and replayed (the fold reads its routing on
+the device precisely so that it can be captured); eager launch cost, which
+the host launch path dominates for the small decode calls, is reported too.
 
 Inputs are resident in HBM before timing starts. The step cycles through
 `copies` independent copies of x, A, B, base_out and the tables, so each step
@@ -217,6 +220,75 @@ def cpu_baseline(case, budget_s=10.0):
 # ---------------------------------------------------------------------------
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counter runs
+# ---------------------------------------------------------------------------
+
+CALIB_BYTES = 1 << 29  # 512 MiB copied by --calibrate-copy
+
+
+def calibrate_copy():
+    """A plain device copy of CALIB_BYTES (read CALIB_BYTES, write CALIB_BYTES);
+    run under `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` to scale the
+    counters of the fold runs."""
+    import torch
+    src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": CALIB_BYTES}), flush=True)
+
+
+def _pmc_rows(path):
+    import csv
+    rows = []
+    for root, _, files in os.walk(path):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                rows.extend(csv.DictReader(open(os.path.join(root, f))))
+    return rows
+
+
+def _mean_counter(rows, counter, match):
+    vals = [float(r["Counter_Value"]) for r in rows
+            if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """Per-launch HBM bytes of the fold kernel from FETCH_SIZE / WRITE_SIZE runs
+    (KiB per dispatch), each scaled by what the counter reads for the plain copy
+    of CALIB_BYTES; recorded in profiles/traffic.json with the kernel hash."""
+    is_fold = lambda n: "fold_kernel" in n  # noqa: E731
+    is_copy = lambda n: "fold" not in n  # noqa: E731
+    f_kib, nf = _mean_counter(_pmc_rows(fetch_dir), "FETCH_SIZE", is_fold)
+    w_kib, nw = _mean_counter(_pmc_rows(write_dir), "WRITE_SIZE", is_fold)
+    cal_rows_f = _pmc_rows(cal_fetch_dir)
+    cal_rows_w = _pmc_rows(cal_write_dir)
+    # the copy dispatch is the largest FETCH_SIZE / WRITE_SIZE in the calibration runs
+    cf = max(float(r["Counter_Value"]) for r in cal_rows_f
+             if r["Counter_Name"] == "FETCH_SIZE" and is_copy(r["Kernel_Name"]))
+    cw = max(float(r["Counter_Value"]) for r in cal_rows_w
+             if r["Counter_Name"] == "WRITE_SIZE" and is_copy(r["Kernel_Name"]))
+    kf = CALIB_BYTES / (cf * 1024.0)
+    kw = CALIB_BYTES / (cw * 1024.0)
+    rec = {
+        "kernel_sha256_16": kernel_hash(),
+        "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+        "dispatches": [nf, nw],
+        "copy_scale_fetch": kf, "copy_scale_write": kw,
+        "hbm_bytes_per_launch": f_kib * 1024.0 * kf + w_kib * 1024.0 * kw,
+    }
+    data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    data[workload] = rec
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps({workload: rec}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,7 +298,17 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of graph replays")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the plain copy used to scale HBM counters")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="rocprofv3 --pmc output dirs -> profiles/traffic.json (no GPU)")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        traffic_from(args.workload, *args.traffic_from)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the fold needs no collective and this "
@@ -241,6 +323,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     t_gen = time.perf_counter()
     case = workloads.CONFIGS[args.workload]()
@@ -264,30 +349,65 @@ def main():
             ml.mlora_grouped_down_windows(case.n_rows, case.cap)
     host_us = (time.perf_counter() - t0) / 50 * 1e6
 
-    stream = torch.cuda.current_stream()
+    # The fold reads its routing on the device, so a step is captured once in a
+    # HIP graph and replayed, as a decode loop runs it. One graph holds one step
+    # per rotating copy; K steps are K / copies replays (K rounded up).
     for i in range(args.warmup):
         st.step(i)
     torch.cuda.synchronize()
+    if args.eager:
+        class _Eager:
+            def replay(self):
+                for i in range(copies):
+                    st.step(i)
+        graph = _Eager()
+    else:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for i in range(copies):
+                    st.step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+    replays = max(1, math.ceil(args.steps / copies))
+    steps = replays * copies
+    for _ in range(max(1, math.ceil(args.warmup / copies))):
+        graph.replay()
+    torch.cuda.synchronize()
 
-    # timed region: K steps, wall clock
+    # timed region: `steps` steps, wall clock and HIP events on the replay stream
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per_replay = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        st.step(i)
+    e0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    # per-step device duration with HIP events on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        st.step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dur_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    step_ms = float(np.mean(dur_ms))
+    step_ms = e0.elapsed_time(e1) / steps
     per_launch_s = step_ms / 1e3 / launches
+
+    # spread of the per-replay duration (a second, separately timed pass)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(replays)]
+    for r in range(replays):
+        ev[r][0].record(stream)
+        graph.replay()
+        ev[r][1].record(stream)
+    torch.cuda.synchronize()
+    dur_ms = np.array([a.elapsed_time(b) for a, b in ev]) / copies
+
+    # eager launches (host launch path included), for the record
+    t0 = time.perf_counter()
+    for i in range(copies):
+        st.step(i)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) / copies * 1e6
 
     achieved = alg_bytes / launches / per_launch_s / 1e9
     traffic = None
@@ -303,13 +423,13 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(case, args.cpu_seconds)
 
-    ms_per_step = wall / args.steps * 1e3
+    ms_per_step = wall / steps * 1e3
     out = {
         "metric": METRIC,
-        "value": rows * args.steps / wall,
+        "value": rows * steps / wall,
         "unit": "rows/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
@@ -324,6 +444,8 @@ def main():
             "folded_rows_per_step": folded,
             "launches_per_step": launches,
             "rotating_copies": copies,
+            "timing": ("eager launches" if args.eager else
+                       "HIP graph of one step per copy, replayed"),
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -340,6 +462,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "host_setup_us": host_us,
+        "eager_step_us": eager_us,
         "notes": "the pages quote no performance numbers; vs_baseline is null",
     }
     print(json.dumps(out), flush=True)

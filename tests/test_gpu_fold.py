@@ -341,3 +341,50 @@ def test_empty_calls_enqueue_nothing():
     dev = DeviceCase(c, DEV)
     got = dev.run(windows=[(10, 10), (80, 80)])
     assert np.array_equal(got, c.base)
+
+
+def test_graph_replay_reads_routing_on_device():
+    """A fold captured in a HIP graph and replayed matches the eager fold, and a
+    replay after the routing (indices, map) and table cells are rewritten in
+    place uses the new contents: the host never reads routing data."""
+    _need_gpu()
+    from tests.device import DeviceCase, from_torch, to_torch
+    c = workloads.make_gather_case(82, n_seq=48, padded_n=56, top_k=4, n_route=16, k_in=256,
+                                   n_out=320, max_rank=16, n_adapted=12, skip_seqs=4)
+    dev = DeviceCase(c, DEV)
+    pristine = to_torch(c.base, "bf16", DEV)
+    base = pristine.clone()
+    eager1 = dev.run()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            dev.fold(base)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        base.copy_(pristine)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_torch(base), eager1)
+    # new routing, new map and one table cell cleared, written in place
+    rng = np.random.default_rng(83)
+    new_idx = rng.integers(0, 16, size=c.indices.shape, dtype=np.int64).astype(np.int32)
+    new_map = np.where(rng.random(dev.row_adapter.numel()) < 0.3, -1, 1).astype(np.int32)
+    dev.indices.copy_(torch.from_numpy(new_idx))
+    dev.row_adapter.copy_(torch.from_numpy(new_map))
+    live_e = int(np.flatnonzero(dev.tables_host[0])[0])
+    dev.a_table[live_e] = 0
+    base.copy_(pristine)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    c2 = workloads.FoldCase(**{k: getattr(c, k) for k in c.__dataclass_fields__})
+    c2.indices = new_idx
+    view = OracleView(c2)
+    view.row_adapter = new_map
+    view.a_table = list(view.a_table)
+    view.a_table[live_e] = 0
+    check(view, from_torch(base), c.base, "graph replay, new routing")
