@@ -623,6 +623,186 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
   consume(keep_b);
 }
 
+
+// ---------------------------------------------------------------------------
+// gather, decode fast path: resident weights
+// ---------------------------------------------------------------------------
+
+// When a wave's whole share of A_e (its k steps) and of B_e (its column steps)
+// fits in registers, both are requested together with the routing scan,
+// before any row is known; after the scan only x and base_out are loaded.
+// One 16-row block per chunk; the weights serve every chunk of the slice.
+constexpr int kResSteps = 8;  // k steps, and column steps, per wave
+
+template <int NB, bool FULL_R>
+__global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p) {
+  constexpr int HW = 4 * NB;
+  __shared__ float s_part[kWaves * 64 * HW];
+  __shared__ int s_rows[kScanMax];
+  __shared__ int s_toks[kScanMax];
+  __shared__ int s_cnt;
+
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u0 = xcd * p.per_xcd + slot;
+  if (u0 >= p.units) return;
+  const int per_e = p.rs_count * p.ns_count;
+  const int e = u0 / per_e;
+  const int within = u0 - e * per_e;
+  const int rs = within / p.ns_count, ns = within - rs * p.ns_count;
+
+  const uint64_t a_addr = uniform_u64(p.a_table[e]), b_addr = uniform_u64(p.b_table[e]);
+  const float scale = uniform_f32(p.scale_table[e]);
+
+  const rsrc_t r_idx = make_buf(p.indices, (uint32_t)p.n_slots * 4u);
+  const rsrc_t r_map = make_buf(p.row_adapter, (uint32_t)p.n_tokens * 4u);
+  const int start = rs * p.scan_len;
+  const int end = min(start + p.scan_len, p.n_slots);
+  constexpr int kPer = kScanMax / kThreads;
+  const int rounds = (end - start + kThreads - 1) / kThreads;
+  int iv[kPer], mv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    iv[i] = -1;
+    mv[i] = -1;
+    if (i < rounds) {
+      const int row = start + i * kThreads + (int)threadIdx.x;
+      const bool in = row < end;
+      const uint32_t tok = udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
+      iv[i] = (int)bld4(r_idx, in ? (uint32_t)row * 4u : kOOB);
+      mv[i] = (int)bld4(r_map, in ? tok * 4u : kOOB);
+    }
+  }
+  if (a_addr == 0 || b_addr == 0) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N, R = p.R;
+  const int n_lo = ns * p.ns_cols;
+  const int n_hi = min(n_lo + p.ns_cols, N);
+  const int nks = (K + 31) >> 5;
+  const int ncs = (n_hi - n_lo + kColStep - 1) / kColStep;
+  Bufs bf;
+  bf.x = make_buf(p.x, p.x_bytes);
+  bf.a = make_buf(reinterpret_cast<const void*>(a_addr), (uint32_t)(R * K) * 2u);
+  bf.b = make_buf(reinterpret_cast<const void*>(b_addr), (uint32_t)(N * R) * 2u);
+  bf.out = make_buf(p.out, p.out_bytes);
+
+  // the wave's weights
+  u32x4 av[kResSteps][NB];
+#pragma unroll
+  for (int u = 0; u < kResSteps; ++u) {
+    const int s = wave + u * kWaves;
+    const int k0 = s * 32 + g * 8;
+    const bool kin = s < nks && k0 < K;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
+      av[u][b] = bld16(bf.a, (kin && rank < R) ? (uint32_t)(rank * K + k0) * 2u : kOOB);
+    }
+  }
+  BFrag<NB> bw[kResSteps];
+#pragma unroll
+  for (int u = 0; u < kResSteps; ++u) {
+    const int cs = wave + u * kWaves;
+    load_bfrag<NB, FULL_R>(bw[u], bf.b, R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li, g);
+  }
+
+  if (threadIdx.x == 0) s_cnt = 0;
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (i >= rounds) break;
+    const int row = start + i * kThreads + (int)threadIdx.x;
+    const bool hit = row < end && iv[i] == e && mv[i] >= 0;
+    const int tok = (int)udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
+    wave_append(hit, row, tok, &s_cnt, s_rows, s_toks, kScanMax);
+  }
+  lds_barrier();
+  const int n = __builtin_amdgcn_readfirstlane(s_cnt);
+
+  for (int c = 0; c < n; c += 16) {
+    const int m = c + li;
+    int t = -1, r = 0;
+    if (m < n) {
+      t = s_toks[m];
+      r = s_rows[m];
+    }
+    const bool valid = t >= 0;
+    const uint32_t xoff = (uint32_t)(valid ? t : 0) * (uint32_t)K * 2u;
+    const uint32_t ooff = (uint32_t)r * (uint32_t)N * 2u;
+    u32x4 xv[kResSteps], ov[kResSteps];
+#pragma unroll
+    for (int u = 0; u < kResSteps; ++u) {
+      const int s = wave + u * kWaves;
+      const int k0 = s * 32 + g * 8;
+      xv[u] = bld16(bf.x, (valid && s < nks && k0 < K) ? xoff + 2u * k0 : kOOB);
+    }
+#pragma unroll
+    for (int u = 0; u < kResSteps; ++u) {
+      const int cs = wave + u * kWaves;
+      const int col = n_lo + cs * kColStep + 8 * g;
+      ov[u] = bld16(bf.out, (valid && cs < ncs && col < n_hi) ? ooff + 2u * col : kOOB);
+    }
+    // shrink
+    f32x4 hacc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) hacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kResSteps; ++u) {
+      if (wave + u * kWaves < nks) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) hacc[b] = mfma16x16x32(as_bf(av[u][b]), as_bf(xv[u]), hacc[b]);
+      }
+    }
+    float* dst = s_part + ((size_t)wave * 64 + lane) * HW;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(dst + 4 * b) = hacc[b];
+    lds_barrier();
+    HOp<NB> hop;
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      f32x4 h = *reinterpret_cast<const f32x4*>(s_part + (size_t)lane * HW + 4 * s);
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w)
+        h += *reinterpret_cast<const f32x4*>(s_part + ((size_t)w * 64 + lane) * HW + 4 * s);
+      const f32x4 v = scale * h;
+      const uint32_t hi01 = pack_bf16(v.x, v.y), hi23 = pack_bf16(v.z, v.w);
+      const uint32_t lo01 = pack_bf16(v.x - lo_f(hi01), v.y - hi_f(hi01));
+      const uint32_t lo23 = pack_bf16(v.z - lo_f(hi23), v.w - hi_f(hi23));
+      constexpr int CR = Chunk<NB>::kRanks;
+      const int q = (4 * s) / CR, w0 = ((4 * s) % CR) / 2;
+      hop.hi[q][w0] = hi01;
+      hop.hi[q][w0 + 1] = hi23;
+      hop.lo[q][w0] = lo01;
+      hop.lo[q][w0 + 1] = lo23;
+    }
+    // expand
+#pragma unroll
+    for (int u = 0; u < kResSteps; ++u) {
+      const int cs = wave + u * kWaves;
+      if (cs < ncs) {
+        f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < Chunk<NB>::kCount; ++q) {
+          d0 = mfma_chunk(bw[u].w[0][q], hop.hi[q], d0);
+          d1 = mfma_chunk(bw[u].w[1][q], hop.hi[q], d1);
+          d0 = mfma_chunk(bw[u].w[0][q], hop.lo[q], d0);
+          d1 = mfma_chunk(bw[u].w[1][q], hop.lo[q], d1);
+        }
+        const int col = n_lo + cs * kColStep + 8 * g;
+        const u32x4 bq = ov[u];
+        const uint32_t o0 = pack_bf16(lo_f(bq.x) + d0.x, hi_f(bq.x) + d0.y);
+        const uint32_t o1 = pack_bf16(lo_f(bq.y) + d0.z, hi_f(bq.y) + d0.w);
+        const uint32_t o2 = pack_bf16(lo_f(bq.z) + d1.x, hi_f(bq.z) + d1.y);
+        const uint32_t o3 = pack_bf16(lo_f(bq.w) + d1.z, hi_f(bq.w) + d1.w);
+        bst16(bf.out, (valid && col < n_hi) ? ooff + 2u * col : kOOB, u32x4{o0, o1, o2, o3});
+      }
+    }
+    lds_barrier();  // s_part is rewritten by the next chunk
+  }
+}
+
 // ---------------------------------------------------------------------------
 // grouped (prefill) kernel
 // ---------------------------------------------------------------------------
@@ -840,8 +1020,31 @@ void launch_gather(const GatherArgs& a, int grid, hipStream_t s) {
 
 // Rank blocks of 16 -> (NB, MB) instantiation. `small` picks one 16-row block
 // per chunk, for slices that hold few rows of their expert (decode).
-void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small) {
+// The decode fast path applies when every wave's k steps and column steps fit
+// the resident register arrays.
+bool gather_resident_fits(const GatherArgs& a) {
   const int nb = (a.R + 15) / 16;
+  const int nks = (a.K + 31) / 32;
+  const int ncs = (a.ns_cols + kColStep - 1) / kColStep;
+  return nb <= 2 && nks <= kWaves * kResSteps && ncs <= kWaves * kResSteps;
+}
+
+void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small, bool resident) {
+  const int nb = (a.R + 15) / 16;
+  if (resident && gather_resident_fits(a)) {
+    if (nb <= 1) {
+      if (a.R == 16)
+        hipLaunchKernelGGL((gather_resident_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((gather_resident_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    } else {
+      if (a.R == 32)
+        hipLaunchKernelGGL((gather_resident_kernel<2, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((gather_resident_kernel<2, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    }
+    return;
+  }
   if (nb <= 1) {
     if (small) launch_gather<1, 1>(a, grid, s); else launch_gather<1, 4>(a, grid, s);
   } else if (nb <= 2) {
@@ -944,12 +1147,12 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   const int64_t rows_per_e = (n_slots + E - 1) / E;
   int rs = (int)((n_slots + kScanMax - 1) / kScanMax);
   int ns = 1;
-  const int64_t target = 512;
+  const int64_t target = 256;  // one workgroup per CU; measured better than two
   while ((int64_t)E * rs * ns < target && rows_per_e / (rs * 2) >= 32) rs *= 2;
   const double shrink_b = 2.0 * R * K + 2.0 * (double)rows_per_e / rs * K;
   const double expand_b = 2.0 * N * R + 4.0 * (double)rows_per_e / rs * N;
   while ((int64_t)E * rs * ns < target && ns * 2 <= ns_max &&
-         (ns * 2) * shrink_b <= shrink_b + expand_b)
+         (ns * 2) * shrink_b <= 2.0 * (shrink_b + expand_b))
     ns *= 2;
   rs = env_int("MLORA_GATHER_RS", rs);
   ns = env_int("MLORA_GATHER_NS", ns);
@@ -993,7 +1196,10 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   // one 16-row block per chunk when a slice is expected to hold few rows
   const int64_t rows_per_slice = (n_slots + (int64_t)E * rs - 1) / ((int64_t)E * rs);
   const int small = env_int("MLORA_GATHER_SMALL", rows_per_slice <= 16 ? 1 : 0);
-  dispatch_gather(a, grid, s, small != 0);
+  // weights held in registers when a slice is expected to hold at most two
+  // 16-row blocks (and the wave's share fits)
+  const int resident = env_int("MLORA_GATHER_RESIDENT", rows_per_slice <= 32 ? 1 : 0);
+  dispatch_gather(a, grid, s, small != 0, resident != 0);
   return launched(who);
 }
 

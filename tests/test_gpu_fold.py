@@ -312,6 +312,35 @@ def test_small_cases(label, kw):
     assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
 
 
+@pytest.mark.parametrize("label", ["cfg2", "gather_r24_k72", "gather_slots_not_multiple",
+                                   "gather_r16_ns4"])
+def test_resident_weights_path_equals_streaming_path(label, monkeypatch):
+    """The decode path that holds a wave's weights in registers and the
+    streaming path fold in the same order: outputs equal bit for bit, and the
+    resident one passes the oracle bar on its own."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    if label == "cfg2":
+        case, view, dev = staged(label)
+    elif label == "gather_r16_ns4":
+        case = workloads.make_gather_case(77, n_seq=40, padded_n=48, top_k=6, n_route=30,
+                                          k_in=1000, n_out=1000, max_rank=16, n_adapted=25,
+                                          skip_seqs=3, name=label)
+        view, dev = OracleView(case), None
+    else:
+        case = build_small(label, dict(SMALL)[label])
+        view, dev = OracleView(case), None
+    dev = dev or DeviceCase(case, DEV)
+    if label == "gather_r16_ns4":
+        monkeypatch.setenv("MLORA_GATHER_NS", "4")
+    monkeypatch.setenv("MLORA_GATHER_RESIDENT", "1")
+    res = dev.run()
+    check(view, res, case.base, f"{label} resident")
+    monkeypatch.setenv("MLORA_GATHER_RESIDENT", "0")
+    stream = dev.run()
+    assert np.array_equal(res.view(np.uint8), stream.view(np.uint8))
+
+
 def test_guard_bands_untouched():
     """Fold into a slice of a larger buffer: the bytes around it stay as they were."""
     _need_gpu()
