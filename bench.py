@@ -124,11 +124,14 @@ def algorithmic_traffic(case, tables, row_adapter):
 # ---------------------------------------------------------------------------
 
 class Staged:
-    def __init__(self, case, copies, device="cuda"):
+    def __init__(self, case, copies, device="cuda", two_kernel=True):
         import torch
         from tests.device import DeviceCase
         self.case = case
-        self.primary = DeviceCase(case, device)
+        self.primary = DeviceCase(case, device, two_kernel=two_kernel)
+        if case.path == "grouped" and two_kernel:
+            # one workspace, allocated before any capture, shared by every copy
+            self.primary.workspace_for(self.primary.windows)
         self.copies = [self.primary]
         for _ in range(copies - 1):
             self.copies.append(self.primary_clone(device))
@@ -298,6 +301,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--one-kernel", action="store_true",
+                    help="grouped: run the one-kernel form (no workspace)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of graph replays")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -332,7 +337,7 @@ def main():
     t_gen = time.perf_counter() - t_gen
     cb = copy_bytes(case)
     copies = args.copies or max(2, min(64, math.ceil(640e6 / cb)))
-    st = Staged(case, copies)
+    st = Staged(case, copies, two_kernel=not args.one_kernel)
     tables = st.primary.tables_host
     ra = st.primary.row_adapter_host
     alg_bytes, flops, rows, folded, launches = algorithmic_traffic(case, tables, ra)
@@ -443,6 +448,7 @@ def main():
             "rows_per_step": rows,
             "folded_rows_per_step": folded,
             "launches_per_step": launches,
+            "kernels_per_launch": (1 if case.path == "gather" or args.one_kernel else 2),
             "rotating_copies": copies,
             "timing": ("eager launches" if args.eager else
                        "HIP graph of one step per copy, replayed"),

@@ -194,13 +194,34 @@ int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void* x, int64_
  *   sorted_ids     [n_rows]          int32
  *   row_adapter    [n_tokens]        int32
  * 0 <= row_offset <= row_end <= n_rows. An empty window enqueues nothing.
- * Returns MLORA_OK, MLORA_ERR_INVALID or MLORA_ERR_HIP.
+ *
+ * Workspace (device, caller-owned, optional): with workspace == NULL and
+ * workspace_bytes == 0 the fold runs as one kernel. With a workspace of at
+ * least mlora_grouped_down_workspace_bytes(row_offset, row_end, max_rank)
+ * bytes, 256-byte aligned, it runs as two kernels (shrink into the workspace,
+ * then expand), which streams base_out faster on large windows; both forms
+ * give the same bits. The contents need no initialisation and are dead once
+ * the call's kernels finish; calls that share one workspace must be ordered
+ * (one stream). bf16 only uses it; an f32 route ignores it.
+ * Returns MLORA_OK, MLORA_ERR_INVALID (arguments, including a misaligned or
+ * NULL-with-size workspace), MLORA_ERR_CAPACITY (workspace too small;
+ * nothing enqueued) or MLORA_ERR_HIP.
  */
 int32_t mlora_grouped_down(const mlora_expert_route* route, const void* x, int64_t n_tokens,
                            void* base_out, int64_t n_rows, const int32_t* expert_offsets,
                            int32_t n_route, const int32_t* sorted_ids,
                            const int32_t* row_adapter, int32_t top_k, int64_t row_offset,
-                           int64_t row_end, void* stream);
+                           int64_t row_end, void* workspace, uint64_t workspace_bytes,
+                           void* stream);
+
+/* Bytes of workspace mlora_grouped_down needs for its two-kernel form on the
+ * window [row_offset, row_end) at this max_rank: (row_end - row_offset) rows
+ * of 64 * NB bytes, NB = ceil(max_rank / 16) rounded up to 1, 2, 4 or 8,
+ * rounded up to 256, plus 8 bytes per row, rounded up to 256. 0 for an empty
+ * window or invalid arguments (negative offsets, row_end < row_offset,
+ * max_rank outside [1, 128]). */
+uint64_t mlora_grouped_down_workspace_bytes(int64_t row_offset, int64_t row_end,
+                                            int32_t max_rank);
 
 #ifdef __cplusplus
 }  /* extern "C" */

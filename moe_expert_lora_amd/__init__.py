@@ -45,6 +45,7 @@ EXPORTS = (
     "mlora_last_error",
     "mlora_gather_bgmv",
     "mlora_grouped_down",
+    "mlora_grouped_down_workspace_bytes",
 )
 
 
@@ -110,7 +111,8 @@ def load() -> ctypes.CDLL:
         "mlora_gather_bgmv": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, vp, vp, i64,
                                     i32, vp]),
         "mlora_grouped_down": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64, vp, i32,
-                                     vp, vp, i32, i64, i64, vp]),
+                                     vp, vp, i32, i64, i64, vp, ctypes.c_uint64, vp]),
+        "mlora_grouped_down_workspace_bytes": (ctypes.c_uint64, [i64, i64, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -311,10 +313,19 @@ def mlora_gather_bgmv(route: ExpertRoute, x, base_out, indices, row_adapter, top
         raise _err(rc)
 
 
+def mlora_grouped_down_workspace_bytes(row_offset: int, row_end: int, max_rank: int) -> int:
+    """Workspace bytes of the two-kernel grouped fold on [row_offset, row_end)."""
+    return int(load().mlora_grouped_down_workspace_bytes(int(row_offset), int(row_end),
+                                                         int(max_rank)))
+
+
 def mlora_grouped_down(route: ExpertRoute, x, base_out, expert_offsets, sorted_ids,
                        row_adapter, top_k: int, row_offset: int, row_end: int,
-                       stream=None) -> None:
-    """Grouped fold of sorted rows [row_offset, row_end) of ``base_out``, in place."""
+                       workspace=None, stream=None) -> None:
+    """Grouped fold of sorted rows [row_offset, row_end) of ``base_out``, in place.
+
+    ``workspace``: None (one kernel) or a contiguous device tensor of at least
+    ``mlora_grouped_down_workspace_bytes`` bytes (two kernels)."""
     import torch
     if _dtype_code(x) != route.dtype or _dtype_code(base_out) != route.dtype:
         raise TypeError("x / base_out dtype differs from the route's")
@@ -330,11 +341,15 @@ def mlora_grouped_down(route: ExpertRoute, x, base_out, expert_offsets, sorted_i
     n_route = expert_offsets.numel() - 1
     if n_route < 0:
         raise ValueError("expert_offsets needs at least one entry")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
     rc = load().mlora_grouped_down(
         ctypes.byref(route), _dev(x, "x"), x.shape[0], _dev(base_out, "base_out"), n_rows,
         _dev(expert_offsets, "expert_offsets", torch.int32), int(n_route),
         _dev(sorted_ids, "sorted_ids", torch.int32),
         _dev(row_adapter, "row_adapter", torch.int32), int(top_k), int(row_offset),
-        int(row_end), _stream_handle(stream))
+        int(row_end), ws_ptr, ws_bytes, _stream_handle(stream))
     if rc != MLORA_OK:
         raise _err(rc)

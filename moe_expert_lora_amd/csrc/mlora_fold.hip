@@ -118,6 +118,14 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return ((uint64_t)hi << 32) | lo;
 }
+// The 64-bit value (lo, hi) of lane `lane` (wave-uniform) as a scalar. The
+// builtin returns int: each half goes back through uint32_t, so the low word
+// is never sign-extended into the high one.
+__device__ __forceinline__ uint64_t lane_u64(uint32_t lo, uint32_t hi, int lane) {
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)lo, lane);
+  const uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)hi, lane);
+  return ((uint64_t)h << 32) | l;
+}
 __device__ __forceinline__ float uniform_f32(float v) {
   return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
 }
@@ -382,6 +390,83 @@ __device__ __forceinline__ void mma_store_expand(const ExpandBatch<NB, MB, UE>& 
   }
 }
 
+// Shrink of up to MB row blocks over this wave's k steps: H[rank][row] for
+// the k steps wave, wave + kWaves, ... (in increasing order).
+template <int NB, int MB>
+__device__ __forceinline__ void shrink_k(f32x4 (&hacc)[MB][NB], const Bufs& bf, int K, int R,
+                                         const Rows<MB>& rw, int nrb, int wave, int li, int g) {
+  constexpr int US = Batch<NB, MB>::US;
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) hacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = (K + 31) >> 5;
+  constexpr int kStep = kWaves * US;
+  // The next batch is requested before the current one is used, without a
+  // condition: steps past the end load nothing (their offsets are out of
+  // range), and straight-line code keeps the wait counts exact.
+  ShrinkBatch<NB, MB, US> s0b, s1b;
+  int s0 = wave;
+  load_shrink<NB, MB, US>(s0b, bf, K, R, rw, s0, nks, li, g);
+  while (s0 < nks) {
+    const int s1 = s0 + kStep;
+    load_shrink<NB, MB, US>(s1b, bf, K, R, rw, s1, nks, li, g);
+    mma_shrink<NB, MB, US>(hacc, s0b, nrb);
+    if (s1 >= nks) break;
+    const int s2 = s1 + kStep;
+    load_shrink<NB, MB, US>(s0b, bf, K, R, rw, s2, nks, li, g);
+    mma_shrink<NB, MB, US>(hacc, s1b, nrb);
+    s0 = s2;
+  }
+}
+
+// K-split reduction of the shrink through LDS, the partial sums of the waves
+// added in a fixed order, then the hi / lo operands of scale * H for each row
+// block. Every wave ends up with the operands of every row block. Contains a
+// workgroup barrier: all threads call it with the same arguments.
+template <int NB, int MB>
+__device__ __forceinline__ void reduce_split(const f32x4 (&hacc)[MB][NB], float* s_part,
+                                             float scale, int nrb, int wave, int lane,
+                                             HOp<NB> (&hop)[MB]) {
+  constexpr int HW = 4 * NB;  // ranks per lane
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    if (rb < nrb) {
+      float* dst = s_part + ((size_t)(wave * MB + rb) * 64 + lane) * HW;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        *reinterpret_cast<f32x4*>(dst + 4 * b) = hacc[rb][b];
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    if (rb < nrb) {
+#pragma unroll
+      for (int s = 0; s < NB; ++s) {
+        f32x4 h = *reinterpret_cast<const f32x4*>(
+            s_part + ((size_t)(0 * MB + rb) * 64 + lane) * HW + 4 * s);
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+          h += *reinterpret_cast<const f32x4*>(
+              s_part + ((size_t)(w * MB + rb) * 64 + lane) * HW + 4 * s);
+        const f32x4 v = scale * h;
+        const uint32_t hi01 = pack_bf16(v.x, v.y), hi23 = pack_bf16(v.z, v.w);
+        const uint32_t lo01 = pack_bf16(v.x - lo_f(hi01), v.y - hi_f(hi01));
+        const uint32_t lo23 = pack_bf16(v.z - lo_f(hi23), v.w - hi_f(hi23));
+        // ranks 4s .. 4s+3 of this lane: chunk (4s) / kRanks, word offset inside it
+        constexpr int CR = Chunk<NB>::kRanks;
+        const int q = (4 * s) / CR, w0 = ((4 * s) % CR) / 2;
+        hop[rb].hi[q][w0] = hi01;
+        hop[rb].hi[q][w0 + 1] = hi23;
+        hop[rb].lo[q][w0] = lo01;
+        hop[rb].lo[q][w0 + 1] = lo23;
+      }
+    }
+  }
+}
+
 // Folds rows 0..nrows-1 (nrows <= 16*MB) of one expert into columns
 // [n_lo, n_hi) of base_out. Row m writes base_out row
 // (s_row ? s_row[m] : row_base + m) of bf.out, from token s_tok[m]
@@ -391,7 +476,6 @@ template <int NB, int MB, bool FULL_R>
 __device__ void fold_rows(const Bufs& bf, int K, int N, int R, float scale, const int* s_row,
                           int row_base, const int* s_tok, int nrows, int n_lo, int n_hi,
                           float* s_part) {
-  constexpr int US = Batch<NB, MB>::US;
   constexpr int UE = Batch<NB, MB>::UE;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -418,74 +502,10 @@ __device__ void fold_rows(const Bufs& bf, int K, int N, int R, float scale, cons
   ExpandBatch<NB, MB, UE> e0, e1;
   load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, wave, ncs, n_lo, n_hi, li, g);
 
-  // ---- shrink: H[rank][row] over this wave's k steps ----------------------
   f32x4 hacc[MB][NB];
-#pragma unroll
-  for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) hacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nks = (K + 31) >> 5;
-  {
-    constexpr int kStep = kWaves * US;
-    // The next batch is requested before the current one is used, without a
-    // condition: steps past the end load nothing (their offsets are out of
-    // range), and straight-line code keeps the wait counts exact.
-    ShrinkBatch<NB, MB, US> s0b, s1b;
-    int s0 = wave;
-    load_shrink<NB, MB, US>(s0b, bf, K, R, rw, s0, nks, li, g);
-    while (s0 < nks) {
-      const int s1 = s0 + kStep;
-      load_shrink<NB, MB, US>(s1b, bf, K, R, rw, s1, nks, li, g);
-      mma_shrink<NB, MB, US>(hacc, s0b, nrb);
-      if (s1 >= nks) break;
-      const int s2 = s1 + kStep;
-      load_shrink<NB, MB, US>(s0b, bf, K, R, rw, s2, nks, li, g);
-      mma_shrink<NB, MB, US>(hacc, s1b, nrb);
-      s0 = s2;
-    }
-  }
-
-  // ---- K-split reduction through LDS (fixed order) -----------------------
-  constexpr int HW = 4 * NB;  // ranks per lane
-#pragma unroll
-  for (int rb = 0; rb < MB; ++rb) {
-    if (rb < nrb) {
-      float* dst = s_part + ((size_t)(wave * MB + rb) * 64 + lane) * HW;
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        *reinterpret_cast<f32x4*>(dst + 4 * b) = hacc[rb][b];
-    }
-  }
-  lds_barrier();
-
-  // hi / lo operands of scale * H, chunk by chunk (4 ranks at a time here).
+  shrink_k<NB, MB>(hacc, bf, K, R, rw, nrb, wave, li, g);
   HOp<NB> hop[MB];
-#pragma unroll
-  for (int rb = 0; rb < MB; ++rb) {
-    if (rb < nrb) {
-#pragma unroll
-      for (int s = 0; s < NB; ++s) {
-        f32x4 h = *reinterpret_cast<const f32x4*>(
-            s_part + ((size_t)(0 * MB + rb) * 64 + lane) * HW + 4 * s);
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w)
-          h += *reinterpret_cast<const f32x4*>(
-              s_part + ((size_t)(w * MB + rb) * 64 + lane) * HW + 4 * s);
-        const f32x4 v = scale * h;
-        const uint32_t hi01 = pack_bf16(v.x, v.y), hi23 = pack_bf16(v.z, v.w);
-        const uint32_t lo01 = pack_bf16(v.x - lo_f(hi01), v.y - hi_f(hi01));
-        const uint32_t lo23 = pack_bf16(v.z - lo_f(hi23), v.w - hi_f(hi23));
-        // ranks 4s .. 4s+3 of this lane: chunk (4s) / kRanks, word offset inside it
-        constexpr int CR = Chunk<NB>::kRanks;
-        const int q = (4 * s) / CR, w0 = ((4 * s) % CR) / 2;
-        hop[rb].hi[q][w0] = hi01;
-        hop[rb].hi[q][w0 + 1] = hi23;
-        hop[rb].lo[q][w0] = lo01;
-        hop[rb].lo[q][w0 + 1] = lo23;
-      }
-    }
-  }
+  reduce_split<NB, MB>(hacc, s_part, scale, nrb, wave, lane, hop);
 
   // ---- expand + read-modify-write, two batches in flight -------------------
   {
@@ -821,6 +841,10 @@ struct GroupedArgs {
   int32_t n_experts, K, N, R, n_route, top_k, n_tokens;
   uint32_t top_k_magic;
   int32_t n_tiles, ns_count, ns_cols, units, per_xcd;  // units = tiles * sub-tiles * ns
+  // two-kernel form only: the workspace regions
+  uint8_t* ws_h;
+  uint64_t* ws_meta;
+  uint32_t ws_h_bytes, ws_meta_bytes;
 };
 
 // One workgroup folds a sub-tile of 16*MB rows of one MLORA_MLG_M_TILE-row
@@ -896,6 +920,309 @@ __global__ __launch_bounds__(kThreads) void grouped_fold_kernel(GroupedArgs p) {
     for (int c = lo; c < hi; c += 16 * MB)
       fold_rows<NB, MB, FULL_R>(bf, p.K, p.N, p.R, scale, nullptr, tile_row + c, s_tok + c,
                                 min(16 * MB, hi - c), n_lo, n_hi, s_part);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grouped (prefill), two-kernel form: shrink into a workspace, then expand
+// ---------------------------------------------------------------------------
+
+// Workspace of a window of L rows, RP = 16 * NB (the kernels' rank blocks):
+//   h     L rows of 4*RP bytes: RP bf16 of hi(scale_e * H[row]) (the lane
+//         order of the shrink: lane group g holds ranks g*4NB .. g*4NB+4NB-1),
+//         then RP bf16 of lo;
+//   meta  L uint64 at a 256-byte boundary: the B_e address of the row's expert
+//         when the row folds, 0 when it folds nothing.
+// The shrink kernel writes both for every row of the window; the expand
+// kernel reads them. Nothing in it carries over from one call to the next.
+
+__device__ __forceinline__ void bst8(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(
+      __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r, off, 0, 0);
+}
+
+// The 2*NB words of one half (hi or lo) of a lane's H operands, to / from
+// 8*NB consecutive bytes. `ok` false: nothing stored, zeros loaded.
+template <int NB>
+__device__ __forceinline__ void store_half(rsrc_t r, bool ok, uint32_t off,
+                                           const uint32_t (&w)[Chunk<NB>::kCount][Chunk<NB>::kWords]) {
+  if constexpr (NB == 1) {
+    bst8(r, ok ? off : kOOB, u32x2{w[0][0], w[0][1]});
+  } else {
+#pragma unroll
+    for (int q = 0; q < Chunk<NB>::kCount; ++q)
+      bst16(r, ok ? off + 16u * q : kOOB, u32x4{w[q][0], w[q][1], w[q][2], w[q][3]});
+  }
+}
+template <int NB>
+__device__ __forceinline__ void load_half(rsrc_t r, bool ok, uint32_t off,
+                                          uint32_t (&w)[Chunk<NB>::kCount][Chunk<NB>::kWords]) {
+  if constexpr (NB == 1) {
+    const u32x2 v = bld8(r, ok ? off : kOOB);
+    w[0][0] = v.x;
+    w[0][1] = v.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < Chunk<NB>::kCount; ++q) {
+      const u32x4 v = bld16(r, ok ? off + 16u * q : kOOB);
+      w[q][0] = v.x;
+      w[q][1] = v.y;
+      w[q][2] = v.z;
+      w[q][3] = v.w;
+    }
+  }
+}
+
+// Non-temporal 16-byte access (base_out is read once and written once).
+constexpr int kNT = 2;
+__device__ __forceinline__ u32x4 bld16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
+}
+__device__ __forceinline__ void bst16_nt(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, kNT);
+}
+
+// Orders one wave's LDS writes before its later LDS reads of other lanes'
+// data (the lanes of a wave run in lockstep; this only stops the compiler
+// from reordering across it).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Shrink: one workgroup per 16*MB rows of the window. The routing of its rows
+// (sorted_ids, the expert spans and the table cells of every expert) is
+// requested in one round; the rows' map entries, x rows and A_e fragments in
+// the next. Each expert span meeting the rows goes through the K-split shrink
+// and reduction of the one-kernel form, so H' comes out bit for bit the same.
+template <int NB, int MB>
+__global__ __launch_bounds__(kThreads) void grouped_shrink_kernel(GroupedArgs p) {
+  constexpr int kRows = 16 * MB;
+  constexpr uint32_t kRowBytes = 64u * NB;  // 4 * RP
+  __shared__ float s_part[kWaves * MB * 64 * 4 * NB];
+  __shared__ int s_tok[kRows];
+  __shared__ int s_live[kRows];
+  __shared__ int s_seg_lo[kRows], s_seg_hi[kRows];
+  __shared__ uint64_t s_seg_a[kRows], s_seg_b[kRows];
+  __shared__ float s_seg_s[kRows];
+  __shared__ int s_nseg;
+
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * p.per_xcd + slot;
+  if (u >= p.units) return;
+  const int64_t r0 = p.row_offset + (int64_t)u * kRows;
+  const int64_t r1 = min(r0 + kRows, p.row_end);
+  const int tid = threadIdx.x;
+
+  // round 1: this thread's row id, and span + table cells of expert e = tid
+  int id = -1;
+  if (tid < kRows && r0 + tid < r1) id = p.sorted_ids[r0 + tid];
+  if (tid == 0) s_nseg = 0;
+  lds_barrier();
+  for (int e = tid; e < p.n_route; e += kThreads) {
+    const int64_t lo = max((int64_t)p.offsets[e], r0);
+    const int64_t hi = min((int64_t)p.offsets[e + 1], r1);
+    uint64_t a_addr = 0, b_addr = 0;
+    float sc = 0.f;
+    if (e < p.n_experts) {
+      a_addr = p.a_table[e];
+      b_addr = p.b_table[e];
+      sc = p.scale_table[e];
+    }
+    // spans of experts without both matrices fold nothing
+    if (lo < hi && a_addr != 0 && b_addr != 0) {
+      const int k = atomicAdd(&s_nseg, 1);
+      if (k < kRows) {
+        s_seg_lo[k] = (int)(lo - r0);
+        s_seg_hi[k] = (int)(hi - r0);
+        s_seg_a[k] = a_addr;
+        s_seg_b[k] = b_addr;
+        s_seg_s[k] = sc;
+      }
+    }
+  }
+  int tok = -1;
+  if (id >= 0) {
+    const int cand = (int)udiv((uint32_t)id, (uint32_t)p.top_k, p.top_k_magic);
+    if (cand < p.n_tokens) tok = cand;
+  }
+  if (tid < kRows) s_tok[tid] = tok;
+  lds_barrier();
+  const int nseg = min(__builtin_amdgcn_readfirstlane(s_nseg), kRows);
+
+  // round 2: the map entry of this thread's row; consumed after the shrink
+  // loads of the first span are in flight
+  int map = -1;
+  if (tok >= 0) map = p.row_adapter[tok];
+
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int tile_row = (int)(r0 - p.row_offset);
+  const rsrc_t r_h = make_buf(p.ws_h, p.ws_h_bytes);
+  Bufs bf;
+  bf.x = make_buf(p.x, p.x_bytes);
+  uint64_t my_meta = 0;  // thread t < kRows: meta of row t
+  for (int sg = 0; sg < nseg; ++sg) {
+    const uint64_t a_addr = uniform_u64(s_seg_a[sg]), b_addr = uniform_u64(s_seg_b[sg]);
+    const float scale = uniform_f32(s_seg_s[sg]);
+    bf.a = make_buf(reinterpret_cast<const void*>(a_addr), (uint32_t)(p.R * p.K) * 2u);
+    const int lo = __builtin_amdgcn_readfirstlane(s_seg_lo[sg]);
+    const int hi = __builtin_amdgcn_readfirstlane(s_seg_hi[sg]);
+    const int nrows = hi - lo, nrb = (nrows + 15) >> 4;
+    Rows<MB> rw;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      const int m = rb * 16 + li;
+      const int t = m < nrows ? s_tok[lo + m] : -1;
+      rw.valid[rb] = t >= 0;
+      rw.xoff[rb] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)p.K * 2u;
+      rw.ooff[rb] = 0;
+    }
+    f32x4 hacc[MB][NB];
+    shrink_k<NB, MB>(hacc, bf, p.K, p.R, rw, nrb, wave, li, g);
+    if (sg == 0 && tid < kRows) s_live[tid] = (tok >= 0 && map >= 0) ? 1 : 0;
+    HOp<NB> hop[MB];
+    reduce_split<NB, MB>(hacc, s_part, scale, nrb, wave, lane, hop);
+    // row block rb is written by wave rb % kWaves, live rows only
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      if (rb % kWaves == wave && rb < nrb) {
+        const int m = rb * 16 + li;
+        const bool ok = m < nrows && s_live[lo + m] != 0;
+        const uint32_t off =
+            (uint32_t)(tile_row + lo + m) * kRowBytes + (uint32_t)g * 8u * NB;
+        store_half<NB>(r_h, ok, off, hop[rb].hi);
+        store_half<NB>(r_h, ok, off + 32u * NB, hop[rb].lo);
+      }
+    }
+    if (tid >= lo && tid < hi && tok >= 0 && map >= 0) my_meta = b_addr;
+    lds_barrier();  // s_part is rewritten by the next span
+  }
+  if (tid < kRows && r0 + tid < r1) {
+    const rsrc_t r_meta = make_buf(p.ws_meta, p.ws_meta_bytes);
+    bst8(r_meta, (uint32_t)(tile_row + tid) * 8u,
+         u32x2{(uint32_t)my_meta, (uint32_t)(my_meta >> 32)});
+  }
+}
+
+// Expand: one wave per (16*MB rows, CW column steps). It reads the rows' meta,
+// then requests H', the B_e fragments of the first run of rows (rows with one
+// B_e) and the rows' base_out, the last in a row-contiguous layout: LPR lanes
+// cover one row's CW*32 columns, 16 bytes each. The MFMA deltas (fp32, one
+// lane per row) go through the wave's own LDS to that layout; each row is
+// then rounded once and stored.
+template <int NB, int MB, int CW, bool FULL_R>
+__global__ __launch_bounds__(64) void grouped_expand_kernel(GroupedArgs p) {
+  constexpr int kRows = 16 * MB;
+  constexpr int kCols = CW * kColStep;
+  constexpr int kStride = kCols + 4;  // fp32 per LDS row; the pad spreads rows over banks
+  constexpr int LPR = kCols / 8;      // lanes per row in the contiguous layout
+  constexpr int RPI = 64 / LPR;       // rows per contiguous access
+  constexpr int NI = kRows / RPI;     // contiguous accesses per wave
+  constexpr uint32_t kRowBytes = 64u * NB;
+  constexpr int CC = Chunk<NB>::kCount;
+  static_assert(kRows <= 64 && 64 % LPR == 0 && kRows % RPI == 0, "expand shape");
+  __shared__ float s_d[kRows * kStride];
+
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * p.per_xcd + slot;
+  if (u >= p.units) return;
+  const int ns = u % p.ns_count;
+  const int r0 = (u / p.ns_count) * kRows;  // window-relative
+  const int lane = threadIdx.x, li = lane & 15, g = lane >> 4;
+
+  // rows past the window lie past the meta buffer and read as 0
+  const rsrc_t r_meta = make_buf(p.ws_meta, p.ws_meta_bytes);
+  const u32x2 mv = bld8(r_meta, lane < kRows ? (uint32_t)(r0 + lane) * 8u : kOOB);
+  const bool is_live = (mv.x | mv.y) != 0;
+  const uint64_t live = __ballot(is_live);
+  if (live == 0) return;
+  // a run starts at a live row whose previous live row has another B_e
+  const uint64_t below = live & ((1ull << lane) - 1ull);
+  const int prev = below ? 63 - __clzll((long long)below) : lane;
+  const uint32_t plo = (uint32_t)__shfl((int)mv.x, prev), phi = (uint32_t)__shfl((int)mv.y, prev);
+  uint64_t starts = __ballot(is_live && (below == 0 || plo != mv.x || phi != mv.y));
+
+  const int n_lo = ns * kCols;
+  const int n_hi = min(n_lo + kCols, p.N);
+  const rsrc_t r_out = make_buf(p.out, p.out_bytes);
+  const rsrc_t r_h = make_buf(p.ws_h, p.ws_h_bytes);
+
+  // base_out, row-contiguous
+  const int cr = lane / LPR, cc = lane % LPR;
+  u32x4 bv[NI];
+  uint32_t boff[NI];
+  bool bok[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = i * RPI + cr;
+    const int col = n_lo + 8 * cc;
+    bok[i] = ((live >> row) & 1ull) != 0 && col < n_hi;
+    boff[i] = (uint32_t)(r0 + row) * (uint32_t)p.N * 2u + 2u * col;
+    bv[i] = bld16_nt(r_out, bok[i] ? boff[i] : kOOB);
+  }
+  // H' operands, one lane per row
+  HOp<NB> hop[MB];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    const int row = rb * 16 + li;
+    const bool lv = ((live >> row) & 1ull) != 0;
+    const uint32_t hoff = (uint32_t)(r0 + row) * kRowBytes + (uint32_t)g * 8u * NB;
+    load_half<NB>(r_h, lv, hoff, hop[rb].hi);
+    load_half<NB>(r_h, lv, hoff + 32u * NB, hop[rb].lo);
+  }
+
+  while (starts) {
+    const int s = __ffsll((unsigned long long)starts) - 1;
+    starts &= starts - 1ull;
+    const int e_row = starts ? __ffsll((unsigned long long)starts) - 1 : 64;
+    const uint64_t b_addr = lane_u64(mv.x, mv.y, s);
+    const rsrc_t r_b =
+        make_buf(reinterpret_cast<const void*>(b_addr), (uint32_t)(p.N * p.R) * 2u);
+    BFrag<NB> bw[CW];
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+      load_bfrag<NB, FULL_R>(bw[c], r_b, p.R, n_lo + c * kColStep, n_hi, li, g);
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      if (rb * 16 < e_row && rb * 16 + 16 > s) {
+        const int row = rb * 16 + li;
+        const bool in = row >= s && row < e_row;
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+          f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q = 0; q < CC; ++q) {
+            d0 = mfma_chunk(bw[c].w[0][q], hop[rb].hi[q], d0);
+            d1 = mfma_chunk(bw[c].w[1][q], hop[rb].hi[q], d1);
+            d0 = mfma_chunk(bw[c].w[0][q], hop[rb].lo[q], d0);
+            d1 = mfma_chunk(bw[c].w[1][q], hop[rb].lo[q], d1);
+          }
+          // lane (g, li) holds columns 8g .. 8g+7 of the step for its row
+          if (in) {
+            float* dst = s_d + row * kStride + c * kColStep + 8 * g;
+            *reinterpret_cast<f32x4*>(dst) = d0;
+            *reinterpret_cast<f32x4*>(dst + 4) = d1;
+          }
+        }
+      }
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const float* src = s_d + (i * RPI + cr) * kStride + 8 * cc;
+    const f32x4 d0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 d1 = *reinterpret_cast<const f32x4*>(src + 4);
+    const u32x4 bq = bv[i];
+    const uint32_t o0 = pack_bf16(lo_f(bq.x) + d0.x, hi_f(bq.x) + d0.y);
+    const uint32_t o1 = pack_bf16(lo_f(bq.y) + d0.z, hi_f(bq.y) + d0.w);
+    const uint32_t o2 = pack_bf16(lo_f(bq.z) + d1.x, hi_f(bq.z) + d1.y);
+    const uint32_t o3 = pack_bf16(lo_f(bq.w) + d1.z, hi_f(bq.w) + d1.w);
+    bst16_nt(r_out, bok[i] ? boff[i] : kOOB, u32x4{o0, o1, o2, o3});
   }
 }
 
@@ -1203,13 +1530,114 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   return launched(who);
 }
 
+// Workspace layout of the two-kernel grouped form (see the kernels).
+struct WsLayout {
+  int64_t h_bytes, meta_off, meta_bytes, total;
+};
+
+// Rank blocks the kernels use for max_rank R: ceil(R / 16) rounded up to 1,
+// 2, 4 or 8.
+int kernel_nb(int R) {
+  const int nb = (R + 15) / 16;
+  return nb <= 1 ? 1 : (nb <= 2 ? 2 : (nb <= 4 ? 4 : 8));
+}
+
+WsLayout grouped_ws_layout(int64_t rows, int R) {
+  WsLayout w;
+  const int64_t rp = 16 * (int64_t)kernel_nb(R);
+  w.h_bytes = rows * 4 * rp;
+  w.meta_off = (w.h_bytes + 255) & ~(int64_t)255;
+  w.meta_bytes = rows * 8;
+  w.total = (w.meta_off + w.meta_bytes + 255) & ~(int64_t)255;
+  return w;
+}
+
+// Row blocks per expand wave: the largest of `want` (1, 2 or 4) the rank
+// width supports.
+int expand_mb(int R, int want) {
+  const int nb = kernel_nb(R);
+  const int cap = nb <= 2 ? 4 : (nb <= 4 ? 2 : 1);
+  want = want >= 4 ? 4 : (want >= 2 ? 2 : 1);
+  return want < cap ? want : cap;
+}
+
+template <int NB>
+void launch_shrink(const GroupedArgs& a, int grid, hipStream_t s, int mb) {
+  if (mb >= 2)
+    hipLaunchKernelGGL((grouped_shrink_kernel<NB, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_shrink_kernel<NB, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+
+void dispatch_shrink(const GroupedArgs& a, int grid, hipStream_t s, int mb) {
+  const int nb = (a.R + 15) / 16;
+  if (nb <= 1) launch_shrink<1>(a, grid, s, mb);
+  else if (nb <= 2) launch_shrink<2>(a, grid, s, mb);
+  else if (nb <= 4) launch_shrink<4>(a, grid, s, mb);
+  else launch_shrink<8>(a, grid, s, 1);
+}
+
+// Column steps per expand wave: 4 where the operands leave room (full rank
+// blocks of at most 32 ranks), else 2.
+int expand_cw(int R, int requested) {
+  const int nb = (R + 15) / 16;
+  return (R == 16 * nb && nb <= 2 && requested >= 4) ? 4 : 2;
+}
+
+template <int NB, int MB>
+void launch_expand(const GroupedArgs& a, int grid, hipStream_t s, int cw) {
+  const bool full = a.R == 16 * NB;
+  if (!full) {
+    hipLaunchKernelGGL((grouped_expand_kernel<NB, MB, 2, false>), dim3(grid), dim3(64), 0, s, a);
+  } else if constexpr (NB <= 2) {
+    if (cw >= 4)
+      hipLaunchKernelGGL((grouped_expand_kernel<NB, MB, 4, true>), dim3(grid), dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((grouped_expand_kernel<NB, MB, 2, true>), dim3(grid), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((grouped_expand_kernel<NB, MB, 2, true>), dim3(grid), dim3(64), 0, s, a);
+  }
+}
+
+template <int NB>
+void launch_expand_mb(const GroupedArgs& a, int grid, hipStream_t s, int mb, int cw) {
+  if constexpr (NB <= 2) {
+    if (mb >= 4) return launch_expand<NB, 4>(a, grid, s, cw);
+  }
+  if constexpr (NB <= 4) {
+    if (mb >= 2) return launch_expand<NB, 2>(a, grid, s, cw);
+  }
+  launch_expand<NB, 1>(a, grid, s, cw);
+}
+
+void dispatch_expand(const GroupedArgs& a, int grid, hipStream_t s, int mb, int cw) {
+  switch (kernel_nb(a.R)) {
+    case 1: return launch_expand_mb<1>(a, grid, s, mb, cw);
+    case 2: return launch_expand_mb<2>(a, grid, s, mb, cw);
+    case 4: return launch_expand_mb<4>(a, grid, s, mb, cw);
+    default: return launch_expand_mb<8>(a, grid, s, mb, cw);
+  }
+}
+
+extern "C" uint64_t mlora_grouped_down_workspace_bytes(int64_t row_offset, int64_t row_end,
+                                                       int32_t max_rank) {
+  if (row_offset < 0 || row_end < row_offset || max_rank < 1 || max_rank > 128) return 0;
+  if (row_end == row_offset) return 0;
+  return (uint64_t)grouped_ws_layout(row_end - row_offset, max_rank).total;
+}
+
 extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const void* x,
                                       int64_t n_tokens, void* base_out, int64_t n_rows,
                                       const int32_t* expert_offsets, int32_t n_route,
                                       const int32_t* sorted_ids, const int32_t* row_adapter,
                                       int32_t top_k, int64_t row_offset, int64_t row_end,
+                                      void* workspace, uint64_t workspace_bytes,
                                       void* stream) {
   const char* who = "mlora_grouped_down";
+  if (!workspace && workspace_bytes != 0)
+    return fail(MLORA_ERR_INVALID, "%s: NULL workspace with workspace_bytes > 0", who);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MLORA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
   if (int32_t rc = check_route(route, who)) return rc;
   if (top_k <= 0) return fail(MLORA_ERR_INVALID, "%s: top_k=%d must be positive", who, top_k);
   if (n_route < 0) return fail(MLORA_ERR_INVALID, "%s: n_route < 0", who);
@@ -1224,6 +1652,10 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
   }
   if (!x || !base_out || !expert_offsets || !sorted_ids || !row_adapter)
     return fail(MLORA_ERR_INVALID, "%s: NULL device pointer", who);
+  const WsLayout wsl = grouped_ws_layout(row_end - row_offset, route->max_rank);
+  if (workspace && route->dtype == MLORA_BF16 && (uint64_t)wsl.total > workspace_bytes)
+    return fail(MLORA_ERR_CAPACITY, "%s: workspace of %llu bytes, %lld needed", who,
+                (unsigned long long)workspace_bytes, (long long)wsl.total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
 
@@ -1258,6 +1690,59 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
   const int64_t x_bytes = n_tokens * K * 2, out_bytes = (row_end - row_offset) * N * 2;
   if (x_bytes > (int64_t)kMaxBufBytes || out_bytes > (int64_t)kMaxBufBytes)
     return fail(MLORA_ERR_INVALID, "%s: x or the window of base_out exceeds 4 GiB", who);
+  GroupedArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.out = static_cast<uint16_t*>(base_out) + row_offset * N;
+  a.offsets = expert_offsets;
+  a.sorted_ids = sorted_ids;
+  a.row_adapter = row_adapter;
+  a.a_table = route->a_table;
+  a.b_table = route->b_table;
+  a.scale_table = route->scale_table;
+  a.x_bytes = (uint32_t)x_bytes;
+  a.out_bytes = (uint32_t)out_bytes;
+  a.row_offset = row_offset;
+  a.row_end = row_end;
+  a.n_experts = route->n_experts;
+  a.K = K;
+  a.N = N;
+  a.R = R;
+  a.n_route = n_route;
+  a.top_k = top_k;
+  a.n_tokens = (int32_t)n_tokens;
+  a.top_k_magic = magic_for(top_k);
+
+  if (workspace) {
+    const int64_t rows = row_end - row_offset;
+    const WsLayout& w = wsl;
+    if (w.h_bytes > (int64_t)kMaxBufBytes || w.meta_bytes > (int64_t)kMaxBufBytes)
+      return fail(MLORA_ERR_INVALID, "%s: window too large for one workspace; split it", who);
+    a.ws_h = static_cast<uint8_t*>(workspace);
+    a.ws_meta = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + w.meta_off);
+    a.ws_h_bytes = (uint32_t)w.h_bytes;
+    a.ws_meta_bytes = (uint32_t)w.meta_bytes;
+    // shrink: one workgroup per 16 * smb rows
+    int smb = env_int("MLORA_SHRINK_MB", 1);
+    smb = smb >= 2 ? 2 : 1;
+    const int64_t sunits = (rows + 16 * smb - 1) / (16 * smb);
+    // expand: one wave per (16 * emb rows, cw column steps)
+    const int emb = expand_mb(R, env_int("MLORA_EXPAND_MB", 1));
+    const int cw = expand_cw(R, env_int("MLORA_EXPAND_CW", 4));
+    const int64_t etiles = (rows + 16 * emb - 1) / (16 * emb);
+    const int64_t eslices = (N + cw * kColStep - 1) / (cw * kColStep);
+    if (sunits > 0x3fffffffll || etiles * eslices > 0x3fffffffll)
+      return fail(MLORA_ERR_INVALID, "%s: window too large", who);
+    a.units = (int32_t)sunits;
+    a.per_xcd = (int32_t)((sunits + kXcds - 1) / kXcds);
+    dispatch_shrink(a, a.per_xcd * kXcds, s, smb);
+    if (int32_t rc = launched(who)) return rc;
+    a.ns_count = (int32_t)eslices;
+    a.units = (int32_t)(etiles * eslices);
+    a.per_xcd = (int32_t)((a.units + kXcds - 1) / kXcds);
+    dispatch_expand(a, a.per_xcd * kXcds, s, emb, cw);
+    return launched(who);
+  }
+
   const int64_t tiles = mlora_grouped_down_wc(row_offset, row_end);
   const int ns_max = (N + kColStep - 1) / kColStep;
   // Split a tile's rows over workgroups first (no operand is read twice but
@@ -1281,27 +1766,6 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
   const int64_t units = tiles * (4 / mb) * ns;
   if (units > 0x7fffffffll / 2) return fail(MLORA_ERR_INVALID, "%s: window too large", who);
 
-  GroupedArgs a{};
-  a.x = static_cast<const uint16_t*>(x);
-  a.out = static_cast<uint16_t*>(base_out) + row_offset * N;
-  a.offsets = expert_offsets;
-  a.sorted_ids = sorted_ids;
-  a.row_adapter = row_adapter;
-  a.a_table = route->a_table;
-  a.b_table = route->b_table;
-  a.scale_table = route->scale_table;
-  a.x_bytes = (uint32_t)x_bytes;
-  a.out_bytes = (uint32_t)out_bytes;
-  a.row_offset = row_offset;
-  a.row_end = row_end;
-  a.n_experts = route->n_experts;
-  a.K = K;
-  a.N = N;
-  a.R = R;
-  a.n_route = n_route;
-  a.top_k = top_k;
-  a.n_tokens = (int32_t)n_tokens;
-  a.top_k_magic = magic_for(top_k);
   a.n_tiles = (int32_t)tiles;
   a.ns_count = ns;
   a.ns_cols = ns_cols_for(N, ns);

@@ -38,9 +38,11 @@ def u64_to_device(a: np.ndarray, device) -> torch.Tensor:
 class DeviceCase:
     """Everything one fold call needs, resident on the GPU."""
 
-    def __init__(self, case: FoldCase, device="cuda"):
+    def __init__(self, case: FoldCase, device="cuda", two_kernel: bool = True):
         self.case = case
         self.device = device
+        self.two_kernel = two_kernel
+        self._ws = None
         c = case
         self.tdtype = torch.bfloat16 if c.dtype == "bf16" else torch.float32
         self.x = to_torch(c.x, c.dtype, device)
@@ -90,21 +92,38 @@ class DeviceCase:
             self.offsets = torch.from_numpy(np.ascontiguousarray(c.expert_offsets, np.int32)).to(device)
             self.windows = ml.mlora_grouped_down_windows(c.n_rows, c.cap)
 
-    def fold(self, base: torch.Tensor, windows=None, stream=None) -> torch.Tensor:
-        """Fold in place into ``base`` (a device tensor shaped like base_out)."""
+    def workspace_for(self, windows) -> torch.Tensor:
+        """A device workspace large enough for every window (grown on demand)."""
+        need = max([ml.mlora_grouped_down_workspace_bytes(s, e, self.case.max_rank)
+                    for (s, e) in windows] + [0])
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def fold(self, base: torch.Tensor, windows=None, stream=None,
+             two_kernel: bool = None) -> torch.Tensor:
+        """Fold in place into ``base`` (a device tensor shaped like base_out).
+        Grouped calls take the two-kernel form (with a workspace) when
+        ``two_kernel`` is set, else the one-kernel form; None means the
+        case's default (``self.two_kernel``)."""
         c = self.case
         if c.path == "gather":
             ml.mlora_gather_bgmv(self.route, self.x, base, self.indices, self.row_adapter,
                                  c.top_k, stream=stream)
         else:
-            for (s, e) in (self.windows if windows is None else windows):
+            wins = self.windows if windows is None else windows
+            two = self.two_kernel if two_kernel is None else two_kernel
+            ws = self.workspace_for(wins) if two else None
+            for (s, e) in wins:
                 ml.mlora_grouped_down(self.route, self.x, base, self.offsets, self.sorted_ids,
-                                      self.row_adapter, c.top_k, s, e, stream=stream)
+                                      self.row_adapter, c.top_k, s, e, workspace=ws,
+                                      stream=stream)
         return base
 
-    def run(self, base_host: np.ndarray = None, windows=None) -> np.ndarray:
+    def run(self, base_host: np.ndarray = None, windows=None,
+            two_kernel: bool = None) -> np.ndarray:
         base = self.base0.clone() if base_host is None else to_torch(base_host, self.case.dtype,
                                                                      self.device)
-        self.fold(base, windows=windows)
+        self.fold(base, windows=windows, two_kernel=two_kernel)
         torch.cuda.synchronize()
         return from_torch(base)

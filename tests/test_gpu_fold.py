@@ -312,6 +312,48 @@ def test_small_cases(label, kw):
     assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
 
 
+GROUPED_SMALL = [s for s in SMALL if s[1]["kind"] == "grouped"]
+
+
+@pytest.mark.parametrize("label", ["cfg3", "cfg5b"] + [s[0] for s in GROUPED_SMALL])
+def test_grouped_two_kernel_equals_one_kernel(label):
+    """The workspace (shrink, then expand) form and the one-kernel form of the
+    grouped fold give the same bits, and the one-kernel form passes the
+    oracle bar on its own (the other tests run the two-kernel form)."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    if label.startswith("cfg"):
+        case, view, dev = staged(label)
+    else:
+        case = build_small(label, dict(SMALL)[label])
+        view, dev = OracleView(case), DeviceCase(case, DEV)
+    one = dev.run(two_kernel=False)
+    check(view, one, case.base, f"{label} one-kernel")
+    two = dev.run(two_kernel=True)
+    assert np.array_equal(one.view(np.uint8), two.view(np.uint8))
+
+
+def test_grouped_workspace_reused_across_windows_and_calls():
+    """One workspace serves successive windows and calls; stale contents from a
+    larger call never leak into a smaller one."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    big = workloads.make_grouped_case(91, stream_lens=[300, 211], top_k=4, n_route=12,
+                                      k_in=256, n_out=384, max_rank=32, routing="zipf",
+                                      n_unadapted=2, cap=256)
+    small = workloads.make_grouped_case(92, stream_lens=[40], top_k=2, n_route=12,
+                                        k_in=256, n_out=384, max_rank=32, n_unadapted=5,
+                                        cap=64, stream_slot_values=[1])
+    db, ds = DeviceCase(big, DEV), DeviceCase(small, DEV)
+    ds._ws = db.workspace_for(db.windows)  # shared
+    for _ in range(2):
+        got_b = db.run()
+        ds._ws = db._ws
+        got_s = ds.run()
+        check(OracleView(big), got_b, big.base, "big")
+        check(OracleView(small), got_s, small.base, "small")
+
+
 @pytest.mark.parametrize("label", ["cfg2", "gather_r24_k72", "gather_slots_not_multiple",
                                    "gather_r16_ns4"])
 def test_resident_weights_path_equals_streaming_path(label, monkeypatch):

@@ -277,7 +277,7 @@ def test_grouped_rejects_bad_args(lib):
     call = lambda **k: lib.mlora_grouped_down(  # noqa: E731
         ctypes.byref(k.get("route", r)), FAKE, k.get("n_tok", 4), FAKE, k.get("n_rows", 8),
         FAKE, k.get("n_route", 4), FAKE, FAKE, k.get("top_k", 2), k.get("off", 0),
-        k.get("end", 8), None)
+        k.get("end", 8), k.get("ws", None), k.get("ws_bytes", 0), None)
     assert call(top_k=0) == -1
     assert call(off=5, end=4) == -1
     assert call(end=9) == -1
@@ -287,6 +287,26 @@ def test_grouped_rejects_bad_args(lib):
     assert call(route=_route(max_rank=200)) == -1
     assert call(off=3, end=3) == 0          # empty window
     assert call(n_route=0) == 0             # no spans
+    # workspace: NULL with a size, misaligned, too small
+    assert call(ws_bytes=256) == -1
+    assert call(ws=FAKE + 16, ws_bytes=1 << 20) == -1
+    need = lib.mlora_grouped_down_workspace_bytes(0, 8, 16)
+    assert call(ws=FAKE, ws_bytes=need - 1) == ml.MLORA_ERR_CAPACITY
+
+
+def test_grouped_workspace_bytes(lib):
+    f = lib.mlora_grouped_down_workspace_bytes
+    # rows * 64 * NB (NB = ceil(r / 16) rounded up to a power of two), rounded
+    # to 256, then 8 bytes per row, rounded
+    assert f(0, 8, 16) == 512 + 256
+    assert f(0, 8, 100) == 8 * 512 + 256   # 7 rank blocks run as 8
+    assert f(0, 8, 48) == 8 * 256 + 256    # 3 rank blocks run as 4
+    assert f(10, 20, 17) == 1280 + 256
+    assert f(0, 8192, 32) == 8192 * 128 + 8192 * 8
+    assert f(0, 1, 128) == 512 + 256
+    assert f(5, 5, 16) == 0
+    assert f(5, 4, 16) == 0 and f(-1, 4, 16) == 0
+    assert f(0, 8, 0) == 0 and f(0, 8, 129) == 0
 
 
 def test_single_hip_runtime_in_process():
