@@ -406,17 +406,24 @@ __device__ __forceinline__ void shrink_k(f32x4 (&hacc)[MB][NB], const Bufs& bf, 
   // The next batch is requested before the current one is used, without a
   // condition: steps past the end load nothing (their offsets are out of
   // range), and straight-line code keeps the wait counts exact.
+  // The scheduling barriers keep each batch's loads ahead of the MFMAs of the
+  // batch before it (the scheduler would otherwise sink them below, and the
+  // loop would wait for every load at its head).
   ShrinkBatch<NB, MB, US> s0b, s1b;
   int s0 = wave;
   load_shrink<NB, MB, US>(s0b, bf, K, R, rw, s0, nks, li, g);
   while (s0 < nks) {
     const int s1 = s0 + kStep;
     load_shrink<NB, MB, US>(s1b, bf, K, R, rw, s1, nks, li, g);
+    __builtin_amdgcn_sched_barrier(0);
     mma_shrink<NB, MB, US>(hacc, s0b, nrb);
+    __builtin_amdgcn_sched_barrier(0);
     if (s1 >= nks) break;
     const int s2 = s1 + kStep;
     load_shrink<NB, MB, US>(s0b, bf, K, R, rw, s2, nks, li, g);
+    __builtin_amdgcn_sched_barrier(0);
     mma_shrink<NB, MB, US>(hacc, s1b, nrb);
+    __builtin_amdgcn_sched_barrier(0);
     s0 = s2;
   }
 }
@@ -514,11 +521,15 @@ __device__ void fold_rows(const Bufs& bf, int K, int N, int R, float scale, cons
     while (c0 < ncs) {
       const int c1 = c0 + kStep;
       load_expand<NB, MB, UE, FULL_R>(e1, bf, R, rw, c1, ncs, n_lo, n_hi, li, g);
+      __builtin_amdgcn_sched_barrier(0);
       mma_store_expand<NB, MB, UE>(e0, hop, bf, rw, nrb, c0, ncs, n_lo, n_hi, g);
+      __builtin_amdgcn_sched_barrier(0);
       if (c1 >= ncs) break;
       const int c2 = c1 + kStep;
       load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, c2, ncs, n_lo, n_hi, li, g);
+      __builtin_amdgcn_sched_barrier(0);
       mma_store_expand<NB, MB, UE>(e1, hop, bf, rw, nrb, c1, ncs, n_lo, n_hi, g);
+      __builtin_amdgcn_sched_barrier(0);
       c0 = c2;
     }
   }
@@ -599,16 +610,15 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
   const int rounds = (end - start + kThreads - 1) / kThreads;  // wave-uniform, <= kPer
   int iv[kPer], mv[kPer];
 #pragma unroll
+  // Loads for every round, those past the slice at an out-of-range offset:
+  // straight-line code keeps the wait before the scan exact, so it does not
+  // also wait for the weight loads issued after these.
   for (int i = 0; i < kPer; ++i) {
-    iv[i] = -1;
-    mv[i] = -1;
-    if (i < rounds) {
-      const int row = start + i * kThreads + (int)threadIdx.x;
-      const bool in = row < end;
-      const uint32_t tok = udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
-      iv[i] = (int)bld4(r_idx, in ? (uint32_t)row * 4u : kOOB);
-      mv[i] = (int)bld4(r_map, in ? tok * 4u : kOOB);
-    }
+    const int row = start + i * kThreads + (int)threadIdx.x;
+    const bool in = i < rounds && row < end;
+    const uint32_t tok = udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
+    iv[i] = (int)bld4(r_idx, in ? (uint32_t)row * 4u : kOOB);
+    mv[i] = (int)bld4(r_map, in ? tok * 4u : kOOB);
   }
   if (a_addr == 0 || b_addr == 0) return;
 
@@ -636,7 +646,12 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
   }
   lds_barrier();
   const int n = __builtin_amdgcn_readfirstlane(s_cnt);
-  for (int c = 0; c < n; c += 16 * MB)
+  // The first row block runs outside the loop (a loop header would make its
+  // loads wait for the weight-line requests above).
+  if (n > 0)
+    fold_rows<NB, MB, FULL_R>(bf, p.K, p.N, p.R, scale, s_rows, 0, s_toks, min(16 * MB, n),
+                              n_lo, n_hi, s_part);
+  for (int c = 16 * MB; c < n; c += 16 * MB)
     fold_rows<NB, MB, FULL_R>(bf, p.K, p.N, p.R, scale, s_rows + c, 0, s_toks + c,
                               min(16 * MB, n - c), n_lo, n_hi, s_part);
   consume(keep_a);
@@ -681,16 +696,15 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p)
   const int rounds = (end - start + kThreads - 1) / kThreads;
   int iv[kPer], mv[kPer];
 #pragma unroll
+  // Loads for every round, those past the slice at an out-of-range offset:
+  // straight-line code keeps the wait before the scan exact, so it does not
+  // also wait for the weight loads issued after these.
   for (int i = 0; i < kPer; ++i) {
-    iv[i] = -1;
-    mv[i] = -1;
-    if (i < rounds) {
-      const int row = start + i * kThreads + (int)threadIdx.x;
-      const bool in = row < end;
-      const uint32_t tok = udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
-      iv[i] = (int)bld4(r_idx, in ? (uint32_t)row * 4u : kOOB);
-      mv[i] = (int)bld4(r_map, in ? tok * 4u : kOOB);
-    }
+    const int row = start + i * kThreads + (int)threadIdx.x;
+    const bool in = i < rounds && row < end;
+    const uint32_t tok = udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
+    iv[i] = (int)bld4(r_idx, in ? (uint32_t)row * 4u : kOOB);
+    mv[i] = (int)bld4(r_map, in ? tok * 4u : kOOB);
   }
   if (a_addr == 0 || b_addr == 0) return;
 
@@ -741,7 +755,11 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p)
   lds_barrier();
   const int n = __builtin_amdgcn_readfirstlane(s_cnt);
 
-  for (int c = 0; c < n; c += 16) {
+  // One 16-row chunk: its x and base_out loads, shrink, k-split reduction,
+  // expand and store. The first chunk runs outside the loop: a loop header
+  // merges the load counts of the paths that reach it and would make the
+  // chunk's loads wait for the weight loads still in flight.
+  auto chunk = [&](int c) {
     const int m = c + li;
     int t = -1, r = 0;
     if (m < n) {
@@ -820,7 +838,9 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p)
       }
     }
     lds_barrier();  // s_part is rewritten by the next chunk
-  }
+  };
+  if (n > 0) chunk(0);
+  for (int c = 16; c < n; c += 16) chunk(c);
 }
 
 // ---------------------------------------------------------------------------
@@ -992,16 +1012,79 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// Shrink batch of one pass over up to two experts: the A fragments of both and
+// the x fragments of the rows, for US k steps. A row's sum runs over the same
+// k steps in the same order whichever expert it belongs to.
+template <int NB, int MB, int US>
+struct ShrinkBatch2 {
+  u32x4 a0[US][NB];
+  u32x4 a1[US][NB];
+  u32x4 x[US][MB];
+};
+
+template <int NB, int MB, int US>
+__device__ __forceinline__ void load_shrink2(ShrinkBatch2<NB, MB, US>& sb, rsrc_t rx, rsrc_t ra0,
+                                             rsrc_t ra1, bool two, int K, int R,
+                                             const Rows<MB>& rw, int s0, int nks, int li, int g) {
+#pragma unroll
+  for (int u = 0; u < US; ++u) {
+    const int s = s0 + u * kWaves;
+    const int k0 = s * 32 + g * 8;
+    const bool kin = s < nks && k0 < K;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
+      const uint32_t off = (kin && rank < R) ? (uint32_t)(rank * K + k0) * 2u : kOOB;
+      sb.a0[u][b] = bld16(ra0, off);
+      sb.a1[u][b] = bld16(ra1, two ? off : kOOB);
+    }
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+      sb.x[u][rb] = bld16(rx, (kin && rw.valid[rb]) ? rw.xoff[rb] + 2u * k0 : kOOB);
+  }
+}
+
+template <int NB, int MB, int US>
+__device__ __forceinline__ void mma_shrink2(f32x4 (&h0)[MB][NB], f32x4 (&h1)[MB][NB],
+                                            const ShrinkBatch2<NB, MB, US>& sb, int nrb,
+                                            bool two) {
+#pragma unroll
+  for (int u = 0; u < US; ++u) {
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      if (rb < nrb) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          h0[rb][b] = mfma16x16x32(as_bf(sb.a0[u][b]), as_bf(sb.x[u][rb]), h0[rb][b]);
+        if (two) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            h1[rb][b] = mfma16x16x32(as_bf(sb.a1[u][b]), as_bf(sb.x[u][rb]), h1[rb][b]);
+        }
+      }
+    }
+  }
+}
+
+// Batch size of the shrink kernel's passes: about 72 VGPRs per batch buffer.
+template <int NB, int MB>
+struct ShrinkUS {
+  static constexpr int US = cclamp(72 / (4 * (2 * NB + MB)), 1, 8);
+};
+
 // Shrink: one workgroup per 16*MB rows of the window. The routing of its rows
 // (sorted_ids, the expert spans and the table cells of every expert) is
 // requested in one round; the rows' map entries, x rows and A_e fragments in
-// the next. Each expert span meeting the rows goes through the K-split shrink
-// and reduction of the one-kernel form, so H' comes out bit for bit the same.
+// the next. The expert spans meeting the rows are taken two per pass, x
+// fragments shared. The k-split and the reduction are those of the one-kernel
+// form, so H' comes out bit for bit the same.
 template <int NB, int MB>
 __global__ __launch_bounds__(kThreads) void grouped_shrink_kernel(GroupedArgs p) {
   constexpr int kRows = 16 * MB;
+  constexpr int US = ShrinkUS<NB, MB>::US;
   constexpr uint32_t kRowBytes = 64u * NB;  // 4 * RP
-  __shared__ float s_part[kWaves * MB * 64 * 4 * NB];
+  constexpr int kPart = kWaves * MB * 64 * 4 * NB;
+  __shared__ float s_part[2 * kPart];
   __shared__ int s_tok[kRows];
   __shared__ int s_live[kRows];
   __shared__ int s_seg_lo[kRows], s_seg_hi[kRows];
@@ -1051,9 +1134,17 @@ __global__ __launch_bounds__(kThreads) void grouped_shrink_kernel(GroupedArgs p)
   if (tid < kRows) s_tok[tid] = tok;
   lds_barrier();
   const int nseg = min(__builtin_amdgcn_readfirstlane(s_nseg), kRows);
+  if (nseg == 0) {
+    // nothing folds here: mark the rows so
+    if (tid < kRows && r0 + tid < r1) {
+      const rsrc_t r_meta = make_buf(p.ws_meta, p.ws_meta_bytes);
+      bst8(r_meta, (uint32_t)(r0 - p.row_offset + tid) * 8u, u32x2{0u, 0u});
+    }
+    return;
+  }
 
   // round 2: the map entry of this thread's row; consumed after the shrink
-  // loads of the first span are in flight
+  // loads of the first pass are in flight
   int map = -1;
   if (tok >= 0) map = p.row_adapter[tok];
 
@@ -1061,45 +1152,113 @@ __global__ __launch_bounds__(kThreads) void grouped_shrink_kernel(GroupedArgs p)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
   const int tile_row = (int)(r0 - p.row_offset);
+  const int nrb = (int)((r1 - r0 + 15) >> 4);
   const rsrc_t r_h = make_buf(p.ws_h, p.ws_h_bytes);
-  Bufs bf;
-  bf.x = make_buf(p.x, p.x_bytes);
+  const rsrc_t r_x = make_buf(p.x, p.x_bytes);
+  Rows<MB> rw;
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    const int t = s_tok[rb * 16 + li];
+    rw.valid[rb] = t >= 0;
+    rw.xoff[rb] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)p.K * 2u;
+    rw.ooff[rb] = 0;
+  }
+  const int nks = (p.K + 31) >> 5;
+  constexpr int kStep = kWaves * US;
+  constexpr int HW = 4 * NB;
   uint64_t my_meta = 0;  // thread t < kRows: meta of row t
-  for (int sg = 0; sg < nseg; ++sg) {
-    const uint64_t a_addr = uniform_u64(s_seg_a[sg]), b_addr = uniform_u64(s_seg_b[sg]);
-    const float scale = uniform_f32(s_seg_s[sg]);
-    bf.a = make_buf(reinterpret_cast<const void*>(a_addr), (uint32_t)(p.R * p.K) * 2u);
-    const int lo = __builtin_amdgcn_readfirstlane(s_seg_lo[sg]);
-    const int hi = __builtin_amdgcn_readfirstlane(s_seg_hi[sg]);
-    const int nrows = hi - lo, nrb = (nrows + 15) >> 4;
-    Rows<MB> rw;
+  for (int sg = 0; sg < nseg; sg += 2) {
+    const bool two = sg + 1 < nseg;
+    const uint64_t a0 = uniform_u64(s_seg_a[sg]);
+    const uint64_t a1 = two ? uniform_u64(s_seg_a[sg + 1]) : a0;
+    const rsrc_t ra0 = make_buf(reinterpret_cast<const void*>(a0), (uint32_t)(p.R * p.K) * 2u);
+    const rsrc_t ra1 = make_buf(reinterpret_cast<const void*>(a1), (uint32_t)(p.R * p.K) * 2u);
+    f32x4 h0[MB][NB], h1[MB][NB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        h0[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        h1[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    {
+      ShrinkBatch2<NB, MB, US> b0, b1;
+      int s0 = wave;
+      load_shrink2<NB, MB, US>(b0, r_x, ra0, ra1, two, p.K, p.R, rw, s0, nks, li, g);
+      while (s0 < nks) {
+        const int s1 = s0 + kStep;
+        load_shrink2<NB, MB, US>(b1, r_x, ra0, ra1, two, p.K, p.R, rw, s1, nks, li, g);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_shrink2<NB, MB, US>(h0, h1, b0, nrb, two);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s1 >= nks) break;
+        const int s2 = s1 + kStep;
+        load_shrink2<NB, MB, US>(b0, r_x, ra0, ra1, two, p.K, p.R, rw, s2, nks, li, g);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_shrink2<NB, MB, US>(h0, h1, b1, nrb, two);
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = s2;
+      }
+    }
+    if (sg == 0 && tid < kRows) s_live[tid] = (tok >= 0 && map >= 0) ? 1 : 0;
+    // k-split partial sums of both experts through LDS, then hi / lo
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
-      const int m = rb * 16 + li;
-      const int t = m < nrows ? s_tok[lo + m] : -1;
-      rw.valid[rb] = t >= 0;
-      rw.xoff[rb] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)p.K * 2u;
-      rw.ooff[rb] = 0;
+      if (rb < nrb) {
+        float* d0 = s_part + ((size_t)(wave * MB + rb) * 64 + lane) * HW;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          *reinterpret_cast<f32x4*>(d0 + 4 * b) = h0[rb][b];
+          if (two) *reinterpret_cast<f32x4*>(d0 + kPart + 4 * b) = h1[rb][b];
+        }
+      }
     }
-    f32x4 hacc[MB][NB];
-    shrink_k<NB, MB>(hacc, bf, p.K, p.R, rw, nrb, wave, li, g);
-    if (sg == 0 && tid < kRows) s_live[tid] = (tok >= 0 && map >= 0) ? 1 : 0;
-    HOp<NB> hop[MB];
-    reduce_split<NB, MB>(hacc, s_part, scale, nrb, wave, lane, hop);
-    // row block rb is written by wave rb % kWaves, live rows only
+    lds_barrier();
+    const int lo0 = __builtin_amdgcn_readfirstlane(s_seg_lo[sg]);
+    const int hi0 = __builtin_amdgcn_readfirstlane(s_seg_hi[sg]);
+    const int lo1 = two ? __builtin_amdgcn_readfirstlane(s_seg_lo[sg + 1]) : 0;
+    const int hi1 = two ? __builtin_amdgcn_readfirstlane(s_seg_hi[sg + 1]) : 0;
+    const float sc0 = uniform_f32(s_seg_s[sg]);
+    const float sc1 = two ? uniform_f32(s_seg_s[sg + 1]) : 0.f;
+    // row block rb is reduced and written by wave rb % kWaves, live rows only
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
       if (rb % kWaves == wave && rb < nrb) {
         const int m = rb * 16 + li;
-        const bool ok = m < nrows && s_live[lo + m] != 0;
-        const uint32_t off =
-            (uint32_t)(tile_row + lo + m) * kRowBytes + (uint32_t)g * 8u * NB;
-        store_half<NB>(r_h, ok, off, hop[rb].hi);
-        store_half<NB>(r_h, ok, off + 32u * NB, hop[rb].lo);
+        const bool in1 = two && m >= lo1 && m < hi1;
+        const bool in0 = m >= lo0 && m < hi0;
+        const bool ok = (in0 || in1) && s_live[m] != 0;
+        const float* src = s_part + (in1 ? kPart : 0);
+        const float scale = in1 ? sc1 : sc0;
+        HOp<NB> hop;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          f32x4 h = *reinterpret_cast<const f32x4*>(src + ((size_t)rb * 64 + lane) * HW + 4 * q);
+#pragma unroll
+          for (int w = 1; w < kWaves; ++w)
+            h += *reinterpret_cast<const f32x4*>(
+                src + ((size_t)(w * MB + rb) * 64 + lane) * HW + 4 * q);
+          const f32x4 v = scale * h;
+          const uint32_t hi01 = pack_bf16(v.x, v.y), hi23 = pack_bf16(v.z, v.w);
+          const uint32_t lo01 = pack_bf16(v.x - lo_f(hi01), v.y - hi_f(hi01));
+          const uint32_t lo23 = pack_bf16(v.z - lo_f(hi23), v.w - hi_f(hi23));
+          constexpr int CR = Chunk<NB>::kRanks;
+          const int cq = (4 * q) / CR, w0 = ((4 * q) % CR) / 2;
+          hop.hi[cq][w0] = hi01;
+          hop.hi[cq][w0 + 1] = hi23;
+          hop.lo[cq][w0] = lo01;
+          hop.lo[cq][w0 + 1] = lo23;
+        }
+        const uint32_t off = (uint32_t)(tile_row + m) * kRowBytes + (uint32_t)g * 8u * NB;
+        store_half<NB>(r_h, ok, off, hop.hi);
+        store_half<NB>(r_h, ok, off + 32u * NB, hop.lo);
       }
     }
-    if (tid >= lo && tid < hi && tok >= 0 && map >= 0) my_meta = b_addr;
-    lds_barrier();  // s_part is rewritten by the next span
+    if (tid < kRows && tok >= 0 && map >= 0) {
+      if (tid >= lo0 && tid < hi0) my_meta = uniform_u64(s_seg_b[sg]);
+      if (two && tid >= lo1 && tid < hi1) my_meta = uniform_u64(s_seg_b[sg + 1]);
+    }
+    lds_barrier();  // s_part is rewritten by the next pass
   }
   if (tid < kRows && r0 + tid < r1) {
     const rsrc_t r_meta = make_buf(p.ws_meta, p.ws_meta_bytes);
@@ -1134,8 +1293,31 @@ __global__ __launch_bounds__(64) void grouped_expand_kernel(GroupedArgs p) {
   const int r0 = (u / p.ns_count) * kRows;  // window-relative
   const int lane = threadIdx.x, li = lane & 15, g = lane >> 4;
 
-  // rows past the window lie past the meta buffer and read as 0
+  const int n_lo = ns * kCols;
+  const int n_hi = min(n_lo + kCols, p.N);
+  const rsrc_t r_out = make_buf(p.out, p.out_bytes);
+  const rsrc_t r_h = make_buf(p.ws_h, p.ws_h_bytes);
   const rsrc_t r_meta = make_buf(p.ws_meta, p.ws_meta_bytes);
+
+  // Everything addressed by row alone is requested before the rows' meta is
+  // known: base_out (row-contiguous), H' (one lane per row) and the meta.
+  // Rows past the window lie past all three buffers and read as 0.
+  const int cr = lane / LPR, cc = lane % LPR;
+  u32x4 bv[NI];
+  uint32_t boff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int col = n_lo + 8 * cc;
+    boff[i] = (uint32_t)(r0 + i * RPI + cr) * (uint32_t)p.N * 2u + 2u * col;
+    bv[i] = bld16_nt(r_out, col < n_hi ? boff[i] : kOOB);
+  }
+  HOp<NB> hop[MB];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    const uint32_t hoff = (uint32_t)(r0 + rb * 16 + li) * kRowBytes + (uint32_t)g * 8u * NB;
+    load_half<NB>(r_h, true, hoff, hop[rb].hi);
+    load_half<NB>(r_h, true, hoff + 32u * NB, hop[rb].lo);
+  }
   const u32x2 mv = bld8(r_meta, lane < kRows ? (uint32_t)(r0 + lane) * 8u : kOOB);
   const bool is_live = (mv.x | mv.y) != 0;
   const uint64_t live = __ballot(is_live);
@@ -1145,35 +1327,6 @@ __global__ __launch_bounds__(64) void grouped_expand_kernel(GroupedArgs p) {
   const int prev = below ? 63 - __clzll((long long)below) : lane;
   const uint32_t plo = (uint32_t)__shfl((int)mv.x, prev), phi = (uint32_t)__shfl((int)mv.y, prev);
   uint64_t starts = __ballot(is_live && (below == 0 || plo != mv.x || phi != mv.y));
-
-  const int n_lo = ns * kCols;
-  const int n_hi = min(n_lo + kCols, p.N);
-  const rsrc_t r_out = make_buf(p.out, p.out_bytes);
-  const rsrc_t r_h = make_buf(p.ws_h, p.ws_h_bytes);
-
-  // base_out, row-contiguous
-  const int cr = lane / LPR, cc = lane % LPR;
-  u32x4 bv[NI];
-  uint32_t boff[NI];
-  bool bok[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int row = i * RPI + cr;
-    const int col = n_lo + 8 * cc;
-    bok[i] = ((live >> row) & 1ull) != 0 && col < n_hi;
-    boff[i] = (uint32_t)(r0 + row) * (uint32_t)p.N * 2u + 2u * col;
-    bv[i] = bld16_nt(r_out, bok[i] ? boff[i] : kOOB);
-  }
-  // H' operands, one lane per row
-  HOp<NB> hop[MB];
-#pragma unroll
-  for (int rb = 0; rb < MB; ++rb) {
-    const int row = rb * 16 + li;
-    const bool lv = ((live >> row) & 1ull) != 0;
-    const uint32_t hoff = (uint32_t)(r0 + row) * kRowBytes + (uint32_t)g * 8u * NB;
-    load_half<NB>(r_h, lv, hoff, hop[rb].hi);
-    load_half<NB>(r_h, lv, hoff + 32u * NB, hop[rb].lo);
-  }
 
   while (starts) {
     const int s = __ffsll((unsigned long long)starts) - 1;
@@ -1222,7 +1375,8 @@ __global__ __launch_bounds__(64) void grouped_expand_kernel(GroupedArgs p) {
     const uint32_t o1 = pack_bf16(lo_f(bq.y) + d0.z, hi_f(bq.y) + d0.w);
     const uint32_t o2 = pack_bf16(lo_f(bq.z) + d1.x, hi_f(bq.z) + d1.y);
     const uint32_t o3 = pack_bf16(lo_f(bq.w) + d1.z, hi_f(bq.w) + d1.w);
-    bst16_nt(r_out, bok[i] ? boff[i] : kOOB, u32x4{o0, o1, o2, o3});
+    const bool ok = ((live >> (i * RPI + cr)) & 1ull) != 0 && n_lo + 8 * cc < n_hi;
+    bst16_nt(r_out, ok ? boff[i] : kOOB, u32x4{o0, o1, o2, o3});
   }
 }
 
@@ -1722,7 +1876,7 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
     a.ws_h_bytes = (uint32_t)w.h_bytes;
     a.ws_meta_bytes = (uint32_t)w.meta_bytes;
     // shrink: one workgroup per 16 * smb rows
-    int smb = env_int("MLORA_SHRINK_MB", 1);
+    int smb = env_int("MLORA_SHRINK_MB", kernel_nb(R) <= 2 ? 2 : 1);
     smb = smb >= 2 ? 2 : 1;
     const int64_t sunits = (rows + 16 * smb - 1) / (16 * smb);
     // expand: one wave per (16 * emb rows, cw column steps)
