@@ -129,9 +129,9 @@ class Staged:
         from tests.device import DeviceCase
         self.case = case
         self.primary = DeviceCase(case, device, two_kernel=two_kernel)
-        if case.path == "grouped" and two_kernel:
+        if two_kernel:
             # one workspace, allocated before any capture, shared by every copy
-            self.primary.workspace_for(self.primary.windows)
+            self.primary.workspace_for(getattr(self.primary, "windows", None))
         self.copies = [self.primary]
         for _ in range(copies - 1):
             self.copies.append(self.primary_clone(device))
@@ -302,7 +302,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--one-kernel", action="store_true",
-                    help="grouped: run the one-kernel form (no workspace)")
+                    help="run the folds without a workspace (one-kernel forms)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of graph replays")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -448,7 +448,7 @@ def main():
             "rows_per_step": rows,
             "folded_rows_per_step": folded,
             "launches_per_step": launches,
-            "kernels_per_launch": (1 if case.path == "gather" or args.one_kernel else 2),
+            "workspace": not args.one_kernel,
             "rotating_copies": copies,
             "timing": ("eager launches" if args.eager else
                        "HIP graph of one step per copy, replayed"),

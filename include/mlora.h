@@ -168,12 +168,32 @@ const char* mlora_last_error(void);
  *   row_adapter [n_tokens]         int32 per-token map, read on device
  * n_tokens must be >= ceil(n_slots / top_k). x and base_out must be 16-byte
  * aligned. n_slots == 0 or n_experts == 0 enqueues nothing.
- * Returns MLORA_OK, MLORA_ERR_INVALID (arguments; nothing enqueued) or
- * MLORA_ERR_HIP (launch rejected).
+ *
+ * Workspace (device, caller-owned, optional): with workspace == NULL and
+ * workspace_bytes == 0 the fold runs as one kernel. With a workspace of at
+ * least mlora_gather_bgmv_workspace_bytes(n_slots, k_in, max_rank) bytes,
+ * 256-byte aligned, calls whose k_in spans more than 16 k steps of 32 and
+ * whose experts hold at most 64 rows on average run as two kernels (a shrink
+ * split over k ranges into the workspace, then the expand), which spreads each
+ * expert's A_e over more workgroups; other calls stay on one kernel. The two forms may differ in the
+ * last bits (the k sums are grouped differently); both meet the same bound.
+ * The contents need no initialisation and are dead once the call's kernels
+ * finish; calls that share one workspace must be ordered (one stream). An f32
+ * route ignores it.
+ * Returns MLORA_OK, MLORA_ERR_INVALID (arguments; nothing enqueued, including
+ * a misaligned or NULL-with-size workspace), MLORA_ERR_CAPACITY (workspace too
+ * small; nothing enqueued) or MLORA_ERR_HIP (launch rejected).
  */
 int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void* x, int64_t n_tokens,
                           void* base_out, const int32_t* indices, const int32_t* row_adapter,
-                          int64_t n_slots, int32_t top_k, void* stream);
+                          int64_t n_slots, int32_t top_k, void* workspace,
+                          uint64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mlora_gather_bgmv may use: KC * n_slots * 64 * NB, KC =
+ * clamp(ceil(ceil(k_in / 32) / 16), 1, 4) k ranges, NB = ceil(max_rank / 16)
+ * rounded up to 1, 2, 4 or 8, rounded up to 256. 0 for n_slots <= 0 or invalid
+ * k_in / max_rank. */
+uint64_t mlora_gather_bgmv_workspace_bytes(int64_t n_slots, int32_t k_in, int32_t max_rank);
 
 /*
  * [P2 moe_lora_grouped_down] Prefill fold over expert-sorted rows in the

@@ -46,6 +46,7 @@ EXPORTS = (
     "mlora_gather_bgmv",
     "mlora_grouped_down",
     "mlora_grouped_down_workspace_bytes",
+    "mlora_gather_bgmv_workspace_bytes",
 )
 
 
@@ -109,7 +110,8 @@ def load() -> ctypes.CDLL:
         "mlora_m_tile": (i32, []),
         "mlora_last_error": (ctypes.c_char_p, []),
         "mlora_gather_bgmv": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, vp, vp, i64,
-                                    i32, vp]),
+                                    i32, vp, ctypes.c_uint64, vp]),
+        "mlora_gather_bgmv_workspace_bytes": (ctypes.c_uint64, [i64, i32, i32]),
         "mlora_grouped_down": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64, vp, i32,
                                      vp, vp, i32, i64, i64, vp, ctypes.c_uint64, vp]),
         "mlora_grouped_down_workspace_bytes": (ctypes.c_uint64, [i64, i64, i32]),
@@ -290,9 +292,17 @@ def _dev(t, name, dtype=None):
     return t.data_ptr()
 
 
+def mlora_gather_bgmv_workspace_bytes(n_slots: int, k_in: int, max_rank: int) -> int:
+    """Workspace bytes the two-kernel gather fold may use."""
+    return int(load().mlora_gather_bgmv_workspace_bytes(int(n_slots), int(k_in), int(max_rank)))
+
+
 def mlora_gather_bgmv(route: ExpertRoute, x, base_out, indices, row_adapter, top_k: int,
-                      stream=None) -> None:
-    """Gather fold of every flat row of ``base_out`` [n_slots, n_out], in place."""
+                      workspace=None, stream=None) -> None:
+    """Gather fold of every flat row of ``base_out`` [n_slots, n_out], in place.
+
+    ``workspace``: None (one kernel) or a contiguous device tensor of at least
+    ``mlora_gather_bgmv_workspace_bytes`` bytes (two kernels where that pays)."""
     import torch
     if _dtype_code(x) != route.dtype or _dtype_code(base_out) != route.dtype:
         raise TypeError("x / base_out dtype differs from the route's")
@@ -305,10 +315,14 @@ def mlora_gather_bgmv(route: ExpertRoute, x, base_out, indices, row_adapter, top
         raise ValueError("indices must have one entry per base_out row")
     if row_adapter.numel() < x.shape[0]:
         raise ValueError("row_adapter must cover every x row")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
     rc = load().mlora_gather_bgmv(
         ctypes.byref(route), _dev(x, "x"), x.shape[0], _dev(base_out, "base_out"),
         _dev(indices, "indices", torch.int32), _dev(row_adapter, "row_adapter", torch.int32),
-        n_slots, int(top_k), _stream_handle(stream))
+        n_slots, int(top_k), ws_ptr, ws_bytes, _stream_handle(stream))
     if rc != MLORA_OK:
         raise _err(rc)
 

@@ -390,18 +390,20 @@ __device__ __forceinline__ void mma_store_expand(const ExpandBatch<NB, MB, UE>& 
   }
 }
 
-// Shrink of up to MB row blocks over this wave's k steps: H[rank][row] for
-// the k steps wave, wave + kWaves, ... (in increasing order).
+// Shrink of up to MB row blocks over this wave's k steps in [s_begin, s_end):
+// H[rank][row] for the k steps s_begin + wave, s_begin + wave + kWaves, ...
+// (in increasing order).
 template <int NB, int MB>
 __device__ __forceinline__ void shrink_k(f32x4 (&hacc)[MB][NB], const Bufs& bf, int K, int R,
-                                         const Rows<MB>& rw, int nrb, int wave, int li, int g) {
+                                         const Rows<MB>& rw, int nrb, int wave, int li, int g,
+                                         int s_begin = 0, int s_end = 1 << 30) {
   constexpr int US = Batch<NB, MB>::US;
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
     for (int b = 0; b < NB; ++b) hacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nks = (K + 31) >> 5;
+  const int nks = min((K + 31) >> 5, s_end);
   constexpr int kStep = kWaves * US;
   // The next batch is requested before the current one is used, without a
   // condition: steps past the end load nothing (their offsets are out of
@@ -410,7 +412,7 @@ __device__ __forceinline__ void shrink_k(f32x4 (&hacc)[MB][NB], const Bufs& bf, 
   // batch before it (the scheduler would otherwise sink them below, and the
   // loop would wait for every load at its head).
   ShrinkBatch<NB, MB, US> s0b, s1b;
-  int s0 = wave;
+  int s0 = s_begin + wave;
   load_shrink<NB, MB, US>(s0b, bf, K, R, rw, s0, nks, li, g);
   while (s0 < nks) {
     const int s1 = s0 + kStep;
@@ -479,16 +481,12 @@ __device__ __forceinline__ void reduce_split(const f32x4 (&hacc)[MB][NB], float*
 // (s_row ? s_row[m] : row_base + m) of bf.out, from token s_tok[m]
 // (negative: a dead row, neither read nor written).
 // All threads of the workgroup must call it with the same arguments.
-template <int NB, int MB, bool FULL_R>
-__device__ void fold_rows(const Bufs& bf, int K, int N, int R, float scale, const int* s_row,
-                          int row_base, const int* s_tok, int nrows, int n_lo, int n_hi,
-                          float* s_part) {
-  constexpr int UE = Batch<NB, MB>::UE;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 15, g = lane >> 4;
-  const int nrb = (nrows + 15) >> 4;
-
+// Lane state of row blocks 0..MB-1 of a row list: rows 0..nrows-1, row m of
+// base_out row (s_row ? s_row[m] : row_base + m), token s_tok[m] (negative:
+// a dead row, neither read nor written).
+template <int MB>
+__device__ __forceinline__ Rows<MB> rows_of(int K, int N, const int* s_row, int row_base,
+                                            const int* s_tok, int nrows, int li) {
   Rows<MB> rw;
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb) {
@@ -502,37 +500,59 @@ __device__ void fold_rows(const Bufs& bf, int K, int N, int R, float scale, cons
     rw.xoff[rb] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)K * 2u;
     rw.ooff[rb] = (uint32_t)r * (uint32_t)N * 2u;
   }
+  return rw;
+}
+
+// Expand + read-modify-write of this wave's column steps, two batches in
+// flight; e0 already holds the wave's first batch.
+template <int NB, int MB, bool FULL_R>
+__device__ __forceinline__ void expand_rows(const Bufs& bf, int R, const Rows<MB>& rw,
+                                            const HOp<NB> (&hop)[MB], int nrb, int n_lo,
+                                            int n_hi, int wave, int li, int g,
+                                            ExpandBatch<NB, MB, Batch<NB, MB>::UE>& e0) {
+  constexpr int UE = Batch<NB, MB>::UE;
+  constexpr int kStep = kWaves * UE;
+  const int ncs = (n_hi - n_lo + kColStep - 1) / kColStep;
+  ExpandBatch<NB, MB, UE> e1;
+  int c0 = wave;
+  while (c0 < ncs) {
+    const int c1 = c0 + kStep;
+    load_expand<NB, MB, UE, FULL_R>(e1, bf, R, rw, c1, ncs, n_lo, n_hi, li, g);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_store_expand<NB, MB, UE>(e0, hop, bf, rw, nrb, c0, ncs, n_lo, n_hi, g);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c1 >= ncs) break;
+    const int c2 = c1 + kStep;
+    load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, c2, ncs, n_lo, n_hi, li, g);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_store_expand<NB, MB, UE>(e1, hop, bf, rw, nrb, c1, ncs, n_lo, n_hi, g);
+    __builtin_amdgcn_sched_barrier(0);
+    c0 = c2;
+  }
+}
+
+template <int NB, int MB, bool FULL_R>
+__device__ void fold_rows(const Bufs& bf, int K, int N, int R, float scale, const int* s_row,
+                          int row_base, const int* s_tok, int nrows, int n_lo, int n_hi,
+                          float* s_part) {
+  constexpr int UE = Batch<NB, MB>::UE;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int nrb = (nrows + 15) >> 4;
+  const Rows<MB> rw = rows_of<MB>(K, N, s_row, row_base, s_tok, nrows, li);
 
   // The first expand batch does not depend on the shrink: request it now so
   // its latency hides behind the shrink.
   const int ncs = (n_hi - n_lo + kColStep - 1) / kColStep;
-  ExpandBatch<NB, MB, UE> e0, e1;
+  ExpandBatch<NB, MB, UE> e0;
   load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, wave, ncs, n_lo, n_hi, li, g);
 
   f32x4 hacc[MB][NB];
   shrink_k<NB, MB>(hacc, bf, K, R, rw, nrb, wave, li, g);
   HOp<NB> hop[MB];
   reduce_split<NB, MB>(hacc, s_part, scale, nrb, wave, lane, hop);
-
-  // ---- expand + read-modify-write, two batches in flight -------------------
-  {
-    constexpr int kStep = kWaves * UE;
-    int c0 = wave;
-    while (c0 < ncs) {
-      const int c1 = c0 + kStep;
-      load_expand<NB, MB, UE, FULL_R>(e1, bf, R, rw, c1, ncs, n_lo, n_hi, li, g);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_store_expand<NB, MB, UE>(e0, hop, bf, rw, nrb, c0, ncs, n_lo, n_hi, g);
-      __builtin_amdgcn_sched_barrier(0);
-      if (c1 >= ncs) break;
-      const int c2 = c1 + kStep;
-      load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, c2, ncs, n_lo, n_hi, li, g);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_store_expand<NB, MB, UE>(e1, hop, bf, rw, nrb, c1, ncs, n_lo, n_hi, g);
-      __builtin_amdgcn_sched_barrier(0);
-      c0 = c2;
-    }
-  }
+  expand_rows<NB, MB, FULL_R>(bf, R, rw, hop, nrb, n_lo, n_hi, wave, li, g, e0);
   // s_part and the caller's row lists are reused by the next call.
   lds_barrier();
 }
@@ -578,8 +598,13 @@ struct GatherArgs {
   int32_t ns_count;      // column slices per expert
   int32_t scan_len;      // rows per row slice (<= kScanMax)
   int32_t ns_cols;       // columns per column slice (multiple of kColStep)
-  int32_t units;         // n_experts * rs_count * ns_count
+  int32_t units;         // n_experts * rs_count * ns_count (kc_count for the shrink)
   int32_t per_xcd;       // ceil(units / kXcds)
+  // two-kernel form only
+  float* ws;             // partial H: kc_count x n_slots x RP fp32
+  uint32_t ws_bytes;
+  int32_t kc_count;      // k ranges of the shrink
+  int32_t kc_steps;      // 32-wide k steps per range
 };
 
 template <int NB, int MB, bool FULL_R>
@@ -658,6 +683,313 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
   consume(keep_b);
 }
 
+
+// ---------------------------------------------------------------------------
+// gather, two-kernel form: k-split shrink into a workspace, then expand
+// ---------------------------------------------------------------------------
+
+// Workspace: kc_count planes of n_slots rows x RP fp32 (RP = 16 * NB), the
+// partial H of each folded row over one k range, unscaled, each row in the
+// lane order of the shrink (lane group g holds ranks g*4NB .. g*4NB+4NB-1).
+// A plane's rows of other experts, or of rows that fold nothing, are not
+// written and not read.
+
+// The routing of flat rows [start, end): indices and map entries, requested
+// for every round (rounds past the slice at an out-of-range offset), so the
+// wait before the scan is exact even with other loads issued after these.
+struct ScanLoads {
+  static constexpr int kPer = kScanMax / kThreads;
+  int iv[kPer], mv[kPer];
+  int rounds;
+};
+
+__device__ __forceinline__ void request_scan(const GatherArgs& p, int start, int end,
+                                             ScanLoads& sl) {
+  const rsrc_t r_idx = make_buf(p.indices, (uint32_t)p.n_slots * 4u);
+  const rsrc_t r_map = make_buf(p.row_adapter, (uint32_t)p.n_tokens * 4u);
+  sl.rounds = (end - start + kThreads - 1) / kThreads;
+#pragma unroll
+  for (int i = 0; i < ScanLoads::kPer; ++i) {
+    const int row = start + i * kThreads + (int)threadIdx.x;
+    const bool in = i < sl.rounds && row < end;
+    const uint32_t tok = udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
+    sl.iv[i] = (int)bld4(r_idx, in ? (uint32_t)row * 4u : kOOB);
+    sl.mv[i] = (int)bld4(r_map, in ? tok * 4u : kOOB);
+  }
+}
+
+// Appends the rows of expert e whose token is mapped to s_rows / s_toks and
+// returns their number (wave-uniform). Contains workgroup barriers.
+__device__ __forceinline__ int finish_scan(const GatherArgs& p, int e, int start, int end,
+                                           const ScanLoads& sl, int* s_rows, int* s_toks,
+                                           int* s_cnt) {
+  if (threadIdx.x == 0) *s_cnt = 0;
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < ScanLoads::kPer; ++i) {
+    if (i >= sl.rounds) break;
+    const int row = start + i * kThreads + (int)threadIdx.x;
+    const bool hit = row < end && sl.iv[i] == e && sl.mv[i] >= 0;
+    const int tok = (int)udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
+    wave_append(hit, row, tok, s_cnt, s_rows, s_toks, kScanMax);
+  }
+  lds_barrier();
+  return __builtin_amdgcn_readfirstlane(*s_cnt);
+}
+
+// k steps (and column steps) one wave of the two-kernel gather holds.
+constexpr int kTwoSteps = 4;
+
+// Shrink: one workgroup per (expert, row slice, k range of at most
+// kWaves * kTwoSteps k steps). The range's A_e fragments are requested with
+// the routing, before any row is known; after the scan only x is loaded. The
+// waves split the range's k steps; their sums meet in LDS in a fixed order.
+template <int NB, int MB>
+__global__ __launch_bounds__(kThreads) void gather_shrink_kernel(GatherArgs p) {
+  constexpr int HW = 4 * NB;
+  constexpr uint32_t kRowBytes = 64u * NB;  // RP fp32
+  __shared__ float s_part[kWaves * MB * 64 * HW];
+  __shared__ int s_rows[kScanMax];
+  __shared__ int s_toks[kScanMax];
+  __shared__ int s_cnt;
+
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * p.per_xcd + slot;
+  if (u >= p.units) return;
+  const int per_e = p.rs_count * p.kc_count;
+  const int e = u / per_e;
+  const int within = u - e * per_e;
+  const int rs = within / p.kc_count, kc = within - rs * p.kc_count;
+  const uint64_t a_addr = uniform_u64(p.a_table[e]), b_addr = uniform_u64(p.b_table[e]);
+  const int start = rs * p.scan_len;
+  const int end = min(start + p.scan_len, p.n_slots);
+  ScanLoads sl;
+  request_scan(p, start, end, sl);
+  if (a_addr == 0 || b_addr == 0) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int K = p.K;
+  const int s_end = min((K + 31) >> 5, (kc + 1) * p.kc_steps);
+  const rsrc_t r_x = make_buf(p.x, p.x_bytes);
+  const rsrc_t r_a = make_buf(reinterpret_cast<const void*>(a_addr), (uint32_t)(p.R * K) * 2u);
+  const rsrc_t r_ws = make_buf(p.ws, p.ws_bytes);
+  // this wave's k steps: kc * kc_steps + wave + kWaves * t
+  int step[kTwoSteps];
+  u32x4 av[kTwoSteps][NB];
+  auto request_a = [&]() {
+#pragma unroll
+    for (int t = 0; t < kTwoSteps; ++t) {
+      step[t] = kc * p.kc_steps + wave + t * kWaves;
+      const int k0 = step[t] * 32 + g * 8;
+      const bool kin = step[t] < s_end && k0 < K;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
+        av[t][b] = bld16(r_a, (kin && rank < p.R) ? (uint32_t)(rank * K + k0) * 2u : kOOB);
+      }
+    }
+  };
+  request_a();
+  const int n = finish_scan(p, e, start, end, sl, s_rows, s_toks, &s_cnt);
+  const uint32_t plane = (uint32_t)kc * (uint32_t)p.n_slots;
+
+  auto block = [&](int c) {
+    const int nrows = min(16 * MB, n - c), nrb = (nrows + 15) >> 4;
+    const Rows<MB> rw = rows_of<MB>(K, p.N, s_rows + c, 0, s_toks + c, nrows, li);
+    u32x4 xv[kTwoSteps][MB];
+#pragma unroll
+    for (int t = 0; t < kTwoSteps; ++t) {
+      const int k0 = step[t] * 32 + g * 8;
+      const bool kin = step[t] < s_end && k0 < K;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+        xv[t][rb] = bld16(r_x, (kin && rw.valid[rb]) ? rw.xoff[rb] + 2u * k0 : kOOB);
+    }
+    f32x4 hacc[MB][NB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) hacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kTwoSteps; ++t) {
+      if (step[t] < s_end) {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          if (rb < nrb) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+              hacc[rb][b] = mfma16x16x32(as_bf(av[t][b]), as_bf(xv[t][rb]), hacc[rb][b]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      if (rb < nrb) {
+        float* dst = s_part + ((size_t)(wave * MB + rb) * 64 + lane) * HW;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(dst + 4 * b) = hacc[rb][b];
+      }
+    }
+    lds_barrier();
+    // row block rb is reduced and stored by wave rb % kWaves
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      if (rb % kWaves == wave && rb < nrb) {
+        const int m = rb * 16 + li;
+        const bool ok = rw.valid[rb];
+        const uint32_t row = (uint32_t)(m < nrows ? s_rows[c + m] : 0);
+        const uint32_t off = (plane + row) * kRowBytes + (uint32_t)g * 4u * HW;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          f32x4 h = *reinterpret_cast<const f32x4*>(s_part + ((size_t)rb * 64 + lane) * HW + 4 * q);
+#pragma unroll
+          for (int w = 1; w < kWaves; ++w)
+            h += *reinterpret_cast<const f32x4*>(
+                s_part + ((size_t)(w * MB + rb) * 64 + lane) * HW + 4 * q);
+          bst16(r_ws, ok ? off + 16u * q : kOOB, __builtin_bit_cast(u32x4, h));
+        }
+      }
+    }
+    lds_barrier();  // s_part is rewritten by the next block
+  };
+  // the first block runs outside the loop (see the resident gather kernel)
+  if (n > 0) block(0);
+  for (int c = 16 * MB; c < n; c += 16 * MB) block(c);
+}
+
+// Expand: one workgroup per (expert, row slice, column slice of at most
+// kWaves * kTwoSteps column steps). The slice's B_e fragments are requested
+// with the routing; after the scan, the rows' partial H (summed over the k
+// ranges in order, scaled and split into hi / lo as in the one-kernel form)
+// and base_out fragments.
+constexpr int kMaxKc = 4;
+
+template <int NB, int MB, bool FULL_R>
+__global__ __launch_bounds__(kThreads) void gather_expand_kernel(GatherArgs p) {
+  constexpr uint32_t kRowBytes = 64u * NB;
+  constexpr int CC = Chunk<NB>::kCount;
+  __shared__ int s_rows[kScanMax];
+  __shared__ int s_toks[kScanMax];
+  __shared__ int s_cnt;
+
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * p.per_xcd + slot;
+  if (u >= p.units) return;
+  const int per_e = p.rs_count * p.ns_count;
+  const int e = u / per_e;
+  const int within = u - e * per_e;
+  const int rs = within / p.ns_count, ns = within - rs * p.ns_count;
+  const uint64_t a_addr = uniform_u64(p.a_table[e]), b_addr = uniform_u64(p.b_table[e]);
+  const float scale = uniform_f32(p.scale_table[e]);
+  const int start = rs * p.scan_len;
+  const int end = min(start + p.scan_len, p.n_slots);
+  ScanLoads sl;
+  request_scan(p, start, end, sl);
+  if (a_addr == 0 || b_addr == 0) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int n_lo = ns * p.ns_cols;
+  const int n_hi = min(n_lo + p.ns_cols, p.N);
+  const int ncs = (n_hi - n_lo + kColStep - 1) / kColStep;
+  const rsrc_t r_b = make_buf(reinterpret_cast<const void*>(b_addr), (uint32_t)(p.N * p.R) * 2u);
+  const rsrc_t r_out = make_buf(p.out, p.out_bytes);
+  const rsrc_t r_ws = make_buf(p.ws, p.ws_bytes);
+  BFrag<NB> bw[kTwoSteps];
+  auto request_b = [&]() {
+#pragma unroll
+    for (int t = 0; t < kTwoSteps; ++t) {
+      const int cs = wave + t * kWaves;
+      load_bfrag<NB, FULL_R>(bw[t], r_b, p.R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li, g);
+    }
+  };
+  request_b();
+  const int n = finish_scan(p, e, start, end, sl, s_rows, s_toks, &s_cnt);
+  const int kcs = p.kc_count;
+
+  auto block = [&](int c) {
+    const int nrows = min(16 * MB, n - c), nrb = (nrows + 15) >> 4;
+    const Rows<MB> rw = rows_of<MB>(p.K, p.N, s_rows + c, 0, s_toks + c, nrows, li);
+    // partial sums of every k range and the base_out fragments, requested together
+    u32x4 pv[kMaxKc][MB][NB];
+#pragma unroll
+    for (int k = 0; k < kMaxKc; ++k)
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) {
+        const int m = rb * 16 + li;
+        const uint32_t row = (uint32_t)(m < nrows ? s_rows[c + m] : 0);
+        const bool ok = k < kcs && rw.valid[rb];
+        const uint32_t off = ((uint32_t)k * (uint32_t)p.n_slots + row) * kRowBytes +
+                             (uint32_t)g * 16u * NB;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) pv[k][rb][q] = bld16(r_ws, ok ? off + 16u * q : kOOB);
+      }
+    u32x4 ov[kTwoSteps][MB];
+#pragma unroll
+    for (int t = 0; t < kTwoSteps; ++t) {
+      const int cs = wave + t * kWaves;
+      const int col = n_lo + cs * kColStep + 8 * g;
+      const bool cok = cs < ncs && col < n_hi;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+        ov[t][rb] = bld16(r_out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
+    }
+    HOp<NB> hop[MB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        f32x4 h = __builtin_bit_cast(f32x4, pv[0][rb][q]);
+#pragma unroll
+        for (int k = 1; k < kMaxKc; ++k)
+          if (k < kcs) h += __builtin_bit_cast(f32x4, pv[k][rb][q]);
+        const f32x4 v = scale * h;
+        const uint32_t hi01 = pack_bf16(v.x, v.y), hi23 = pack_bf16(v.z, v.w);
+        const uint32_t lo01 = pack_bf16(v.x - lo_f(hi01), v.y - hi_f(hi01));
+        const uint32_t lo23 = pack_bf16(v.z - lo_f(hi23), v.w - hi_f(hi23));
+        constexpr int CR = Chunk<NB>::kRanks;
+        const int cq = (4 * q) / CR, w0 = ((4 * q) % CR) / 2;
+        hop[rb].hi[cq][w0] = hi01;
+        hop[rb].hi[cq][w0 + 1] = hi23;
+        hop[rb].lo[cq][w0] = lo01;
+        hop[rb].lo[cq][w0 + 1] = lo23;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kTwoSteps; ++t) {
+      const int cs = wave + t * kWaves;
+      if (cs < ncs) {
+        const int col = n_lo + cs * kColStep + 8 * g;
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          if (rb < nrb) {
+            f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < CC; ++q) {
+              d0 = mfma_chunk(bw[t].w[0][q], hop[rb].hi[q], d0);
+              d1 = mfma_chunk(bw[t].w[1][q], hop[rb].hi[q], d1);
+              d0 = mfma_chunk(bw[t].w[0][q], hop[rb].lo[q], d0);
+              d1 = mfma_chunk(bw[t].w[1][q], hop[rb].lo[q], d1);
+            }
+            const u32x4 bq = ov[t][rb];
+            const uint32_t o0 = pack_bf16(lo_f(bq.x) + d0.x, hi_f(bq.x) + d0.y);
+            const uint32_t o1 = pack_bf16(lo_f(bq.y) + d0.z, hi_f(bq.y) + d0.w);
+            const uint32_t o2 = pack_bf16(lo_f(bq.z) + d1.x, hi_f(bq.z) + d1.y);
+            const uint32_t o3 = pack_bf16(lo_f(bq.w) + d1.z, hi_f(bq.w) + d1.w);
+            bst16(r_out, (rw.valid[rb] && col < n_hi) ? rw.ooff[rb] + 2u * col : kOOB,
+                  u32x4{o0, o1, o2, o3});
+          }
+        }
+      }
+    }
+  };
+  if (n > 0) block(0);
+  for (int c = 16 * MB; c < n; c += 16 * MB) block(c);
+}
 
 // ---------------------------------------------------------------------------
 // gather, decode fast path: resident weights
@@ -1510,6 +1842,65 @@ bool gather_resident_fits(const GatherArgs& a) {
   return nb <= 2 && nks <= kWaves * kResSteps && ncs <= kWaves * kResSteps;
 }
 
+// Rank blocks the kernels use for max_rank R: ceil(R / 16) rounded up to 1,
+// 2, 4 or 8.
+int kernel_nb(int R) {
+  const int nb = (R + 15) / 16;
+  return nb <= 1 ? 1 : (nb <= 2 ? 2 : (nb <= 4 ? 4 : 8));
+}
+
+// Two-kernel gather: k ranges of the shrink (about 16 k steps each, at most
+// kMaxKc), and the workspace they need.
+int gather_kc(int K) {
+  const int nks = (K + 31) / 32;
+  const int kc = (nks + kWaves * kTwoSteps - 1) / (kWaves * kTwoSteps);
+  return kc < 1 ? 1 : (kc > kMaxKc ? kMaxKc : kc);
+}
+
+int64_t gather_ws_bytes(int64_t n_slots, int K, int R) {
+  return ((int64_t)gather_kc(K) * n_slots * 64 * kernel_nb(R) + 255) & ~(int64_t)255;
+}
+
+// Row blocks per pass of the two-kernel gather for a slice of `rows` rows.
+int gather_two_mb(int R, int64_t rows) {
+  const int nb = kernel_nb(R);
+  const int cap = nb <= 2 ? 4 : (nb <= 4 ? 2 : 1);
+  const int want = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  return want < cap ? want : cap;
+}
+
+template <int NB, int MB>
+void launch_gather_two(const GatherArgs& g1, const GatherArgs& g2, hipStream_t s) {
+  hipLaunchKernelGGL((gather_shrink_kernel<NB, MB>), dim3(g1.per_xcd * kXcds), dim3(kThreads), 0,
+                     s, g1);
+  if (g2.R == 16 * NB)
+    hipLaunchKernelGGL((gather_expand_kernel<NB, MB, true>), dim3(g2.per_xcd * kXcds),
+                       dim3(kThreads), 0, s, g2);
+  else
+    hipLaunchKernelGGL((gather_expand_kernel<NB, MB, false>), dim3(g2.per_xcd * kXcds),
+                       dim3(kThreads), 0, s, g2);
+}
+
+template <int NB>
+void dispatch_gather_two_mb(const GatherArgs& g1, const GatherArgs& g2, hipStream_t s, int mb) {
+  if constexpr (NB <= 2) {
+    if (mb >= 4) return launch_gather_two<NB, 4>(g1, g2, s);
+  }
+  if constexpr (NB <= 4) {
+    if (mb >= 2) return launch_gather_two<NB, 2>(g1, g2, s);
+  }
+  launch_gather_two<NB, 1>(g1, g2, s);
+}
+
+void dispatch_gather_two(const GatherArgs& g1, const GatherArgs& g2, hipStream_t s, int mb) {
+  switch (kernel_nb(g1.R)) {
+    case 1: return dispatch_gather_two_mb<1>(g1, g2, s, mb);
+    case 2: return dispatch_gather_two_mb<2>(g1, g2, s, mb);
+    case 4: return dispatch_gather_two_mb<4>(g1, g2, s, mb);
+    default: return dispatch_gather_two_mb<8>(g1, g2, s, mb);
+  }
+}
+
 void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small, bool resident) {
   const int nb = (a.R + 15) / 16;
   if (resident && gather_resident_fits(a)) {
@@ -1574,9 +1965,13 @@ using namespace mlora;
 extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void* x,
                                      int64_t n_tokens, void* base_out, const int32_t* indices,
                                      const int32_t* row_adapter, int64_t n_slots, int32_t top_k,
-                                     void* stream) {
+                                     void* workspace, uint64_t workspace_bytes, void* stream) {
   const char* who = "mlora_gather_bgmv";
   if (int32_t rc = check_route(route, who)) return rc;
+  if (!workspace && workspace_bytes != 0)
+    return fail(MLORA_ERR_INVALID, "%s: NULL workspace with workspace_bytes > 0", who);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MLORA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
   if (top_k <= 0) return fail(MLORA_ERR_INVALID, "%s: top_k=%d must be positive", who, top_k);
   if (n_slots < 0 || n_slots > (int64_t)0x7fffffff - kScanMax)
     return fail(MLORA_ERR_INVALID, "%s: n_slots=%lld out of range", who, (long long)n_slots);
@@ -1590,6 +1985,10 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   }
   if (!x || !base_out || !indices || !row_adapter)
     return fail(MLORA_ERR_INVALID, "%s: NULL device pointer", who);
+  const int64_t ws_need = gather_ws_bytes(n_slots, route->k_in, route->max_rank);
+  if (workspace && route->dtype == MLORA_BF16 && (uint64_t)ws_need > workspace_bytes)
+    return fail(MLORA_ERR_CAPACITY, "%s: workspace of %llu bytes, %lld needed", who,
+                (unsigned long long)workspace_bytes, (long long)ws_need);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
 
@@ -1680,6 +2079,57 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   // weights held in registers when a slice is expected to hold at most two
   // 16-row blocks (and the wave's share fits)
   const int resident = env_int("MLORA_GATHER_RESIDENT", rows_per_slice <= 32 ? 1 : 0);
+  const bool use_resident = resident != 0 && gather_resident_fits(a);
+  // The two-kernel form holds at most kWaves * kTwoSteps k steps per range.
+  // It pays where an expert's A_e outweighs its rows' x (few rows per expert,
+  // k_in split over several ranges); an expert with many rows streams x once
+  // per row in one kernel anyway.
+  const bool two_fits = (K + 31) / 32 <= kMaxKc * kWaves * kTwoSteps;
+  const int64_t rows_e_all = (n_slots + E - 1) / E;
+  const int two_default = (gather_kc(K) > 1 && rows_e_all <= 64) ? 1 : 0;
+  if (workspace && !use_resident && two_fits &&
+      env_int("MLORA_GATHER_TWO", two_default) != 0) {
+    if (ws_need > (int64_t)kMaxBufBytes)
+      return fail(MLORA_ERR_INVALID, "%s: workspace above 4 GiB; split the call", who);
+    // k-split shrink, then expand; slices of at most 64 rows of an expert
+    const int64_t rows_e = (n_slots + E - 1) / E;
+    int64_t rs2 = (n_slots + kScanMax - 1) / kScanMax;
+    const int64_t want = (rows_e + 63) / 64;
+    if (want > rs2) rs2 = want;
+    if (rs2 > n_slots) rs2 = n_slots;
+    const int scan2 = (int)((n_slots + rs2 - 1) / rs2);
+    const int64_t rows_slice = (rows_e + rs2 - 1) / rs2;
+    const int mb = gather_two_mb(R, rows_slice);
+    const int kc = gather_kc(K);
+    const int nks = (K + 31) / 32;
+    // column slices of at most kWaves * kTwoSteps steps, more while short of
+    // one workgroup per CU
+    int ns2 = (ns_max + kWaves * kTwoSteps - 1) / (kWaves * kTwoSteps);
+    while ((int64_t)E * rs2 * ns2 < 256 && ns2 * 2 <= ns_max) ns2 *= 2;
+    ns2 = env_int("MLORA_GATHER_TWO_NS", ns2);
+    if (ns2 < 1) ns2 = 1;
+    if (ns2 > ns_max) ns2 = ns_max;
+    if (ns_cols_for(N, ns2) > kWaves * kTwoSteps * kColStep)
+      ns2 = (ns_max + kWaves * kTwoSteps - 1) / (kWaves * kTwoSteps);
+    GatherArgs g1 = a, g2 = a;
+    g1.ws = g2.ws = static_cast<float*>(workspace);
+    g1.ws_bytes = g2.ws_bytes = (uint32_t)ws_need;
+    g1.kc_count = g2.kc_count = kc;
+    g1.kc_steps = g2.kc_steps = (nks + kc - 1) / kc;
+    g1.rs_count = g2.rs_count = (int32_t)rs2;
+    g1.scan_len = g2.scan_len = scan2;
+    const int64_t u1 = (int64_t)E * rs2 * kc, u2 = (int64_t)E * rs2 * ns2;
+    if (u1 > 0x3fffffffll || u2 > 0x3fffffffll)
+      return fail(MLORA_ERR_INVALID, "%s: launch too large", who);
+    g1.units = (int32_t)u1;
+    g1.per_xcd = (int32_t)((u1 + kXcds - 1) / kXcds);
+    g2.ns_count = ns2;
+    g2.ns_cols = ns_cols_for(N, ns2);
+    g2.units = (int32_t)u2;
+    g2.per_xcd = (int32_t)((u2 + kXcds - 1) / kXcds);
+    dispatch_gather_two(g1, g2, s, mb);
+    return launched(who);
+  }
   dispatch_gather(a, grid, s, small != 0, resident != 0);
   return launched(who);
 }
@@ -1688,13 +2138,6 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
 struct WsLayout {
   int64_t h_bytes, meta_off, meta_bytes, total;
 };
-
-// Rank blocks the kernels use for max_rank R: ceil(R / 16) rounded up to 1,
-// 2, 4 or 8.
-int kernel_nb(int R) {
-  const int nb = (R + 15) / 16;
-  return nb <= 1 ? 1 : (nb <= 2 ? 2 : (nb <= 4 ? 4 : 8));
-}
 
 WsLayout grouped_ws_layout(int64_t rows, int R) {
   WsLayout w;
@@ -1771,6 +2214,12 @@ void dispatch_expand(const GroupedArgs& a, int grid, hipStream_t s, int mb, int 
     case 4: return launch_expand_mb<4>(a, grid, s, mb, cw);
     default: return launch_expand_mb<8>(a, grid, s, mb, cw);
   }
+}
+
+extern "C" uint64_t mlora_gather_bgmv_workspace_bytes(int64_t n_slots, int32_t k_in,
+                                                      int32_t max_rank) {
+  if (n_slots <= 0 || k_in < 1 || max_rank < 1 || max_rank > 128) return 0;
+  return (uint64_t)gather_ws_bytes(n_slots, k_in, max_rank);
 }
 
 extern "C" uint64_t mlora_grouped_down_workspace_bytes(int64_t row_offset, int64_t row_end,

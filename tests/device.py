@@ -92,10 +92,15 @@ class DeviceCase:
             self.offsets = torch.from_numpy(np.ascontiguousarray(c.expert_offsets, np.int32)).to(device)
             self.windows = ml.mlora_grouped_down_windows(c.n_rows, c.cap)
 
-    def workspace_for(self, windows) -> torch.Tensor:
-        """A device workspace large enough for every window (grown on demand)."""
-        need = max([ml.mlora_grouped_down_workspace_bytes(s, e, self.case.max_rank)
-                    for (s, e) in windows] + [0])
+    def workspace_for(self, windows=None) -> torch.Tensor:
+        """A device workspace large enough for the call(s) (grown on demand):
+        every window of a grouped case, or the gather call."""
+        c = self.case
+        if c.path == "gather":
+            need = ml.mlora_gather_bgmv_workspace_bytes(c.indices.shape[0], c.k_in, c.max_rank)
+        else:
+            need = max([ml.mlora_grouped_down_workspace_bytes(s, e, c.max_rank)
+                        for (s, e) in windows] + [0])
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
         return self._ws
@@ -103,16 +108,17 @@ class DeviceCase:
     def fold(self, base: torch.Tensor, windows=None, stream=None,
              two_kernel: bool = None) -> torch.Tensor:
         """Fold in place into ``base`` (a device tensor shaped like base_out).
-        Grouped calls take the two-kernel form (with a workspace) when
-        ``two_kernel`` is set, else the one-kernel form; None means the
-        case's default (``self.two_kernel``)."""
+        With ``two_kernel`` set the call gets a workspace (the two-kernel
+        form where the library takes it), else none (one kernel); None means
+        the case's default (``self.two_kernel``)."""
         c = self.case
+        two = self.two_kernel if two_kernel is None else two_kernel
         if c.path == "gather":
+            ws = self.workspace_for() if two else None
             ml.mlora_gather_bgmv(self.route, self.x, base, self.indices, self.row_adapter,
-                                 c.top_k, stream=stream)
+                                 c.top_k, workspace=ws, stream=stream)
         else:
             wins = self.windows if windows is None else windows
-            two = self.two_kernel if two_kernel is None else two_kernel
             ws = self.workspace_for(wins) if two else None
             for (s, e) in wins:
                 ml.mlora_grouped_down(self.route, self.x, base, self.offsets, self.sorted_ids,

@@ -333,6 +333,65 @@ def test_grouped_two_kernel_equals_one_kernel(label):
     assert np.array_equal(one.view(np.uint8), two.view(np.uint8))
 
 
+GATHER_SMALL = [s[0] for s in SMALL if s[1]["kind"] == "gather" and s[1].get("dtype") != "f32"]
+
+
+@pytest.mark.parametrize("label", ["cfg4", "cfg5a"] + GATHER_SMALL)
+def test_gather_one_kernel_form(label):
+    """The gather fold without a workspace (one kernel) passes the oracle bar;
+    the other tests give it a workspace, which large calls use for the
+    two-kernel form."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    if label.startswith("cfg"):
+        case, view, dev = staged(label)
+    else:
+        case = build_small(label, dict(SMALL)[label])
+        view, dev = OracleView(case), DeviceCase(case, DEV)
+    check(view, dev.run(two_kernel=False), case.base, f"{label} one-kernel")
+    zero = np.zeros_like(case.base)
+    if view.live_rows().any():
+        check(view, dev.run(zero, two_kernel=False), zero, f"{label} one-kernel Z")
+
+
+TWO_GATHER = ["gather_r24_k72", "gather_r48", "gather_r100", "gather_r128",
+              "gather_r64_many_rows", "gather_topk1_one_expert", "gather_slots_not_multiple",
+              "gather_all_skip", "gather_k1000_r100", "gather_k2048_r64_skew"]
+
+
+def _two_gather_case(label):
+    if label == "gather_k1000_r100":
+        return workloads.make_gather_case(83, n_seq=60, padded_n=64, top_k=4, n_route=20,
+                                          k_in=1000, n_out=392, max_rank=100, n_adapted=15,
+                                          skip_seqs=4, name=label)
+    if label == "gather_k2048_r64_skew":
+        return workloads.make_gather_case(84, n_seq=300, padded_n=300, top_k=2, n_route=3,
+                                          k_in=2048, n_out=264, max_rank=64, name=label)
+    return build_small(label, dict(SMALL)[label])
+
+
+@pytest.mark.parametrize("label", TWO_GATHER)
+def test_gather_two_kernel_form(label, monkeypatch):
+    """The two-kernel gather (k-split shrink into the workspace, then expand),
+    forced on: oracle bar on a random and a zero base, untouched rows bit
+    for bit. k_in 1000 and 2048 split into 2 and 4 k ranges."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    monkeypatch.setenv("MLORA_GATHER_TWO", "1")
+    monkeypatch.setenv("MLORA_GATHER_RESIDENT", "0")
+    case = _two_gather_case(label)
+    view, dev = OracleView(case), DeviceCase(case, DEV)
+    check(view, dev.run(two_kernel=True), case.base, f"{label} two-kernel")
+    zero = np.zeros_like(case.base)
+    if view.live_rows().any():
+        check(view, dev.run(zero, two_kernel=True), zero, f"{label} two-kernel Z")
+    live = view.live_rows()
+    base = case.base.copy()
+    put_sentinel(base, ~live, case.dtype)
+    got = dev.run(base, two_kernel=True)
+    assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
+
+
 def test_grouped_workspace_reused_across_windows_and_calls():
     """One workspace serves successive windows and calls; stale contents from a
     larger call never leak into a smaller one."""
@@ -379,7 +438,7 @@ def test_resident_weights_path_equals_streaming_path(label, monkeypatch):
     res = dev.run()
     check(view, res, case.base, f"{label} resident")
     monkeypatch.setenv("MLORA_GATHER_RESIDENT", "0")
-    stream = dev.run()
+    stream = dev.run(two_kernel=False)
     assert np.array_equal(res.view(np.uint8), stream.view(np.uint8))
 
 

@@ -255,21 +255,29 @@ FAKE = 1 << 24  # never dereferenced: every call below is rejected before launch
                                 dict(a_table=0)])
 def test_gather_rejects_bad_route(lib, kw):
     r = _route(**kw)
-    rc = lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, 8, 2, None)
+    rc = lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, 8, 2, None, 0, None)
     assert rc == ml.MLORA_ERR_INVALID
     assert ml.load().mlora_last_error()
 
 
 def test_gather_rejects_bad_args(lib):
     r = _route()
-    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, 8, 0, None) == -1
-    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 3, FAKE, FAKE, FAKE, 8, 2, None) == -1
-    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, -1, 2, None) == -1
-    assert lib.mlora_gather_bgmv(ctypes.byref(r), None, 4, FAKE, FAKE, FAKE, 8, 2, None) == -1
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, 8, 0, None, 0, None) == -1
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 3, FAKE, FAKE, FAKE, 8, 2, None, 0, None) == -1
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, -1, 2, None, 0, None) == -1
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), None, 4, FAKE, FAKE, FAKE, 8, 2, None, 0, None) == -1
     # nothing to fold: accepted without touching the device
-    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 0, FAKE, FAKE, FAKE, 0, 2, None) == 0
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 0, FAKE, FAKE, FAKE, 0, 2, None, 0, None) == 0
+    # workspace: NULL with a size, misaligned, too small
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, 8, 2, None, 256,
+                                 None) == -1
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, 8, 2, FAKE + 16,
+                                 1 << 20, None) == -1
+    need = lib.mlora_gather_bgmv_workspace_bytes(8, r.k_in, r.max_rank)
+    assert lib.mlora_gather_bgmv(ctypes.byref(r), FAKE, 4, FAKE, FAKE, FAKE, 8, 2, FAKE,
+                                 need - 1, None) == ml.MLORA_ERR_CAPACITY
     r0 = _route(n_experts=0)
-    assert lib.mlora_gather_bgmv(ctypes.byref(r0), FAKE, 4, FAKE, FAKE, FAKE, 8, 2, None) == 0
+    assert lib.mlora_gather_bgmv(ctypes.byref(r0), FAKE, 4, FAKE, FAKE, FAKE, 8, 2, None, 0, None) == 0
 
 
 def test_grouped_rejects_bad_args(lib):
@@ -292,6 +300,19 @@ def test_grouped_rejects_bad_args(lib):
     assert call(ws=FAKE + 16, ws_bytes=1 << 20) == -1
     need = lib.mlora_grouped_down_workspace_bytes(0, 8, 16)
     assert call(ws=FAKE, ws_bytes=need - 1) == ml.MLORA_ERR_CAPACITY
+
+
+def test_gather_workspace_bytes(lib):
+    f = lib.mlora_gather_bgmv_workspace_bytes
+    # KC k ranges (16 k steps each, at most 4) x n_slots x 64 x NB bytes,
+    # rounded to 256
+    assert f(640, 768, 16) == 2 * 640 * 64       # 24 k steps -> two ranges
+    assert f(640, 512, 16) == 1 * 640 * 64       # 16 k steps -> one range
+    assert f(2048, 2048, 64) == 4 * 2048 * 64 * 4  # 64 k steps -> 4 ranges
+    assert f(8192, 2048, 16) == 4 * 8192 * 64
+    assert f(10, 4096, 100) == (4 * 10 * 64 * 8 + 255) // 256 * 256  # capped at 4, NB 7 -> 8
+    assert f(3, 64, 8) == 256
+    assert f(0, 768, 16) == 0 and f(8, 0, 16) == 0 and f(8, 768, 0) == 0 and f(8, 768, 129) == 0
 
 
 def test_grouped_workspace_bytes(lib):
