@@ -59,8 +59,15 @@ WORKLOAD_TEXT = {
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: line comments and blank lines are
+    dropped first, so an edit of the comments keeps recorded counters valid."""
+    code = []
+    with open(KERNEL_SOURCE) as f:
+        for line in f:
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -264,10 +271,22 @@ def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     """Per-launch HBM bytes of the fold kernel from FETCH_SIZE / WRITE_SIZE runs
     (KiB per dispatch), each scaled by what the counter reads for the plain copy
     of CALIB_BYTES; recorded in profiles/traffic.json with the kernel hash."""
-    is_fold = lambda n: "fold_kernel" in n  # noqa: E731
-    is_copy = lambda n: "fold" not in n  # noqa: E731
-    f_kib, nf = _mean_counter(_pmc_rows(fetch_dir), "FETCH_SIZE", is_fold)
-    w_kib, nw = _mean_counter(_pmc_rows(write_dir), "WRITE_SIZE", is_fold)
+    # a fold call is one kernel (gather decode, one-kernel forms) or a shrink
+    # and an expand kernel: the per-call figure sums the per-dispatch means of
+    # every fold kernel the runs saw
+    is_copy = lambda n: "mlora" not in n  # noqa: E731
+    rows_f, rows_w = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    names = sorted({r["Kernel_Name"] for r in rows_f + rows_w if "mlora" in r["Kernel_Name"]})
+    f_kib = w_kib = 0.0
+    nf, nw = [], []
+    for name in names:
+        same = lambda n, name=name: n == name  # noqa: E731
+        a, na = _mean_counter(rows_f, "FETCH_SIZE", same)
+        b, nb = _mean_counter(rows_w, "WRITE_SIZE", same)
+        f_kib += a or 0.0
+        w_kib += b or 0.0
+        nf.append(na)
+        nw.append(nb)
     cal_rows_f = _pmc_rows(cal_fetch_dir)
     cal_rows_w = _pmc_rows(cal_write_dir)
     # the copy dispatch is the largest FETCH_SIZE / WRITE_SIZE in the calibration runs
@@ -280,6 +299,7 @@ def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     rec = {
         "kernel_sha256_16": kernel_hash(),
         "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+        "kernels": [n.split("(")[0] for n in names],
         "dispatches": [nf, nw],
         "copy_scale_fetch": kf, "copy_scale_write": kw,
         "hbm_bytes_per_launch": f_kib * 1024.0 * kf + w_kib * 1024.0 * kw,

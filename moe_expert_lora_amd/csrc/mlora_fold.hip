@@ -4,31 +4,37 @@
 //
 //     base_out[row] += scale_e * ((x[token(row)] @ A_e^T) @ B_e^T)
 //
-// Design (one fused kernel per call, no device scratch):
-//  * A work unit is (expert e, up to 16*MB rows of e, a column range of
-//    base_out). The shrink H = X A_e^T and the expand base + s H B_e^T both
-//    run on bf16 MFMA (v_mfma_f32_16x16x32_bf16), with fp32 accumulation.
+// Design:
+//  * Each call runs as one kernel, or, for large calls given a workspace, as
+//    a shrink kernel that writes H (scaled hi/lo bf16 for the grouped fold,
+//    fp32 partial sums over k ranges for the gather fold) and an expand
+//    kernel that reads it back. The shrink H = X A_e^T and the expand
+//    base + s H B_e^T both run on bf16 MFMA (v_mfma_f32_16x16x32_bf16), with
+//    fp32 accumulation.
 //  * Shrink, transposed: D[rank][row] = A_e[rank,:] . x[row,:]. The 4 waves
 //    split k_in; partial sums meet in LDS and are added in a fixed order.
 //    A rank permutation makes each lane end up holding 4*NB consecutive ranks
-//    of one row, which is exactly the operand layout the expand needs.
+//    of one row, which is exactly the operand layout the expand needs (also
+//    the layout H takes in the workspace).
 //  * H is scaled by scale_e and split into hi + lo bf16 halves, so the expand
 //    MFMA sees H to ~16 mantissa bits (rounding H to one bf16 alone would use
 //    most of the error budget that the final bf16 store leaves).
 //  * Expand, transposed: D[col][row] = B_e[col,:] . H'[:,row] with
 //    K' = 2*max_rank (hi then lo). A column permutation gives each lane a run
-//    of 8 consecutive output columns of one row, so base_out is read and
-//    written with 16-byte accesses, 64 contiguous bytes per row per
-//    instruction, and never staged through LDS.
+//    of 8 consecutive output columns of one row. The grouped expand kernel
+//    moves the fp32 deltas through the wave's LDS so that base_out is read
+//    and written row-contiguously; the other kernels access base_out in the
+//    MFMA layout (16 rows x 64 bytes per instruction).
 //  * Every operand moves through raw buffer loads/stores: 32-bit offsets, and
 //    a masked lane simply uses an offset past the buffer (its load returns 0,
 //    its store is dropped), so no access needs a branch. Loads are issued in
-//    batches and consumed after one wait.
+//    batches and consumed after one wait; code that needs an exact wait count
+//    stays straight-line.
 //  * Gather rows are grouped by expert on the device: each workgroup scans a
 //    slice of `indices` for its expert, so each A_e / B_e is streamed from HBM
 //    once per workgroup group and reused across that expert's rows.
-//  * Grouped rows come in MLORA_MLG_M_TILE-row tiles; a tile that straddles
-//    expert spans is folded one span segment at a time.
+//  * Grouped rows come in tiles; a tile that straddles expert spans is folded
+//    one span (or, in the shrink kernel, two spans) at a time.
 //  * Workgroup ids are mapped so that consecutive work units (the splits of
 //    one expert, or neighbouring row tiles) run on the same XCD and share its
 //    L2.
