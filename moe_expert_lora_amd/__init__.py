@@ -47,6 +47,8 @@ EXPORTS = (
     "mlora_grouped_down",
     "mlora_grouped_down_workspace_bytes",
     "mlora_gather_bgmv_workspace_bytes",
+    "mlora_grouped_down_all",
+    "mlora_grouped_down_all_workspace_bytes",
 )
 
 
@@ -115,6 +117,9 @@ def load() -> ctypes.CDLL:
         "mlora_grouped_down": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64, vp, i32,
                                      vp, vp, i32, i64, i64, vp, ctypes.c_uint64, vp]),
         "mlora_grouped_down_workspace_bytes": (ctypes.c_uint64, [i64, i64, i32]),
+        "mlora_grouped_down_all": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64, vp, i32,
+                                         vp, vp, i32, i64, vp, ctypes.c_uint64, vp]),
+        "mlora_grouped_down_all_workspace_bytes": (ctypes.c_uint64, [i64, i64, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -365,5 +370,45 @@ def mlora_grouped_down(route: ExpertRoute, x, base_out, expert_offsets, sorted_i
         _dev(sorted_ids, "sorted_ids", torch.int32),
         _dev(row_adapter, "row_adapter", torch.int32), int(top_k), int(row_offset),
         int(row_end), ws_ptr, ws_bytes, _stream_handle(stream))
+    if rc != MLORA_OK:
+        raise _err(rc)
+
+
+def mlora_grouped_down_all_workspace_bytes(n_rows: int, cap: int, max_rank: int) -> int:
+    """Workspace bytes of the pipelined all-windows grouped fold."""
+    return int(load().mlora_grouped_down_all_workspace_bytes(int(n_rows), int(cap),
+                                                             int(max_rank)))
+
+
+def mlora_grouped_down_all(route: ExpertRoute, x, base_out, expert_offsets, sorted_ids,
+                           row_adapter, top_k: int, cap: int, workspace, stream=None) -> None:
+    """Grouped fold of every sorted row of ``base_out``, windows of ``cap`` rows
+    pipelined; ``workspace`` a contiguous device tensor of at least
+    ``mlora_grouped_down_all_workspace_bytes`` bytes (bf16 routes)."""
+    import torch
+    if _dtype_code(x) != route.dtype or _dtype_code(base_out) != route.dtype:
+        raise TypeError("x / base_out dtype differs from the route's")
+    if x.dim() != 2 or base_out.dim() != 2:
+        raise ValueError("x and base_out must be 2-D")
+    if x.shape[1] != route.k_in or base_out.shape[1] != route.n_out:
+        raise ValueError("x / base_out widths differ from the route's k_in / n_out")
+    n_rows = base_out.shape[0]
+    if sorted_ids.numel() != n_rows:
+        raise ValueError("sorted_ids must have one entry per base_out row")
+    if row_adapter.numel() < x.shape[0]:
+        raise ValueError("row_adapter must cover every x row")
+    n_route = expert_offsets.numel() - 1
+    if n_route < 0:
+        raise ValueError("expert_offsets needs at least one entry")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load().mlora_grouped_down_all(
+        ctypes.byref(route), _dev(x, "x"), x.shape[0], _dev(base_out, "base_out"), n_rows,
+        _dev(expert_offsets, "expert_offsets", torch.int32), int(n_route),
+        _dev(sorted_ids, "sorted_ids", torch.int32),
+        _dev(row_adapter, "row_adapter", torch.int32), int(top_k), int(cap), ws_ptr, ws_bytes,
+        _stream_handle(stream))
     if rc != MLORA_OK:
         raise _err(rc)

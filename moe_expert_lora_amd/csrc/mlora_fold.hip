@@ -1417,22 +1417,34 @@ struct ShrinkUS {
 // fragments shared. The k-split and the reduction are those of the one-kernel
 // form, so H' comes out bit for bit the same.
 template <int NB, int MB>
-__global__ __launch_bounds__(kThreads) void grouped_shrink_kernel(GroupedArgs p) {
-  constexpr int kRows = 16 * MB;
-  constexpr int US = ShrinkUS<NB, MB>::US;
-  constexpr uint32_t kRowBytes = 64u * NB;  // 4 * RP
-  constexpr int kPart = kWaves * MB * 64 * 4 * NB;
-  __shared__ float s_part[2 * kPart];
-  __shared__ int s_tok[kRows];
-  __shared__ int s_live[kRows];
-  __shared__ int s_seg_lo[kRows], s_seg_hi[kRows];
-  __shared__ uint64_t s_seg_a[kRows], s_seg_b[kRows];
-  __shared__ float s_seg_s[kRows];
-  __shared__ int s_nseg;
+struct ShrinkSmem {
+  static constexpr int kRows = 16 * MB;
+  static constexpr int kPart = kWaves * MB * 64 * 4 * NB;
+  float part[2 * kPart];
+  uint64_t seg_a[kRows], seg_b[kRows];
+  int tok[kRows], live[kRows], seg_lo[kRows], seg_hi[kRows];
+  float seg_s[kRows];
+  int nseg;
+};
 
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int u = xcd * p.per_xcd + slot;
-  if (u >= p.units) return;
+// The shrink of work unit u (16*MB rows of the window); all threads of the
+// workgroup call it with the same unit.
+template <int NB, int MB, int US = ShrinkUS<NB, MB>::US>
+__device__ __forceinline__ void grouped_shrink_unit(const GroupedArgs& p, int u,
+                                                    ShrinkSmem<NB, MB>& sm) {
+  constexpr int kRows = 16 * MB;
+  constexpr uint32_t kRowBytes = 64u * NB;  // 4 * RP
+  constexpr int kPart = ShrinkSmem<NB, MB>::kPart;
+  float* s_part = sm.part;
+  int* s_tok = sm.tok;
+  int* s_live = sm.live;
+  int* s_seg_lo = sm.seg_lo;
+  int* s_seg_hi = sm.seg_hi;
+  uint64_t* s_seg_a = sm.seg_a;
+  uint64_t* s_seg_b = sm.seg_b;
+  float* s_seg_s = sm.seg_s;
+  int& s_nseg = sm.nseg;
+
   const int64_t r0 = p.row_offset + (int64_t)u * kRows;
   const int64_t r1 = min(r0 + kRows, p.row_end);
   const int tid = threadIdx.x;
@@ -1605,31 +1617,44 @@ __global__ __launch_bounds__(kThreads) void grouped_shrink_kernel(GroupedArgs p)
   }
 }
 
+template <int NB, int MB>
+__global__ __launch_bounds__(kThreads) void grouped_shrink_kernel(GroupedArgs p) {
+  __shared__ ShrinkSmem<NB, MB> sm;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * p.per_xcd + slot;
+  if (u >= p.units) return;
+  grouped_shrink_unit<NB, MB>(p, u, sm);
+}
+
 // Expand: one wave per (16*MB rows, CW column steps). It reads the rows' meta,
 // then requests H', the B_e fragments of the first run of rows (rows with one
 // B_e) and the rows' base_out, the last in a row-contiguous layout: LPR lanes
 // cover one row's CW*32 columns, 16 bytes each. The MFMA deltas (fp32, one
 // lane per row) go through the wave's own LDS to that layout; each row is
 // then rounded once and stored.
+// LDS floats of one expand wave: its fp32 deltas, one padded row per row.
+template <int MB, int CW>
+struct ExpandSmem {
+  static constexpr int kStride = CW * kColStep + 4;  // the pad spreads rows over banks
+  static constexpr int kFloats = 16 * MB * kStride;
+};
+
+// The expand of work unit u by one wave (no workgroup barriers).
 template <int NB, int MB, int CW, bool FULL_R>
-__global__ __launch_bounds__(64) void grouped_expand_kernel(GroupedArgs p) {
+__device__ __forceinline__ void grouped_expand_unit(const GroupedArgs& p, int u, float* s_d) {
   constexpr int kRows = 16 * MB;
   constexpr int kCols = CW * kColStep;
-  constexpr int kStride = kCols + 4;  // fp32 per LDS row; the pad spreads rows over banks
+  constexpr int kStride = ExpandSmem<MB, CW>::kStride;
   constexpr int LPR = kCols / 8;      // lanes per row in the contiguous layout
   constexpr int RPI = 64 / LPR;       // rows per contiguous access
   constexpr int NI = kRows / RPI;     // contiguous accesses per wave
   constexpr uint32_t kRowBytes = 64u * NB;
   constexpr int CC = Chunk<NB>::kCount;
   static_assert(kRows <= 64 && 64 % LPR == 0 && kRows % RPI == 0, "expand shape");
-  __shared__ float s_d[kRows * kStride];
 
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int u = xcd * p.per_xcd + slot;
-  if (u >= p.units) return;
   const int ns = u % p.ns_count;
   const int r0 = (u / p.ns_count) * kRows;  // window-relative
-  const int lane = threadIdx.x, li = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
 
   const int n_lo = ns * kCols;
   const int n_hi = min(n_lo + kCols, p.N);
@@ -1716,6 +1741,42 @@ __global__ __launch_bounds__(64) void grouped_expand_kernel(GroupedArgs p) {
     const bool ok = ((live >> (i * RPI + cr)) & 1ull) != 0 && n_lo + 8 * cc < n_hi;
     bst16_nt(r_out, ok ? boff[i] : kOOB, u32x4{o0, o1, o2, o3});
   }
+}
+
+template <int NB, int MB, int CW, bool FULL_R>
+__global__ __launch_bounds__(64) void grouped_expand_kernel(GroupedArgs p) {
+  __shared__ float s_d[ExpandSmem<MB, CW>::kFloats];
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * p.per_xcd + slot;
+  if (u >= p.units) return;
+  grouped_expand_unit<NB, MB, CW, FULL_R>(p, u, s_d);
+}
+
+// One launch that expands one window and shrinks the next: blocks
+// 0 .. shrink_blocks-1 run shrink units of `ps`, every later block runs four
+// independent expand waves of `pe`. The two halves touch disjoint workspace
+// slots, so nothing orders them against each other.
+template <int NB, int SMB, int EMB, int CW, bool FULL_R>
+__global__ __launch_bounds__(kThreads) void grouped_pipe_kernel(GroupedArgs ps, GroupedArgs pe) {
+  __shared__ union {
+    ShrinkSmem<NB, SMB> s;
+    float d[kWaves][ExpandSmem<EMB, CW>::kFloats];
+  } sm;
+  const int sblocks = ps.per_xcd * kXcds;
+  if ((int)blockIdx.x < sblocks) {
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int u = xcd * ps.per_xcd + slot;
+    // a batch of one k step per wave: the shrink half runs beside the
+    // expand waves, and the launch's registers are the larger half's
+    if (u < ps.units) grouped_shrink_unit<NB, SMB, 1>(ps, u, sm.s);
+    return;
+  }
+  // sblocks is a multiple of kXcds, so b keeps the block's XCD
+  const int b = (int)blockIdx.x - sblocks;
+  const int xcd = b % kXcds, slot = b / kXcds;
+  const int wave = threadIdx.x >> 6;
+  const int u = (xcd * pe.per_xcd + slot) * kWaves + wave;
+  if (u < pe.units) grouped_expand_unit<NB, EMB, CW, FULL_R>(pe, u, sm.d[wave]);
 }
 
 // ---------------------------------------------------------------------------
@@ -2222,6 +2283,64 @@ void dispatch_expand(const GroupedArgs& a, int grid, hipStream_t s, int mb, int 
   }
 }
 
+// ---- pipelined grouped windows ----
+
+// Launch shape of the two-kernel grouped form on a window of `rows` rows.
+struct TwoPlan {
+  int smb, emb, cw;
+  int64_t sunits, etiles, eslices;
+};
+
+TwoPlan two_plan(int R, int N, int64_t rows, bool fixed) {
+  TwoPlan t;
+  t.smb = kernel_nb(R) <= 2 ? 2 : 1;
+  t.emb = 1;
+  t.cw = expand_cw(R, 4);
+  if (!fixed) {
+    t.smb = env_int("MLORA_SHRINK_MB", t.smb) >= 2 ? 2 : 1;
+    t.emb = expand_mb(R, env_int("MLORA_EXPAND_MB", 1));
+    t.cw = expand_cw(R, env_int("MLORA_EXPAND_CW", 4));
+  }
+  t.sunits = (rows + 16 * t.smb - 1) / (16 * t.smb);
+  t.etiles = (rows + 16 * t.emb - 1) / (16 * t.emb);
+  t.eslices = (N + t.cw * kColStep - 1) / (t.cw * kColStep);
+  return t;
+}
+
+template <int NB, int SMB, int CW, bool FULL_R>
+void launch_pipe(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_pipe_kernel<NB, SMB, 1, CW, FULL_R>), dim3(grid), dim3(kThreads),
+                     0, s, ps, pe);
+}
+
+// The pipelined launches use the default shapes of two_plan(fixed = true).
+template <int NB>
+void dispatch_pipe_nb(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipStream_t s,
+                      int cw) {
+  constexpr int SMB = NB <= 2 ? 2 : 1;
+  if (ps.R != 16 * NB) return launch_pipe<NB, SMB, 2, false>(ps, pe, grid, s);
+  if constexpr (NB <= 2) {
+    if (cw >= 4) return launch_pipe<NB, SMB, 4, true>(ps, pe, grid, s);
+  }
+  launch_pipe<NB, SMB, 2, true>(ps, pe, grid, s);
+}
+
+void dispatch_pipe(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipStream_t s,
+                   int cw) {
+  switch (kernel_nb(ps.R)) {
+    case 1: return dispatch_pipe_nb<1>(ps, pe, grid, s, cw);
+    case 2: return dispatch_pipe_nb<2>(ps, pe, grid, s, cw);
+    case 4: return dispatch_pipe_nb<4>(ps, pe, grid, s, cw);
+    default: return dispatch_pipe_nb<8>(ps, pe, grid, s, cw);
+  }
+}
+
+// Workspace of one window slot of the pipelined call.
+int64_t pipe_slot_bytes(int64_t n_rows, int64_t cap, int R) {
+  const int64_t rows = n_rows < cap ? n_rows : cap;
+  return (grouped_ws_layout(rows, R).total + 255) & ~(int64_t)255;
+}
+
 extern "C" uint64_t mlora_gather_bgmv_workspace_bytes(int64_t n_slots, int32_t k_in,
                                                       int32_t max_rank) {
   if (n_slots <= 0 || k_in < 1 || max_rank < 1 || max_rank > 128) return 0;
@@ -2382,5 +2501,134 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
   a.per_xcd = (int32_t)((units + kXcds - 1) / kXcds);
   const int grid = a.per_xcd * kXcds;
   dispatch_grouped(a, grid, s, mb);
+  return launched(who);
+}
+
+extern "C" uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap,
+                                                           int32_t max_rank) {
+  if (n_rows <= 0 || cap <= 0 || max_rank < 1 || max_rank > 128) return 0;
+  const int64_t slots = n_rows > cap ? 2 : 1;
+  return (uint64_t)(slots * pipe_slot_bytes(n_rows, cap, max_rank));
+}
+
+extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x,
+                                          int64_t n_tokens, void* base_out, int64_t n_rows,
+                                          const int32_t* expert_offsets, int32_t n_route,
+                                          const int32_t* sorted_ids, const int32_t* row_adapter,
+                                          int32_t top_k, int64_t cap, void* workspace,
+                                          uint64_t workspace_bytes, void* stream) {
+  const char* who = "mlora_grouped_down_all";
+  if (int32_t rc = check_route(route, who)) return rc;
+  if (top_k <= 0) return fail(MLORA_ERR_INVALID, "%s: top_k=%d must be positive", who, top_k);
+  if (n_route < 0) return fail(MLORA_ERR_INVALID, "%s: n_route < 0", who);
+  if (n_tokens < 0 || n_tokens > 0x3fffffffll)
+    return fail(MLORA_ERR_INVALID, "%s: n_tokens out of range", who);
+  if (n_rows < 0) return fail(MLORA_ERR_INVALID, "%s: n_rows < 0", who);
+  if (cap <= 0) return fail(MLORA_ERR_INVALID, "%s: cap=%lld must be positive", who, (long long)cap);
+  if (!workspace && workspace_bytes != 0)
+    return fail(MLORA_ERR_INVALID, "%s: NULL workspace with workspace_bytes > 0", who);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MLORA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
+  if (n_rows == 0 || route->n_experts == 0 || n_route == 0) {
+    clear_error();
+    return MLORA_OK;
+  }
+  if (!x || !base_out || !expert_offsets || !sorted_ids || !row_adapter)
+    return fail(MLORA_ERR_INVALID, "%s: NULL device pointer", who);
+  const int64_t n_win = (n_rows + cap - 1) / cap;
+  const int R = route->max_rank, N = route->n_out, K = route->k_in;
+  const int64_t slot = pipe_slot_bytes(n_rows, cap, R);
+  const int64_t need = (n_win > 1 ? 2 : 1) * slot;
+  if (route->dtype == MLORA_BF16 && (!workspace || (uint64_t)need > workspace_bytes))
+    return fail(MLORA_ERR_CAPACITY, "%s: workspace of %llu bytes, %lld needed", who,
+                (unsigned long long)workspace_bytes, (long long)need);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+
+  if (route->dtype == MLORA_F32) {
+    // the plain row-wise kernel has no windows to pipeline: one launch per window
+    for (int64_t w = 0; w < n_win; ++w) {
+      const int64_t r0 = w * cap, r1 = r0 + cap < n_rows ? r0 + cap : n_rows;
+      if (int32_t rc = mlora_grouped_down(route, x, n_tokens, base_out, n_rows, expert_offsets,
+                                          n_route, sorted_ids, row_adapter, top_k, r0, r1,
+                                          nullptr, 0, stream))
+        return rc;
+    }
+    clear_error();
+    return MLORA_OK;
+  }
+
+  if (!aligned16(x) || !aligned16(base_out))
+    return fail(MLORA_ERR_INVALID, "%s: x and base_out must be 16-byte aligned", who);
+  const int64_t x_bytes = n_tokens * K * 2;
+  const int64_t win_rows = n_rows < cap ? n_rows : cap;
+  const WsLayout wl = grouped_ws_layout(win_rows, R);
+  if (x_bytes > (int64_t)kMaxBufBytes || win_rows * N * 2 > (int64_t)kMaxBufBytes ||
+      wl.h_bytes > (int64_t)kMaxBufBytes || wl.meta_bytes > (int64_t)kMaxBufBytes ||
+      (win_rows + 63) / 16 * ((N + kColStep - 1) / kColStep) > 0x3fffffffll)
+    return fail(MLORA_ERR_INVALID, "%s: window of %lld rows too large; lower cap", who,
+                (long long)win_rows);
+
+  // arguments of window w (its rows, its workspace slot), with the shrink or
+  // the expand launch fields
+  auto window = [&](int64_t w, bool expand, int64_t* blocks) {
+    GroupedArgs a{};
+    const int64_t r0 = w * cap, r1 = r0 + cap < n_rows ? r0 + cap : n_rows;
+    const WsLayout l = grouped_ws_layout(r1 - r0, R);
+    uint8_t* base = static_cast<uint8_t*>(workspace) + (w % 2) * slot;
+    a.x = static_cast<const uint16_t*>(x);
+    a.out = static_cast<uint16_t*>(base_out) + r0 * N;
+    a.offsets = expert_offsets;
+    a.sorted_ids = sorted_ids;
+    a.row_adapter = row_adapter;
+    a.a_table = route->a_table;
+    a.b_table = route->b_table;
+    a.scale_table = route->scale_table;
+    a.x_bytes = (uint32_t)x_bytes;
+    a.out_bytes = (uint32_t)((r1 - r0) * N * 2);
+    a.row_offset = r0;
+    a.row_end = r1;
+    a.n_experts = route->n_experts;
+    a.K = K;
+    a.N = N;
+    a.R = R;
+    a.n_route = n_route;
+    a.top_k = top_k;
+    a.n_tokens = (int32_t)n_tokens;
+    a.top_k_magic = magic_for(top_k);
+    a.ws_h = base;
+    a.ws_meta = reinterpret_cast<uint64_t*>(base + l.meta_off);
+    a.ws_h_bytes = (uint32_t)l.h_bytes;
+    a.ws_meta_bytes = (uint32_t)l.meta_bytes;
+    const TwoPlan t = two_plan(R, N, r1 - r0, true);
+    if (!expand) {
+      a.units = (int32_t)t.sunits;
+      a.per_xcd = (int32_t)((t.sunits + kXcds - 1) / kXcds);
+      *blocks = (int64_t)a.per_xcd * kXcds;
+    } else {
+      a.ns_count = (int32_t)t.eslices;
+      a.units = (int32_t)(t.etiles * t.eslices);
+      *blocks = (a.units + kWaves - 1) / kWaves;  // four expand waves per pipe block
+    }
+    return a;
+  };
+  const int cw = two_plan(R, N, win_rows, true).cw;
+  int64_t nb = 0;
+  GroupedArgs first = window(0, false, &nb);
+  dispatch_shrink(first, (int)nb, s, two_plan(R, N, win_rows, true).smb);
+  if (int32_t rc = launched(who)) return rc;
+  for (int64_t w = 1; w < n_win; ++w) {
+    int64_t sb = 0, eb = 0;
+    const GroupedArgs ps = window(w, false, &sb);
+    GroupedArgs pe = window(w - 1, true, &eb);
+    pe.per_xcd = (int32_t)((eb + kXcds - 1) / kXcds);  // expand blocks per XCD
+    const int64_t grid = sb + (int64_t)pe.per_xcd * kXcds;
+    dispatch_pipe(ps, pe, (int)grid, s, cw);
+    if (int32_t rc = launched(who)) return rc;
+  }
+  int64_t lb = 0;
+  GroupedArgs last = window(n_win - 1, true, &lb);
+  last.per_xcd = (int32_t)((last.units + kXcds - 1) / kXcds);
+  dispatch_expand(last, last.per_xcd * kXcds, s, 1, cw);
   return launched(who);
 }

@@ -38,10 +38,12 @@ def u64_to_device(a: np.ndarray, device) -> torch.Tensor:
 class DeviceCase:
     """Everything one fold call needs, resident on the GPU."""
 
-    def __init__(self, case: FoldCase, device="cuda", two_kernel: bool = True):
+    def __init__(self, case: FoldCase, device="cuda", two_kernel: bool = True,
+                 pipelined: bool = True):
         self.case = case
         self.device = device
         self.two_kernel = two_kernel
+        self.pipelined = pipelined
         self._ws = None
         c = case
         self.tdtype = torch.bfloat16 if c.dtype == "bf16" else torch.float32
@@ -100,17 +102,20 @@ class DeviceCase:
             need = ml.mlora_gather_bgmv_workspace_bytes(c.indices.shape[0], c.k_in, c.max_rank)
         else:
             need = max([ml.mlora_grouped_down_workspace_bytes(s, e, c.max_rank)
-                        for (s, e) in windows] + [0])
+                        for (s, e) in (windows or [])] +
+                       [ml.mlora_grouped_down_all_workspace_bytes(c.n_rows, c.cap, c.max_rank)])
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
         return self._ws
 
     def fold(self, base: torch.Tensor, windows=None, stream=None,
-             two_kernel: bool = None) -> torch.Tensor:
+             two_kernel: bool = None, pipelined: bool = None) -> torch.Tensor:
         """Fold in place into ``base`` (a device tensor shaped like base_out).
         With ``two_kernel`` set the call gets a workspace (the two-kernel
-        form where the library takes it), else none (one kernel); None means
-        the case's default (``self.two_kernel``)."""
+        form where the library takes it), else none (one kernel); a grouped
+        case with a workspace and no explicit windows folds every window in
+        one pipelined call when ``pipelined`` is set, else window by window.
+        None means the case's defaults."""
         c = self.case
         two = self.two_kernel if two_kernel is None else two_kernel
         if c.path == "gather":
@@ -118,6 +123,13 @@ class DeviceCase:
             ml.mlora_gather_bgmv(self.route, self.x, base, self.indices, self.row_adapter,
                                  c.top_k, workspace=ws, stream=stream)
         else:
+            pipe = self.pipelined if pipelined is None else pipelined
+            if two and pipe and windows is None:
+                # every window in one pipelined call
+                ml.mlora_grouped_down_all(self.route, self.x, base, self.offsets,
+                                          self.sorted_ids, self.row_adapter, c.top_k, c.cap,
+                                          self.workspace_for(self.windows), stream=stream)
+                return base
             wins = self.windows if windows is None else windows
             ws = self.workspace_for(wins) if two else None
             for (s, e) in wins:
@@ -127,9 +139,9 @@ class DeviceCase:
         return base
 
     def run(self, base_host: np.ndarray = None, windows=None,
-            two_kernel: bool = None) -> np.ndarray:
+            two_kernel: bool = None, pipelined: bool = None) -> np.ndarray:
         base = self.base0.clone() if base_host is None else to_torch(base_host, self.case.dtype,
                                                                      self.device)
-        self.fold(base, windows=windows, two_kernel=two_kernel)
+        self.fold(base, windows=windows, two_kernel=two_kernel, pipelined=pipelined)
         torch.cuda.synchronize()
         return from_torch(base)

@@ -392,6 +392,36 @@ def test_gather_two_kernel_form(label, monkeypatch):
     assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
 
 
+@pytest.mark.parametrize("label", ["cfg3", "cfg5b"] + [s[0] for s in GROUPED_SMALL])
+def test_grouped_all_windows_pipelined_equals_per_window(label):
+    """mlora_grouped_down_all (window w + 1 shrunk in the launch that expands
+    window w) equals one mlora_grouped_down call per window, bit for bit."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    if label.startswith("cfg"):
+        case, view, dev = staged(label)
+    else:
+        case = build_small(label, dict(SMALL)[label])
+        view, dev = OracleView(case), DeviceCase(case, DEV)
+    per_window = dev.run(two_kernel=True, pipelined=False)
+    pipelined = dev.run(two_kernel=True, pipelined=True)
+    assert np.array_equal(per_window.view(np.uint8), pipelined.view(np.uint8))
+
+
+def test_grouped_all_many_small_windows():
+    """Many windows (cap 40 over 1203 rows): both workspace slots alternate."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    case = workloads.make_grouped_case(95, stream_lens=[200, 101], top_k=4, n_route=9,
+                                       k_in=320, n_out=264, max_rank=24, routing="zipf",
+                                       n_unadapted=2, cap=40, stream_slot_values=[1, 1])
+    view, dev = OracleView(case), DeviceCase(case, DEV)
+    assert len(dev.windows) > 20
+    check(view, dev.run(two_kernel=True, pipelined=True), case.base, "cap40 pipelined")
+    assert np.array_equal(dev.run(two_kernel=True, pipelined=True).view(np.uint8),
+                          dev.run(two_kernel=True, pipelined=False).view(np.uint8))
+
+
 def test_grouped_workspace_reused_across_windows_and_calls():
     """One workspace serves successive windows and calls; stale contents from a
     larger call never leak into a smaller one."""

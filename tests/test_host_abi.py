@@ -302,6 +302,31 @@ def test_grouped_rejects_bad_args(lib):
     assert call(ws=FAKE, ws_bytes=need - 1) == ml.MLORA_ERR_CAPACITY
 
 
+def test_grouped_all_rejects_bad_args(lib):
+    r = _route()
+    call = lambda **k: lib.mlora_grouped_down_all(  # noqa: E731
+        ctypes.byref(k.get("route", r)), FAKE, 4, FAKE, k.get("n_rows", 8), FAKE,
+        k.get("n_route", 4), FAKE, FAKE, k.get("top_k", 2), k.get("cap", 4),
+        k.get("ws", FAKE), k.get("ws_bytes", 1 << 20), None)
+    assert call(cap=0) == -1 and call(cap=-3) == -1      # the pages' panic on cap == 0
+    assert call(top_k=0) == -1
+    assert call(n_rows=-1) == -1
+    assert call(ws=None, ws_bytes=256) == -1
+    assert call(ws=FAKE + 16) == -1
+    need = lib.mlora_grouped_down_all_workspace_bytes(8, 4, 8)
+    assert call(ws_bytes=need - 1) == ml.MLORA_ERR_CAPACITY
+    assert call(ws=None, ws_bytes=0) == ml.MLORA_ERR_CAPACITY   # bf16 needs one
+    assert call(n_rows=0) == 0 and call(n_route=0) == 0
+
+
+def test_grouped_all_workspace_bytes(lib):
+    f, g = lib.mlora_grouped_down_all_workspace_bytes, lib.mlora_grouped_down_workspace_bytes
+    assert f(32768, 8192, 32) == 2 * g(0, 8192, 32)
+    assert f(5000, 8192, 32) == g(0, 5000, 32)        # one window, one slot
+    assert f(100, 30, 100) == 2 * g(0, 30, 100)
+    assert f(0, 10, 16) == 0 and f(10, 0, 16) == 0 and f(10, 10, 0) == 0
+
+
 def test_gather_workspace_bytes(lib):
     f = lib.mlora_gather_bgmv_workspace_bytes
     # KC k ranges (16 k steps each, at most 4) x n_slots x 64 x NB bytes,
