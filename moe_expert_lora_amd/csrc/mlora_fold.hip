@@ -2291,15 +2291,18 @@ struct TwoPlan {
   int64_t sunits, etiles, eslices;
 };
 
-TwoPlan two_plan(int R, int N, int64_t rows, bool fixed) {
+TwoPlan two_plan(int R, int N, int64_t rows, bool pipe) {
   TwoPlan t;
   t.smb = kernel_nb(R) <= 2 ? 2 : 1;
-  t.emb = 1;
-  t.cw = expand_cw(R, 4);
-  if (!fixed) {
+  t.emb = expand_mb(R, env_int("MLORA_EXPAND_MB", 1));
+  t.cw = expand_cw(R, env_int("MLORA_EXPAND_CW", 4));
+  if (pipe) {
+    // the pipe kernel takes 1 expand row block, or 2 for full rank blocks of
+    // at most 32 ranks, and always its default shrink tile
+    const bool small_full = R == 16 * kernel_nb(R) && kernel_nb(R) <= 2;
+    t.emb = (t.emb >= 2 && small_full) ? 2 : 1;
+  } else {
     t.smb = env_int("MLORA_SHRINK_MB", t.smb) >= 2 ? 2 : 1;
-    t.emb = expand_mb(R, env_int("MLORA_EXPAND_MB", 1));
-    t.cw = expand_cw(R, env_int("MLORA_EXPAND_CW", 4));
   }
   t.sunits = (rows + 16 * t.smb - 1) / (16 * t.smb);
   t.etiles = (rows + 16 * t.emb - 1) / (16 * t.emb);
@@ -2307,31 +2310,35 @@ TwoPlan two_plan(int R, int N, int64_t rows, bool fixed) {
   return t;
 }
 
-template <int NB, int SMB, int CW, bool FULL_R>
+template <int NB, int SMB, int EMB, int CW, bool FULL_R>
 void launch_pipe(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_pipe_kernel<NB, SMB, 1, CW, FULL_R>), dim3(grid), dim3(kThreads),
-                     0, s, ps, pe);
+  hipLaunchKernelGGL((grouped_pipe_kernel<NB, SMB, EMB, CW, FULL_R>), dim3(grid),
+                     dim3(kThreads), 0, s, ps, pe);
 }
 
-// The pipelined launches use the default shapes of two_plan(fixed = true).
+// The pipelined launches use the shapes of two_plan(pipe = true).
 template <int NB>
 void dispatch_pipe_nb(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipStream_t s,
-                      int cw) {
+                      int emb, int cw) {
   constexpr int SMB = NB <= 2 ? 2 : 1;
-  if (ps.R != 16 * NB) return launch_pipe<NB, SMB, 2, false>(ps, pe, grid, s);
+  if (ps.R != 16 * NB) return launch_pipe<NB, SMB, 1, 2, false>(ps, pe, grid, s);
   if constexpr (NB <= 2) {
-    if (cw >= 4) return launch_pipe<NB, SMB, 4, true>(ps, pe, grid, s);
+    if (emb >= 2) {
+      if (cw >= 4) return launch_pipe<NB, SMB, 2, 4, true>(ps, pe, grid, s);
+      return launch_pipe<NB, SMB, 2, 2, true>(ps, pe, grid, s);
+    }
+    if (cw >= 4) return launch_pipe<NB, SMB, 1, 4, true>(ps, pe, grid, s);
   }
-  launch_pipe<NB, SMB, 2, true>(ps, pe, grid, s);
+  launch_pipe<NB, SMB, 1, 2, true>(ps, pe, grid, s);
 }
 
 void dispatch_pipe(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipStream_t s,
-                   int cw) {
+                   int emb, int cw) {
   switch (kernel_nb(ps.R)) {
-    case 1: return dispatch_pipe_nb<1>(ps, pe, grid, s, cw);
-    case 2: return dispatch_pipe_nb<2>(ps, pe, grid, s, cw);
-    case 4: return dispatch_pipe_nb<4>(ps, pe, grid, s, cw);
-    default: return dispatch_pipe_nb<8>(ps, pe, grid, s, cw);
+    case 1: return dispatch_pipe_nb<1>(ps, pe, grid, s, emb, cw);
+    case 2: return dispatch_pipe_nb<2>(ps, pe, grid, s, emb, cw);
+    case 4: return dispatch_pipe_nb<4>(ps, pe, grid, s, emb, cw);
+    default: return dispatch_pipe_nb<8>(ps, pe, grid, s, emb, cw);
   }
 }
 
@@ -2612,7 +2619,8 @@ extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const
     }
     return a;
   };
-  const int cw = two_plan(R, N, win_rows, true).cw;
+  const TwoPlan plan = two_plan(R, N, win_rows, true);
+  const int cw = plan.cw, emb = plan.emb;
   int64_t nb = 0;
   GroupedArgs first = window(0, false, &nb);
   dispatch_shrink(first, (int)nb, s, two_plan(R, N, win_rows, true).smb);
@@ -2623,12 +2631,12 @@ extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const
     GroupedArgs pe = window(w - 1, true, &eb);
     pe.per_xcd = (int32_t)((eb + kXcds - 1) / kXcds);  // expand blocks per XCD
     const int64_t grid = sb + (int64_t)pe.per_xcd * kXcds;
-    dispatch_pipe(ps, pe, (int)grid, s, cw);
+    dispatch_pipe(ps, pe, (int)grid, s, emb, cw);
     if (int32_t rc = launched(who)) return rc;
   }
   int64_t lb = 0;
   GroupedArgs last = window(n_win - 1, true, &lb);
   last.per_xcd = (int32_t)((last.units + kXcds - 1) / kXcds);
-  dispatch_expand(last, last.per_xcd * kXcds, s, 1, cw);
+  dispatch_expand(last, last.per_xcd * kXcds, s, emb, cw);
   return launched(who);
 }

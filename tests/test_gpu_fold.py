@@ -548,3 +548,59 @@ def test_graph_replay_reads_routing_on_device():
     view.a_table = list(view.a_table)
     view.a_table[live_e] = 0
     check(view, from_torch(base), c.base, "graph replay, new routing")
+
+
+@pytest.mark.parametrize("form", ["grouped_all", "grouped_window", "gather_two"])
+def test_graph_replay_workspace_forms(form, monkeypatch):
+    """The workspace forms captured in a HIP graph: every replay (with eager
+    work and syncs between) equals the eager fold bit for bit, and a replay
+    after the map and one table cell are rewritten in place folds by the new
+    contents."""
+    _need_gpu()
+    from tests.device import DeviceCase, from_torch, to_torch
+    if form == "gather_two":
+        monkeypatch.setenv("MLORA_GATHER_TWO", "1")
+        monkeypatch.setenv("MLORA_GATHER_RESIDENT", "0")
+        c = workloads.make_gather_case(86, n_seq=40, padded_n=48, top_k=4, n_route=10,
+                                       k_in=1024, n_out=256, max_rank=32, n_adapted=8,
+                                       skip_seqs=3)
+        dev = DeviceCase(c, DEV)
+    else:
+        c = workloads.make_grouped_case(87, stream_lens=[150, 90, 61], top_k=4, n_route=12,
+                                        k_in=256, n_out=320, max_rank=32, routing="zipf",
+                                        n_unadapted=2, cap=300, stream_slot_values=[1, 1, 1])
+        dev = DeviceCase(c, DEV, pipelined=(form == "grouped_all"))
+        assert len(dev.windows) > 1
+    dev.workspace_for(getattr(dev, "windows", None))   # allocated before capture
+    pristine = to_torch(c.base, "bf16", DEV)
+    base = pristine.clone()
+    eager = dev.run()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            dev.fold(base)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        base.copy_(pristine)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_torch(base).view(np.uint8), eager.view(np.uint8))
+    rng = np.random.default_rng(88)
+    new_map = np.where(rng.random(dev.row_adapter.numel()) < 0.3, -1, 1).astype(np.int32)
+    dev.row_adapter.copy_(torch.from_numpy(new_map))
+    live_e = int(np.flatnonzero(dev.tables_host[1])[0])
+    dev.b_table[live_e] = 0
+    base.copy_(pristine)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    view = OracleView(c)
+    view.row_adapter = new_map
+    view.b_table = list(view.b_table)
+    view.b_table[live_e] = 0
+    check(view, from_torch(base), c.base, f"{form} graph replay, new map and table")
+
