@@ -29,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -267,26 +268,57 @@ def _mean_counter(rows, counter, match):
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
+def _tables_and_map(case):
+    """Host tables (fake nonzero addresses stand in for the device weights; only
+    which cells are null matters here) and the row map of a workload, from the
+    library's host functions."""
+    import moe_expert_lora_amd as ml
+    import workloads
+    ids = np.array([e for (e, _, _, _) in case.entries], dtype=np.int32)
+    a = np.array([0 if h == workloads.NULL_HANDLE else 16 * (h + 1)
+                  for (_, h, _, _) in case.entries], dtype=np.uint64)
+    b = np.array([0 if h == workloads.NULL_HANDLE else 16 * (h + 1)
+                  for (_, _, h, _) in case.entries], dtype=np.uint64)
+    sc = np.array([s for (_, _, _, s) in case.entries], dtype=np.float32)
+    packed = ml.mlora_pack_expert_tables(ids, a, b, sc)
+    tables = packed if packed is not None else (np.zeros(0, np.uint64), np.zeros(0, np.uint64),
+                                                 np.zeros(0, np.float32), 0)
+    if case.map_kind == "decode":
+        ra = ml.mlora_build_moe_row_adapter_decode(case.adapter_slots, case.padded_n,
+                                                   case.active, case.has_moe_lora)
+    else:
+        ra = ml.mlora_build_moe_row_adapter_host(case.cu_seqlens, case.stream_slots)
+    full = np.full(max(case.n_tokens, ra.shape[0]), -1, dtype=np.int32)
+    full[: ra.shape[0]] = ra
+    return tables, full
+
+
 def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
-    """Per-launch HBM bytes of the fold kernel from FETCH_SIZE / WRITE_SIZE runs
-    (KiB per dispatch), each scaled by what the counter reads for the plain copy
-    of CALIB_BYTES; recorded in profiles/traffic.json with the kernel hash."""
-    # a fold call is one kernel (gather decode, one-kernel forms) or a shrink
-    # and an expand kernel: the per-call figure sums the per-dispatch means of
-    # every fold kernel the runs saw
+    """Per-launch HBM bytes of the fold from FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the counter reads for the plain copy of
+    CALIB_BYTES; recorded in profiles/traffic.json with the kernel hash.
+
+    A step is one or more fold kernels (a shrink and an expand; the pipelined
+    grouped call adds one launch per later window). Every kernel runs at least
+    once per step, so the least frequent one counts the steps, and the
+    per-launch figure is the counters summed over all fold dispatches divided
+    by steps x launches per step (windows, for grouped workloads)."""
     is_copy = lambda n: "mlora" not in n  # noqa: E731
     rows_f, rows_w = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     names = sorted({r["Kernel_Name"] for r in rows_f + rows_w if "mlora" in r["Kernel_Name"]})
-    f_kib = w_kib = 0.0
-    nf, nw = [], []
-    for name in names:
-        same = lambda n, name=name: n == name  # noqa: E731
-        a, na = _mean_counter(rows_f, "FETCH_SIZE", same)
-        b, nb = _mean_counter(rows_w, "WRITE_SIZE", same)
-        f_kib += a or 0.0
-        w_kib += b or 0.0
-        nf.append(na)
-        nw.append(nb)
+    import workloads
+    case = workloads.CONFIGS[workload]()
+    launches = algorithmic_traffic(case, *_tables_and_map(case))[4]
+
+    def per_launch(rows, counter):
+        vals = {n: [float(r["Counter_Value"]) for r in rows
+                    if r["Counter_Name"] == counter and r["Kernel_Name"] == n] for n in names}
+        steps = min(len(v) for v in vals.values())
+        total = sum(sum(v) for v in vals.values())
+        return total / (steps * launches), [len(v) for v in vals.values()]
+
+    f_kib, nf = per_launch(rows_f, "FETCH_SIZE")
+    w_kib, nw = per_launch(rows_w, "WRITE_SIZE")
     cal_rows_f = _pmc_rows(cal_fetch_dir)
     cal_rows_w = _pmc_rows(cal_write_dir)
     # the copy dispatch is the largest FETCH_SIZE / WRITE_SIZE in the calibration runs
@@ -299,8 +331,10 @@ def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     rec = {
         "kernel_sha256_16": kernel_hash(),
         "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
-        "kernels": [n.split("(")[0] for n in names],
+        "kernels": [re.sub(r"\(mlora::.*$", "", n.replace("void mlora::(anonymous namespace)::", ""))
+                    for n in names],
         "dispatches": [nf, nw],
+        "launches_per_step": launches,
         "copy_scale_fetch": kf, "copy_scale_write": kw,
         "hbm_bytes_per_launch": f_kib * 1024.0 * kf + w_kib * 1024.0 * kw,
     }
