@@ -1002,9 +1002,10 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(GatherArgs p) {
 // ---------------------------------------------------------------------------
 
 // When a wave's whole share of A_e (its k steps) and of B_e (its column steps)
-// fits in registers, both are requested together with the routing scan,
-// before any row is known; after the scan only x and base_out are loaded.
-// One 16-row block per chunk; the weights serve every chunk of the slice.
+// fits in registers, A_e is requested together with the routing scan, before
+// any row is known, and B_e right after the first chunk's x and base_out
+// rows. One 16-row block per chunk; the weights serve every chunk of the
+// slice.
 constexpr int kResSteps = 8;  // k steps, and column steps, per wave
 
 template <int NB, bool FULL_R>
@@ -1060,7 +1061,10 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p)
   bf.b = make_buf(reinterpret_cast<const void*>(b_addr), (uint32_t)(N * R) * 2u);
   bf.out = make_buf(p.out, p.out_bytes);
 
-  // the wave's weights
+  // The wave's weights. A_e is requested now, with the routing; B_e only
+  // after the first chunk's x and base_out rows: it is not needed before the
+  // shrink is done, and requesting it here would hold up the scan behind
+  // three times as many loads.
   u32x4 av[kResSteps][NB];
 #pragma unroll
   for (int u = 0; u < kResSteps; ++u) {
@@ -1074,11 +1078,6 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p)
     }
   }
   BFrag<NB> bw[kResSteps];
-#pragma unroll
-  for (int u = 0; u < kResSteps; ++u) {
-    const int cs = wave + u * kWaves;
-    load_bfrag<NB, FULL_R>(bw[u], bf.b, R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li, g);
-  }
 
   if (threadIdx.x == 0) s_cnt = 0;
   lds_barrier();
@@ -1097,7 +1096,7 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p)
   // expand and store. The first chunk runs outside the loop: a loop header
   // merges the load counts of the paths that reach it and would make the
   // chunk's loads wait for the weight loads still in flight.
-  auto chunk = [&](int c) {
+  auto chunk = [&](int c, bool first) {
     const int m = c + li;
     int t = -1, r = 0;
     if (m < n) {
@@ -1119,6 +1118,14 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p)
       const int cs = wave + u * kWaves;
       const int col = n_lo + cs * kColStep + 8 * g;
       ov[u] = bld16(bf.out, (valid && cs < ncs && col < n_hi) ? ooff + 2u * col : kOOB);
+    }
+    if (first) {
+#pragma unroll
+      for (int u = 0; u < kResSteps; ++u) {
+        const int cs = wave + u * kWaves;
+        load_bfrag<NB, FULL_R>(bw[u], bf.b, R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li,
+                               g);
+      }
     }
     // shrink
     f32x4 hacc[NB];
@@ -1177,8 +1184,8 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p)
     }
     lds_barrier();  // s_part is rewritten by the next chunk
   };
-  if (n > 0) chunk(0);
-  for (int c = 16; c < n; c += 16) chunk(c);
+  if (n > 0) chunk(0, true);
+  for (int c = 16; c < n; c += 16) chunk(c, false);
 }
 
 // ---------------------------------------------------------------------------
