@@ -1670,8 +1670,18 @@ __device__ __forceinline__ void grouped_expand_unit(const GroupedArgs& p, int u,
   const rsrc_t r_meta = make_buf(p.ws_meta, p.ws_meta_bytes);
 
   // Everything addressed by row alone is requested before the rows' meta is
-  // known: base_out (row-contiguous), H' (one lane per row) and the meta.
-  // Rows past the window lie past all three buffers and read as 0.
+  // known, in the order it is needed: the meta (which gates the B_e
+  // requests), H' (one lane per row), then base_out (row-contiguous, needed
+  // last). Waits count loads in issue order, so the meta's wait covers the
+  // meta alone. Rows past the window lie past all three buffers and read as 0.
+  const u32x2 mv = bld8(r_meta, lane < kRows ? (uint32_t)(r0 + lane) * 8u : kOOB);
+  HOp<NB> hop[MB];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    const uint32_t hoff = (uint32_t)(r0 + rb * 16 + li) * kRowBytes + (uint32_t)g * 8u * NB;
+    load_half<NB>(r_h, true, hoff, hop[rb].hi);
+    load_half<NB>(r_h, true, hoff + 32u * NB, hop[rb].lo);
+  }
   const int cr = lane / LPR, cc = lane % LPR;
   u32x4 bv[NI];
   uint32_t boff[NI];
@@ -1681,14 +1691,8 @@ __device__ __forceinline__ void grouped_expand_unit(const GroupedArgs& p, int u,
     boff[i] = (uint32_t)(r0 + i * RPI + cr) * (uint32_t)p.N * 2u + 2u * col;
     bv[i] = bld16_nt(r_out, col < n_hi ? boff[i] : kOOB);
   }
-  HOp<NB> hop[MB];
-#pragma unroll
-  for (int rb = 0; rb < MB; ++rb) {
-    const uint32_t hoff = (uint32_t)(r0 + rb * 16 + li) * kRowBytes + (uint32_t)g * 8u * NB;
-    load_half<NB>(r_h, true, hoff, hop[rb].hi);
-    load_half<NB>(r_h, true, hoff + 32u * NB, hop[rb].lo);
-  }
-  const u32x2 mv = bld8(r_meta, lane < kRows ? (uint32_t)(r0 + lane) * 8u : kOOB);
+  // keep all three requests ahead of the meta's first use
+  __builtin_amdgcn_sched_barrier(0);
   const bool is_live = (mv.x | mv.y) != 0;
   const uint64_t live = __ballot(is_live);
   if (live == 0) return;
