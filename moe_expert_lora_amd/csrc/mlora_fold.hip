@@ -747,9 +747,11 @@ __device__ __forceinline__ int finish_scan(const GatherArgs& p, int e, int start
 constexpr int kTwoSteps = 4;
 
 // Shrink: one workgroup per (expert, row slice, k range of at most
-// kWaves * kTwoSteps k steps). The range's A_e fragments are requested with
-// the routing, before any row is known; after the scan only x is loaded. The
-// waves split the range's k steps; their sums meet in LDS in a fixed order.
+// kWaves * kTwoSteps k steps). After the routing scan the first row block's
+// x fragments are requested, then the range's A_e fragments (loaded once,
+// used by every block): the small dependent loads go first, the bulk last.
+// The waves split the range's k steps; their sums meet in LDS in a fixed
+// order.
 template <int NB, int MB>
 __global__ __launch_bounds__(kThreads) void gather_shrink_kernel(GatherArgs p) {
   constexpr int HW = 4 * NB;
@@ -797,22 +799,23 @@ __global__ __launch_bounds__(kThreads) void gather_shrink_kernel(GatherArgs p) {
       }
     }
   };
-  request_a();
   const int n = finish_scan(p, e, start, end, sl, s_rows, s_toks, &s_cnt);
   const uint32_t plane = (uint32_t)kc * (uint32_t)p.n_slots;
 
-  auto block = [&](int c) {
+  auto block = [&](int c, bool first) {
     const int nrows = min(16 * MB, n - c), nrb = (nrows + 15) >> 4;
     const Rows<MB> rw = rows_of<MB>(K, p.N, s_rows + c, 0, s_toks + c, nrows, li);
     u32x4 xv[kTwoSteps][MB];
 #pragma unroll
     for (int t = 0; t < kTwoSteps; ++t) {
-      const int k0 = step[t] * 32 + g * 8;
-      const bool kin = step[t] < s_end && k0 < K;
+      const int k0 = (kc * p.kc_steps + wave + t * kWaves) * 32 + g * 8;
+      const bool kin = kc * p.kc_steps + wave + t * kWaves < s_end && k0 < K;
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb)
         xv[t][rb] = bld16(r_x, (kin && rw.valid[rb]) ? rw.xoff[rb] + 2u * k0 : kOOB);
     }
+    if (first) request_a();
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 hacc[MB][NB];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
@@ -862,15 +865,15 @@ __global__ __launch_bounds__(kThreads) void gather_shrink_kernel(GatherArgs p) {
     lds_barrier();  // s_part is rewritten by the next block
   };
   // the first block runs outside the loop (see the resident gather kernel)
-  if (n > 0) block(0);
-  for (int c = 16 * MB; c < n; c += 16 * MB) block(c);
+  if (n > 0) block(0, true);
+  for (int c = 16 * MB; c < n; c += 16 * MB) block(c, false);
 }
 
 // Expand: one workgroup per (expert, row slice, column slice of at most
-// kWaves * kTwoSteps column steps). The slice's B_e fragments are requested
-// with the routing; after the scan, the rows' partial H (summed over the k
-// ranges in order, scaled and split into hi / lo as in the one-kernel form)
-// and base_out fragments.
+// kWaves * kTwoSteps column steps). After the routing scan: the rows' partial
+// H (summed over the k ranges in order, scaled and split into hi / lo as in
+// the one-kernel form) and base_out fragments, then the slice's B_e
+// fragments (loaded once, used by every block).
 constexpr int kMaxKc = 4;
 
 template <int NB, int MB, bool FULL_R>
@@ -913,11 +916,10 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(GatherArgs p) {
       load_bfrag<NB, FULL_R>(bw[t], r_b, p.R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li, g);
     }
   };
-  request_b();
   const int n = finish_scan(p, e, start, end, sl, s_rows, s_toks, &s_cnt);
   const int kcs = p.kc_count;
 
-  auto block = [&](int c) {
+  auto block = [&](int c, bool first) {
     const int nrows = min(16 * MB, n - c), nrb = (nrows + 15) >> 4;
     const Rows<MB> rw = rows_of<MB>(p.K, p.N, s_rows + c, 0, s_toks + c, nrows, li);
     // partial sums of every k range and the base_out fragments, requested together
@@ -944,6 +946,8 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(GatherArgs p) {
       for (int rb = 0; rb < MB; ++rb)
         ov[t][rb] = bld16(r_out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
     }
+    if (first) request_b();
+    __builtin_amdgcn_sched_barrier(0);
     HOp<NB> hop[MB];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
@@ -993,8 +997,8 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(GatherArgs p) {
       }
     }
   };
-  if (n > 0) block(0);
-  for (int c = 16 * MB; c < n; c += 16 * MB) block(c);
+  if (n > 0) block(0, true);
+  for (int c = 16 * MB; c < n; c += 16 * MB) block(c, false);
 }
 
 // ---------------------------------------------------------------------------
