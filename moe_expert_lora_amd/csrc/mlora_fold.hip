@@ -548,41 +548,20 @@ __device__ void fold_rows(const Bufs& bf, int K, int N, int R, float scale, cons
   const int nrb = (nrows + 15) >> 4;
   const Rows<MB> rw = rows_of<MB>(K, N, s_row, row_base, s_tok, nrows, li);
 
-  // The first expand batch does not depend on the shrink: request it now so
-  // its latency hides behind the shrink.
+  // The first expand batch is requested once the shrink's loads are in and
+  // multiplied, so the shrink's loads never queue behind it; the reduction
+  // below covers part of its latency.
   const int ncs = (n_hi - n_lo + kColStep - 1) / kColStep;
   ExpandBatch<NB, MB, UE> e0;
-  load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, wave, ncs, n_lo, n_hi, li, g);
 
   f32x4 hacc[MB][NB];
   shrink_k<NB, MB>(hacc, bf, K, R, rw, nrb, wave, li, g);
+  load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, wave, ncs, n_lo, n_hi, li, g);
   HOp<NB> hop[MB];
   reduce_split<NB, MB>(hacc, s_part, scale, nrb, wave, lane, hop);
   expand_rows<NB, MB, FULL_R>(bf, R, rw, hop, nrb, n_lo, n_hi, wave, li, g, e0);
   // s_part and the caller's row lists are reused by the next call.
   lds_barrier();
-}
-
-// Requests the cache lines of `bytes` bytes of buffer `r` (one 4-byte load per
-// 128-byte line, NT lines per thread) so that HBM fetches of an expert's
-// weights start while the workgroup is still resolving its rows. Loads past
-// the buffer return 0 without touching memory. The loaded words are kept, and
-// consumed by an empty asm at the end of the kernel, only so the loads are not
-// removed; no wave waits for them earlier.
-template <int NT>
-__device__ __forceinline__ void touch_lines(rsrc_t r, uint32_t first_byte, uint32_t bytes,
-                                            uint32_t (&keep)[NT]) {
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const uint32_t off = ((uint32_t)i * kThreads + threadIdx.x) * 128u;
-    keep[i] = bld4(r, off < bytes ? first_byte + off : kOOB);
-  }
-}
-
-template <int NT>
-__device__ __forceinline__ void consume(const uint32_t (&keep)[NT]) {
-#pragma unroll
-  for (int i = 0; i < NT; ++i) asm volatile("" ::"v"(keep[i]));
 }
 
 // ---------------------------------------------------------------------------
@@ -660,10 +639,7 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
   bf.a = make_buf(reinterpret_cast<const void*>(a_addr), (uint32_t)(p.R * p.K) * 2u);
   bf.b = make_buf(reinterpret_cast<const void*>(b_addr), (uint32_t)(p.N * p.R) * 2u);
   bf.out = make_buf(p.out, p.out_bytes);
-  // Start the HBM fetch of this slice's weights while the rows are resolved.
-  uint32_t keep_a[2], keep_b[2];
-  touch_lines(bf.a, 0u, (uint32_t)(p.R * p.K) * 2u, keep_a);
-  touch_lines(bf.b, (uint32_t)(n_lo * p.R) * 2u, (uint32_t)((n_hi - n_lo) * p.R) * 2u, keep_b);
+
 
   if (threadIdx.x == 0) s_cnt = 0;
   lds_barrier();
@@ -685,8 +661,7 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
   for (int c = 16 * MB; c < n; c += 16 * MB)
     fold_rows<NB, MB, FULL_R>(bf, p.K, p.N, p.R, scale, s_rows + c, 0, s_toks + c,
                               min(16 * MB, n - c), n_lo, n_hi, s_part);
-  consume(keep_a);
-  consume(keep_b);
+
 }
 
 
