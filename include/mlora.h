@@ -238,13 +238,16 @@ int32_t mlora_grouped_down(const mlora_expert_route* route, const void* x, int64
  * Grouped fold of every sorted row, window by window: the windows are those of
  * mlora_grouped_down_windows(n_rows, cap), and the result equals calling
  * mlora_grouped_down on each of them in order with a workspace, bit for bit
- * (rows are independent). The windows are pipelined: one launch expands
- * window w while it shrinks window w + 1, so a window's shrink overlaps the
- * previous window's base_out traffic. Arguments as for mlora_grouped_down;
- * cap <= 0 -> MLORA_ERR_INVALID [P2 grouped_down_windows]. The workspace is
- * required for bf16 (two window slots, see the size query below; NULL or too
- * small -> MLORA_ERR_CAPACITY, nothing enqueued); an f32 route folds the
- * windows one by one without it.
+ * (rows are independent). Consecutive windows are launched together, in
+ * launches of whole windows holding at least 16384 rows (the environment
+ * variable MLORA_ALL_MIN_ROWS sets another minimum; 1 launches one window at
+ * a time), and the launches are pipelined: one kernel expands launch l's rows
+ * while it shrinks launch l + 1's, so a shrink overlaps the previous rows'
+ * base_out traffic. Arguments as for mlora_grouped_down; cap <= 0 ->
+ * MLORA_ERR_INVALID [P2 grouped_down_windows]. The workspace is required for
+ * bf16 (two launch slots, see the size query below; NULL or too small ->
+ * MLORA_ERR_CAPACITY, nothing enqueued); an f32 route folds the windows one
+ * by one without it.
  */
 int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x, int64_t n_tokens,
                                void* base_out, int64_t n_rows, const int32_t* expert_offsets,
@@ -252,10 +255,11 @@ int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x, i
                                const int32_t* row_adapter, int32_t top_k, int64_t cap,
                                void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* Bytes of workspace mlora_grouped_down_all needs: one window slot (the
- * mlora_grouped_down_workspace_bytes of a window of min(cap, n_rows) rows,
- * rounded up to 256) when there is one window, two slots otherwise. 0 for
- * n_rows <= 0, cap <= 0 or max_rank outside [1, 128]. */
+/* Bytes of workspace mlora_grouped_down_all needs: one launch slot (the
+ * mlora_grouped_down_workspace_bytes of L = min(n_rows, cap * ceil(m / cap))
+ * rows, m the launch minimum above, rounded up to 256) when L covers every
+ * row, two slots otherwise. Read the size under the same MLORA_ALL_MIN_ROWS
+ * as the call. 0 for n_rows <= 0, cap <= 0 or max_rank outside [1, 128]. */
 uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap, int32_t max_rank);
 
 /* Bytes of workspace mlora_grouped_down needs for its two-kernel form on the

@@ -2283,13 +2283,15 @@ struct TwoPlan {
 
 TwoPlan two_plan(int R, int N, int64_t rows, bool pipe) {
   TwoPlan t;
+  // two expand row blocks per wave share each B_e fragment where the rank
+  // blocks are full and at most 32 ranks (measured 4% faster per window)
+  const bool small_full = R == 16 * kernel_nb(R) && kernel_nb(R) <= 2;
   t.smb = kernel_nb(R) <= 2 ? 2 : 1;
-  t.emb = expand_mb(R, env_int("MLORA_EXPAND_MB", 1));
+  t.emb = expand_mb(R, env_int("MLORA_EXPAND_MB", small_full ? 2 : 1));
   t.cw = expand_cw(R, env_int("MLORA_EXPAND_CW", 4));
   if (pipe) {
     // the pipe kernel takes 1 expand row block, or 2 for full rank blocks of
     // at most 32 ranks, and always its default shrink tile
-    const bool small_full = R == 16 * kernel_nb(R) && kernel_nb(R) <= 2;
     t.emb = (t.emb >= 2 && small_full) ? 2 : 1;
   } else {
     t.smb = env_int("MLORA_SHRINK_MB", t.smb) >= 2 ? 2 : 1;
@@ -2333,8 +2335,22 @@ void dispatch_pipe(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipSt
 }
 
 // Workspace of one window slot of the pipelined call.
-int64_t pipe_slot_bytes(int64_t n_rows, int64_t cap, int R) {
-  const int64_t rows = n_rows < cap ? n_rows : cap;
+// Rows per launch of the all-windows call: whole windows, at least
+// kAllMinRows of them (MLORA_ALL_MIN_ROWS overrides). Fewer, larger launches
+// pay less launch and drain time than their shorter pipeline hides (measured
+// on 8192-row windows of the prefill down projection: 2 launches of 16384
+// rows beat 4 of 8192 by 10%).
+constexpr int64_t kAllMinRows = 16384;
+
+int64_t all_chunk_rows(int64_t n_rows, int64_t cap) {
+  int64_t min_rows = env_int("MLORA_ALL_MIN_ROWS", (int)kAllMinRows);
+  if (min_rows < 1) min_rows = 1;
+  const int64_t m = cap >= min_rows ? 1 : (min_rows + cap - 1) / cap;
+  const int64_t chunk = m > 1 ? cap * m : cap;  // m > 1 only for cap < min_rows
+  return chunk < n_rows ? chunk : n_rows;
+}
+
+int64_t pipe_slot_bytes(int64_t rows, int R) {
   return (grouped_ws_layout(rows, R).total + 255) & ~(int64_t)255;
 }
 
@@ -2446,25 +2462,19 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
     a.ws_meta = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + w.meta_off);
     a.ws_h_bytes = (uint32_t)w.h_bytes;
     a.ws_meta_bytes = (uint32_t)w.meta_bytes;
-    // shrink: one workgroup per 16 * smb rows
-    int smb = env_int("MLORA_SHRINK_MB", kernel_nb(R) <= 2 ? 2 : 1);
-    smb = smb >= 2 ? 2 : 1;
-    const int64_t sunits = (rows + 16 * smb - 1) / (16 * smb);
-    // expand: one wave per (16 * emb rows, cw column steps)
-    const int emb = expand_mb(R, env_int("MLORA_EXPAND_MB", 1));
-    const int cw = expand_cw(R, env_int("MLORA_EXPAND_CW", 4));
-    const int64_t etiles = (rows + 16 * emb - 1) / (16 * emb);
-    const int64_t eslices = (N + cw * kColStep - 1) / (cw * kColStep);
-    if (sunits > 0x3fffffffll || etiles * eslices > 0x3fffffffll)
+    // shrink: one workgroup per 16 * smb rows; expand: one wave per
+    // (16 * emb rows, cw column steps)
+    const TwoPlan t = two_plan(R, N, rows, false);
+    if (t.sunits > 0x3fffffffll || t.etiles * t.eslices > 0x3fffffffll)
       return fail(MLORA_ERR_INVALID, "%s: window too large", who);
-    a.units = (int32_t)sunits;
-    a.per_xcd = (int32_t)((sunits + kXcds - 1) / kXcds);
-    dispatch_shrink(a, a.per_xcd * kXcds, s, smb);
+    a.units = (int32_t)t.sunits;
+    a.per_xcd = (int32_t)((t.sunits + kXcds - 1) / kXcds);
+    dispatch_shrink(a, a.per_xcd * kXcds, s, t.smb);
     if (int32_t rc = launched(who)) return rc;
-    a.ns_count = (int32_t)eslices;
-    a.units = (int32_t)(etiles * eslices);
+    a.ns_count = (int32_t)t.eslices;
+    a.units = (int32_t)(t.etiles * t.eslices);
     a.per_xcd = (int32_t)((a.units + kXcds - 1) / kXcds);
-    dispatch_expand(a, a.per_xcd * kXcds, s, emb, cw);
+    dispatch_expand(a, a.per_xcd * kXcds, s, t.emb, t.cw);
     return launched(who);
   }
 
@@ -2504,8 +2514,9 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
 extern "C" uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap,
                                                            int32_t max_rank) {
   if (n_rows <= 0 || cap <= 0 || max_rank < 1 || max_rank > 128) return 0;
-  const int64_t slots = n_rows > cap ? 2 : 1;
-  return (uint64_t)(slots * pipe_slot_bytes(n_rows, cap, max_rank));
+  const int64_t chunk = all_chunk_rows(n_rows, cap);
+  const int64_t slots = n_rows > chunk ? 2 : 1;
+  return (uint64_t)(slots * pipe_slot_bytes(chunk, max_rank));
 }
 
 extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x,
@@ -2532,9 +2543,14 @@ extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const
   }
   if (!x || !base_out || !expert_offsets || !sorted_ids || !row_adapter)
     return fail(MLORA_ERR_INVALID, "%s: NULL device pointer", who);
-  const int64_t n_win = (n_rows + cap - 1) / cap;
   const int R = route->max_rank, N = route->n_out, K = route->k_in;
-  const int64_t slot = pipe_slot_bytes(n_rows, cap, R);
+  // launches of whole windows; back to one window per launch where a larger
+  // launch would pass the 4 GiB buffer range
+  int64_t chunk = all_chunk_rows(n_rows, cap);
+  if (chunk > cap && chunk > (int64_t)kMaxBufBytes / (2 * (int64_t)N))
+    chunk = cap < n_rows ? cap : n_rows;
+  const int64_t n_win = (n_rows + chunk - 1) / chunk;
+  const int64_t slot = pipe_slot_bytes(chunk, R);
   const int64_t need = (n_win > 1 ? 2 : 1) * slot;
   if (route->dtype == MLORA_BF16 && (!workspace || (uint64_t)need > workspace_bytes))
     return fail(MLORA_ERR_CAPACITY, "%s: workspace of %llu bytes, %lld needed", who,
@@ -2544,7 +2560,8 @@ extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const
 
   if (route->dtype == MLORA_F32) {
     // the plain row-wise kernel has no windows to pipeline: one launch per window
-    for (int64_t w = 0; w < n_win; ++w) {
+    const int64_t n_cap = (n_rows + cap - 1) / cap;
+    for (int64_t w = 0; w < n_cap; ++w) {
       const int64_t r0 = w * cap, r1 = r0 + cap < n_rows ? r0 + cap : n_rows;
       if (int32_t rc = mlora_grouped_down(route, x, n_tokens, base_out, n_rows, expert_offsets,
                                           n_route, sorted_ids, row_adapter, top_k, r0, r1,
@@ -2558,7 +2575,7 @@ extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const
   if (!aligned16(x) || !aligned16(base_out))
     return fail(MLORA_ERR_INVALID, "%s: x and base_out must be 16-byte aligned", who);
   const int64_t x_bytes = n_tokens * K * 2;
-  const int64_t win_rows = n_rows < cap ? n_rows : cap;
+  const int64_t win_rows = chunk;
   const WsLayout wl = grouped_ws_layout(win_rows, R);
   if (x_bytes > (int64_t)kMaxBufBytes || win_rows * N * 2 > (int64_t)kMaxBufBytes ||
       wl.h_bytes > (int64_t)kMaxBufBytes || wl.meta_bytes > (int64_t)kMaxBufBytes ||
@@ -2570,7 +2587,7 @@ extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const
   // the expand launch fields
   auto window = [&](int64_t w, bool expand, int64_t* blocks) {
     GroupedArgs a{};
-    const int64_t r0 = w * cap, r1 = r0 + cap < n_rows ? r0 + cap : n_rows;
+    const int64_t r0 = w * chunk, r1 = r0 + chunk < n_rows ? r0 + chunk : n_rows;
     const WsLayout l = grouped_ws_layout(r1 - r0, R);
     uint8_t* base = static_cast<uint8_t*>(workspace) + (w % 2) * slot;
     a.x = static_cast<const uint16_t*>(x);

@@ -392,11 +392,15 @@ def test_gather_two_kernel_form(label, monkeypatch):
     assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
 
 
+@pytest.mark.parametrize("min_rows", [None, "1"], ids=["launch16k", "launch1win"])
 @pytest.mark.parametrize("label", ["cfg3", "cfg5b"] + [s[0] for s in GROUPED_SMALL])
-def test_grouped_all_windows_pipelined_equals_per_window(label):
-    """mlora_grouped_down_all (window w + 1 shrunk in the launch that expands
-    window w) equals one mlora_grouped_down call per window, bit for bit."""
+def test_grouped_all_windows_pipelined_equals_per_window(label, min_rows, monkeypatch):
+    """mlora_grouped_down_all (launch l + 1's windows shrunk in the launch that
+    expands launch l's) equals one mlora_grouped_down call per window, bit for
+    bit, with launches of >= 16384 rows (the default) and of one window."""
     _need_gpu()
+    if min_rows:
+        monkeypatch.setenv("MLORA_ALL_MIN_ROWS", min_rows)
     from tests.device import DeviceCase
     if label.startswith("cfg"):
         case, view, dev = staged(label)
@@ -408,9 +412,13 @@ def test_grouped_all_windows_pipelined_equals_per_window(label):
     assert np.array_equal(per_window.view(np.uint8), pipelined.view(np.uint8))
 
 
-def test_grouped_all_many_small_windows():
-    """Many windows (cap 40 over 1203 rows): both workspace slots alternate."""
+@pytest.mark.parametrize("min_rows", ["1", "120", None])
+def test_grouped_all_many_small_windows(min_rows, monkeypatch):
+    """Many windows (cap 40 over 1203 rows), launched one window at a time,
+    three windows at a time, or all at once: both workspace slots alternate."""
     _need_gpu()
+    if min_rows:
+        monkeypatch.setenv("MLORA_ALL_MIN_ROWS", min_rows)
     from tests.device import DeviceCase
     case = workloads.make_grouped_case(95, stream_lens=[200, 101], top_k=4, n_route=9,
                                        k_in=320, n_out=264, max_rank=24, routing="zipf",

@@ -321,10 +321,25 @@ def test_grouped_all_rejects_bad_args(lib):
 
 def test_grouped_all_workspace_bytes(lib):
     f, g = lib.mlora_grouped_down_all_workspace_bytes, lib.mlora_grouped_down_workspace_bytes
-    assert f(32768, 8192, 32) == 2 * g(0, 8192, 32)
-    assert f(5000, 8192, 32) == g(0, 5000, 32)        # one window, one slot
-    assert f(100, 30, 100) == 2 * g(0, 30, 100)
+    # a launch covers whole windows, at least 16384 rows of them; two slots
+    # when there is more than one launch
+    assert f(32768, 8192, 32) == 2 * g(0, 16384, 32)
+    assert f(16384, 8192, 16) == g(0, 16384, 16)      # one launch, one slot
+    assert f(40000, 8192, 16) == 2 * g(0, 16384, 16)
+    assert f(5000, 8192, 32) == g(0, 5000, 32)
+    assert f(100, 30, 100) == g(0, 100, 100)          # 547 windows of 30 > 100 rows
+    assert f(70000, 6000, 16) == 2 * g(0, 18000, 16)  # three windows per launch
+    assert f(100000, 20000, 16) == 2 * g(0, 20000, 16)
     assert f(0, 10, 16) == 0 and f(10, 0, 16) == 0 and f(10, 10, 0) == 0
+
+
+def test_grouped_all_workspace_bytes_window_per_launch(lib, monkeypatch):
+    """MLORA_ALL_MIN_ROWS=1 launches one window at a time."""
+    monkeypatch.setenv("MLORA_ALL_MIN_ROWS", "1")
+    f, g = lib.mlora_grouped_down_all_workspace_bytes, lib.mlora_grouped_down_workspace_bytes
+    assert f(32768, 8192, 32) == 2 * g(0, 8192, 32)
+    assert f(100, 30, 100) == 2 * g(0, 30, 100)
+    assert f(30, 30, 100) == g(0, 30, 100)
 
 
 def test_gather_workspace_bytes(lib):
