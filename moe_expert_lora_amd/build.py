@@ -25,6 +25,9 @@ FLAGS = [
     "-Wall",
     # keep hipcc from forming packed fp32 VALU ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments that lead with plain pointers / ints arrive in SGPRs
+    # (the kernel keeps a prologue that loads them where firmware does not)
+    "-mllvm", "-amdgpu-kernarg-preload-count=10",
     "-I", INCLUDE,
 ]
 

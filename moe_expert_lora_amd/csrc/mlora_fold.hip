@@ -593,7 +593,10 @@ struct GatherArgs {
 };
 
 template <int NB, int MB, bool FULL_R>
-__global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
+__global__ __launch_bounds__(kThreads) void gather_fold_kernel(
+    const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
+    const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
+    GatherArgs p) {
   __shared__ float s_part[kWaves * MB * 64 * 4 * NB];
   __shared__ int s_rows[kScanMax];
   __shared__ int s_toks[kScanMax];
@@ -601,15 +604,14 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(GatherArgs p) {
 
   // XCD-aware unit: consecutive units (the slices of one expert) on one XCD.
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int u = xcd * p.per_xcd + slot;
-  if (u >= p.units) return;
-  const int per_e = p.rs_count * p.ns_count;
+  const int u = xcd * per_xcd + slot;
+  if (u >= units) return;
   const int e = u / per_e;
   const int within = u - e * per_e;
-  const int rs = within / p.ns_count, ns = within - rs * p.ns_count;
+  const int rs = within / inner, ns = within - rs * inner;
 
-  const uint64_t a_addr = uniform_u64(p.a_table[e]), b_addr = uniform_u64(p.b_table[e]);
-  const float scale = uniform_f32(p.scale_table[e]);
+  const uint64_t a_addr = uniform_u64(a_table[e]), b_addr = uniform_u64(b_table[e]);
+  const float scale = uniform_f32(scale_table[e]);
 
   // This slice's routing, requested together with the table cells.
   const rsrc_t r_idx = make_buf(p.indices, (uint32_t)p.n_slots * 4u);
@@ -728,7 +730,10 @@ constexpr int kTwoSteps = 4;
 // The waves split the range's k steps; their sums meet in LDS in a fixed
 // order.
 template <int NB, int MB>
-__global__ __launch_bounds__(kThreads) void gather_shrink_kernel(GatherArgs p) {
+__global__ __launch_bounds__(kThreads) void gather_shrink_kernel(
+    const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
+    const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
+    GatherArgs p) {
   constexpr int HW = 4 * NB;
   constexpr uint32_t kRowBytes = 64u * NB;  // RP fp32
   __shared__ float s_part[kWaves * MB * 64 * HW];
@@ -737,13 +742,13 @@ __global__ __launch_bounds__(kThreads) void gather_shrink_kernel(GatherArgs p) {
   __shared__ int s_cnt;
 
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int u = xcd * p.per_xcd + slot;
-  if (u >= p.units) return;
-  const int per_e = p.rs_count * p.kc_count;
+  const int u = xcd * per_xcd + slot;
+  if (u >= units) return;
   const int e = u / per_e;
   const int within = u - e * per_e;
-  const int rs = within / p.kc_count, kc = within - rs * p.kc_count;
-  const uint64_t a_addr = uniform_u64(p.a_table[e]), b_addr = uniform_u64(p.b_table[e]);
+  const int rs = within / inner, kc = within - rs * inner;
+  const uint64_t a_addr = uniform_u64(a_table[e]), b_addr = uniform_u64(b_table[e]);
+  (void)scale_table;
   const int start = rs * p.scan_len;
   const int end = min(start + p.scan_len, p.n_slots);
   ScanLoads sl;
@@ -852,7 +857,10 @@ __global__ __launch_bounds__(kThreads) void gather_shrink_kernel(GatherArgs p) {
 constexpr int kMaxKc = 4;
 
 template <int NB, int MB, bool FULL_R>
-__global__ __launch_bounds__(kThreads) void gather_expand_kernel(GatherArgs p) {
+__global__ __launch_bounds__(kThreads) void gather_expand_kernel(
+    const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
+    const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
+    GatherArgs p) {
   constexpr uint32_t kRowBytes = 64u * NB;
   constexpr int CC = Chunk<NB>::kCount;
   __shared__ int s_rows[kScanMax];
@@ -860,14 +868,13 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(GatherArgs p) {
   __shared__ int s_cnt;
 
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int u = xcd * p.per_xcd + slot;
-  if (u >= p.units) return;
-  const int per_e = p.rs_count * p.ns_count;
+  const int u = xcd * per_xcd + slot;
+  if (u >= units) return;
   const int e = u / per_e;
   const int within = u - e * per_e;
-  const int rs = within / p.ns_count, ns = within - rs * p.ns_count;
-  const uint64_t a_addr = uniform_u64(p.a_table[e]), b_addr = uniform_u64(p.b_table[e]);
-  const float scale = uniform_f32(p.scale_table[e]);
+  const int rs = within / inner, ns = within - rs * inner;
+  const uint64_t a_addr = uniform_u64(a_table[e]), b_addr = uniform_u64(b_table[e]);
+  const float scale = uniform_f32(scale_table[e]);
   const int start = rs * p.scan_len;
   const int end = min(start + p.scan_len, p.n_slots);
   ScanLoads sl;
@@ -987,8 +994,15 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(GatherArgs p) {
 // slice.
 constexpr int kResSteps = 8;  // k steps, and column steps, per wave
 
+// The table pointers and the unit arithmetic come first, as plain arguments:
+// the library is built with kernel-argument preloading, so they arrive in
+// SGPRs and the table-cell loads issue without waiting for the argument
+// block (measured 0.3 us per call on the decode down projection).
 template <int NB, bool FULL_R>
-__global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p) {
+__global__ __launch_bounds__(kThreads) void gather_resident_kernel(
+    const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
+    const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
+    GatherArgs p) {
   constexpr int HW = 4 * NB;
   __shared__ float s_part[kWaves * 64 * HW];
   __shared__ int s_rows[kScanMax];
@@ -996,15 +1010,14 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(GatherArgs p)
   __shared__ int s_cnt;
 
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int u0 = xcd * p.per_xcd + slot;
-  if (u0 >= p.units) return;
-  const int per_e = p.rs_count * p.ns_count;
+  const int u0 = xcd * per_xcd + slot;
+  if (u0 >= units) return;
   const int e = u0 / per_e;
   const int within = u0 - e * per_e;
-  const int rs = within / p.ns_count, ns = within - rs * p.ns_count;
+  const int rs = within / inner, ns = within - rs * inner;
 
-  const uint64_t a_addr = uniform_u64(p.a_table[e]), b_addr = uniform_u64(p.b_table[e]);
-  const float scale = uniform_f32(p.scale_table[e]);
+  const uint64_t a_addr = uniform_u64(a_table[e]), b_addr = uniform_u64(b_table[e]);
+  const float scale = uniform_f32(scale_table[e]);
 
   const rsrc_t r_idx = make_buf(p.indices, (uint32_t)p.n_slots * 4u);
   const rsrc_t r_map = make_buf(p.row_adapter, (uint32_t)p.n_tokens * 4u);
@@ -1880,12 +1893,21 @@ int ns_cols_for(int N, int ns) {
   return (per + kColStep - 1) / kColStep * kColStep;
 }
 
+// The leading plain arguments of the gather kernels (preloaded into SGPRs):
+// the tables and the unit arithmetic, `inner` being the sub-units per row
+// slice (column slices, or k ranges for the shrink).
+#define LEAD_ARGS(a, inner)                                                              \
+  (a).a_table, (a).b_table, (a).scale_table, (a).per_xcd, (a).units,                    \
+      (a).rs_count * (inner), (inner), (a)
+
 template <int NB, int MB>
 void launch_gather(const GatherArgs& a, int grid, hipStream_t s) {
   if (a.R == 16 * NB)
-    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, true>), dim3(grid), dim3(kThreads), 0, s,
+                       LEAD_ARGS(a, a.ns_count));
   else
-    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, false>), dim3(grid), dim3(kThreads), 0, s,
+                       LEAD_ARGS(a, a.ns_count));
 }
 
 // Rank blocks of 16 -> (NB, MB) instantiation. `small` picks one 16-row block
@@ -1929,13 +1951,13 @@ int gather_two_mb(int R, int64_t rows) {
 template <int NB, int MB>
 void launch_gather_two(const GatherArgs& g1, const GatherArgs& g2, hipStream_t s) {
   hipLaunchKernelGGL((gather_shrink_kernel<NB, MB>), dim3(g1.per_xcd * kXcds), dim3(kThreads), 0,
-                     s, g1);
+                     s, LEAD_ARGS(g1, g1.kc_count));
   if (g2.R == 16 * NB)
     hipLaunchKernelGGL((gather_expand_kernel<NB, MB, true>), dim3(g2.per_xcd * kXcds),
-                       dim3(kThreads), 0, s, g2);
+                       dim3(kThreads), 0, s, LEAD_ARGS(g2, g2.ns_count));
   else
     hipLaunchKernelGGL((gather_expand_kernel<NB, MB, false>), dim3(g2.per_xcd * kXcds),
-                       dim3(kThreads), 0, s, g2);
+                       dim3(kThreads), 0, s, LEAD_ARGS(g2, g2.ns_count));
 }
 
 template <int NB>
@@ -1958,19 +1980,21 @@ void dispatch_gather_two(const GatherArgs& g1, const GatherArgs& g2, hipStream_t
   }
 }
 
+template <int NB, bool FULL_R>
+void launch_resident(const GatherArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R>), dim3(grid), dim3(kThreads), 0, s,
+                     LEAD_ARGS(a, a.ns_count));
+}
+
 void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small, bool resident) {
   const int nb = (a.R + 15) / 16;
   if (resident && gather_resident_fits(a)) {
     if (nb <= 1) {
-      if (a.R == 16)
-        hipLaunchKernelGGL((gather_resident_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((gather_resident_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, a);
+      if (a.R == 16) launch_resident<1, true>(a, grid, s);
+      else launch_resident<1, false>(a, grid, s);
     } else {
-      if (a.R == 32)
-        hipLaunchKernelGGL((gather_resident_kernel<2, true>), dim3(grid), dim3(kThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((gather_resident_kernel<2, false>), dim3(grid), dim3(kThreads), 0, s, a);
+      if (a.R == 32) launch_resident<2, true>(a, grid, s);
+      else launch_resident<2, false>(a, grid, s);
     }
     return;
   }
