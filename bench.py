@@ -299,7 +299,7 @@ def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     CALIB_BYTES; recorded in profiles/traffic.json with the kernel hash.
 
     A step is one or more fold kernels (a shrink and an expand; the pipelined
-    grouped call adds one launch per later window). Every kernel runs at least
+    grouped call adds one launch per later group of windows). Every kernel runs at least
     once per step, so the least frequent one counts the steps, and the
     per-launch figure is the counters summed over all fold dispatches divided
     by steps x launches per step (windows, for grouped workloads)."""
@@ -331,7 +331,7 @@ def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     rec = {
         "kernel_sha256_16": kernel_hash(),
         "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
-        "kernels": [re.sub(r"\(mlora::.*$", "", n.replace("void mlora::(anonymous namespace)::", ""))
+        "kernels": [re.sub(r"(?<=>)\(.*$", "", n.replace("void mlora::(anonymous namespace)::", ""))
                     for n in names],
         "dispatches": [nf, nw],
         "launches_per_step": launches,

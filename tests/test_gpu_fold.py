@@ -333,6 +333,26 @@ def test_grouped_two_kernel_equals_one_kernel(label):
     assert np.array_equal(one.view(np.uint8), two.view(np.uint8))
 
 
+@pytest.mark.parametrize("label", ["cfg3", "cfg5b"] + [s[0] for s in GROUPED_SMALL])
+def test_grouped_launch_shapes_give_the_same_bits(label, monkeypatch):
+    """Shrink tiles of 16, 32 or 64 rows and expand waves of 16 or 32 rows
+    (MLORA_SHRINK_MB / MLORA_EXPAND_MB) change which workgroup computes a row,
+    not how: every shape gives the bits of the default per-window call."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    if label.startswith("cfg"):
+        case, view, dev = staged(label)
+    else:
+        case = build_small(label, dict(SMALL)[label])
+        view, dev = OracleView(case), DeviceCase(case, DEV)
+    ref = dev.run(two_kernel=True, pipelined=False)
+    for smb, emb in [("1", "1"), ("2", "2"), ("4", "1"), ("1", "2")]:
+        monkeypatch.setenv("MLORA_SHRINK_MB", smb)
+        monkeypatch.setenv("MLORA_EXPAND_MB", emb)
+        got = dev.run(two_kernel=True, pipelined=False)
+        assert np.array_equal(ref.view(np.uint8), got.view(np.uint8)), (smb, emb)
+
+
 GATHER_SMALL = [s[0] for s in SMALL if s[1]["kind"] == "gather" and s[1].get("dtype") != "f32"]
 
 
