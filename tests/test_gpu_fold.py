@@ -578,7 +578,8 @@ def test_graph_replay_reads_routing_on_device():
     check(view, from_torch(base), c.base, "graph replay, new routing")
 
 
-@pytest.mark.parametrize("form", ["grouped_all", "grouped_window", "gather_two"])
+@pytest.mark.parametrize("form", ["grouped_all", "grouped_all_per_window", "grouped_window",
+                                  "gather_two"])
 def test_graph_replay_workspace_forms(form, monkeypatch):
     """The workspace forms captured in a HIP graph: every replay (with eager
     work and syncs between) equals the eager fold bit for bit, and a replay
@@ -597,7 +598,10 @@ def test_graph_replay_workspace_forms(form, monkeypatch):
         c = workloads.make_grouped_case(87, stream_lens=[150, 90, 61], top_k=4, n_route=12,
                                         k_in=256, n_out=320, max_rank=32, routing="zipf",
                                         n_unadapted=2, cap=300, stream_slot_values=[1, 1, 1])
-        dev = DeviceCase(c, DEV, pipelined=(form == "grouped_all"))
+        if form == "grouped_all_per_window":
+            # one window per launch: the pipe kernel runs inside the graph
+            monkeypatch.setenv("MLORA_ALL_MIN_ROWS", "1")
+        dev = DeviceCase(c, DEV, pipelined=form.startswith("grouped_all"))
         assert len(dev.windows) > 1
     dev.workspace_for(getattr(dev, "windows", None))   # allocated before capture
     pristine = to_torch(c.base, "bf16", DEV)
