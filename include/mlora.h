@@ -22,6 +22,10 @@
  *     once. The host never reads routing data, so a fold is capturable in a
  *     HIP graph. A device-side fault surfaces at the caller's next sync.
  *   - Layouts are row-major and contiguous. bf16 is stored as its 16 raw bits.
+ *   - Environment variables named MLORA_* override launch shapes (rows and
+ *     columns per workgroup, launches per call). They are read at each call
+ *     and exist for measurement: no value changes what a call computes beyond
+ *     the rounding differences documented for the two-kernel gather.
  */
 #ifndef MLORA_H_
 #define MLORA_H_
