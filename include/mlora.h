@@ -262,8 +262,11 @@ int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x, i
 /* Bytes of workspace mlora_grouped_down_all needs: one launch slot (the
  * mlora_grouped_down_workspace_bytes of L = min(n_rows, cap * ceil(m / cap))
  * rows, m the launch minimum above, rounded up to 256) when L covers every
- * row, two slots otherwise. Read the size under the same MLORA_ALL_MIN_ROWS
- * as the call. 0 for n_rows <= 0, cap <= 0 or max_rank outside [1, 128]. */
+ * row, two slots otherwise; or, if larger, the same for launches of one
+ * window (L = min(n_rows, cap)), which the call falls back to when a group
+ * of windows of base_out would pass 4 GiB. Read the size under the same
+ * MLORA_ALL_MIN_ROWS as the call. 0 for n_rows <= 0, cap <= 0 or max_rank
+ * outside [1, 128]. */
 uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap, int32_t max_rank);
 
 /* Bytes of workspace mlora_grouped_down needs for its two-kernel form on the

@@ -2566,9 +2566,14 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
 extern "C" uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap,
                                                            int32_t max_rank) {
   if (n_rows <= 0 || cap <= 0 || max_rank < 1 || max_rank > 128) return 0;
+  // The call launches groups of windows, or single windows where a group
+  // would pass the 4 GiB buffer range (which depends on n_out, not known
+  // here): the larger of the two needs.
   const int64_t chunk = all_chunk_rows(n_rows, cap);
-  const int64_t slots = n_rows > chunk ? 2 : 1;
-  return (uint64_t)(slots * pipe_slot_bytes(chunk, max_rank));
+  const int64_t win = cap < n_rows ? cap : n_rows;
+  const int64_t by_chunk = (n_rows > chunk ? 2 : 1) * pipe_slot_bytes(chunk, max_rank);
+  const int64_t by_win = (n_rows > win ? 2 : 1) * pipe_slot_bytes(win, max_rank);
+  return (uint64_t)(by_chunk > by_win ? by_chunk : by_win);
 }
 
 extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x,

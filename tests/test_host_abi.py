@@ -313,7 +313,10 @@ def test_grouped_all_rejects_bad_args(lib):
     assert call(n_rows=-1) == -1
     assert call(ws=None, ws_bytes=256) == -1
     assert call(ws=FAKE + 16) == -1
-    need = lib.mlora_grouped_down_all_workspace_bytes(8, 4, 8)
+    # one launch of all 8 rows needs one slot of 8 rows (the size query may
+    # report more: it also covers one-window launches)
+    need = lib.mlora_grouped_down_workspace_bytes(0, 8, 8)
+    assert lib.mlora_grouped_down_all_workspace_bytes(8, 4, 8) >= need
     assert call(ws_bytes=need - 1) == ml.MLORA_ERR_CAPACITY
     assert call(ws=None, ws_bytes=0) == ml.MLORA_ERR_CAPACITY   # bf16 needs one
     assert call(n_rows=0) == 0 and call(n_route=0) == 0
@@ -330,7 +333,24 @@ def test_grouped_all_workspace_bytes(lib):
     assert f(100, 30, 100) == g(0, 100, 100)          # 547 windows of 30 > 100 rows
     assert f(70000, 6000, 16) == 2 * g(0, 18000, 16)  # three windows per launch
     assert f(100000, 20000, 16) == 2 * g(0, 20000, 16)
+    # 1.5 windows: one launch of 12288 rows, or two one-window slots when a
+    # launch group would pass 4 GiB of base_out; the size covers both
+    assert f(12288, 8192, 16) == max(g(0, 12288, 16), 2 * g(0, 8192, 16))
     assert f(0, 10, 16) == 0 and f(10, 0, 16) == 0 and f(10, 10, 0) == 0
+
+
+def test_grouped_all_window_fallback_needs_the_queried_size(lib):
+    """1.5 windows of a base_out so wide (n_out 2^17) that one launch of both
+    would pass 4 GiB: the call falls back to one window per launch (two slots
+    of 12000 rows), and the queried size is exactly what it asks for."""
+    r = _route(n_out=1 << 17, max_rank=16)
+    cap, n_rows = 12000, 18000
+    g = lib.mlora_grouped_down_workspace_bytes
+    need = lib.mlora_grouped_down_all_workspace_bytes(n_rows, cap, 16)
+    assert need == 2 * g(0, cap, 16) > g(0, n_rows, 16)
+    rc = lib.mlora_grouped_down_all(ctypes.byref(r), FAKE, 4, FAKE, n_rows, FAKE, 4, FAKE,
+                                    FAKE, 2, cap, FAKE, need - 1, None)
+    assert rc == ml.MLORA_ERR_CAPACITY
 
 
 def test_grouped_all_workspace_bytes_window_per_launch(lib, monkeypatch):
