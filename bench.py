@@ -40,21 +40,21 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-LoRA fold rows/s + achieved HBM GB/s (decode gather, prefill grouped)"
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "cfg2"
+DEFAULT_WORKLOAD = "decode_down_gather"
 KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_lora_amd", "csrc", "mlora_fold.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOAD_TEXT = {
-    "cfg1": "tiny gather fold f32: 4 tokens x top-2 of 4 experts, k_in 64, n_out 32, rank 8",
-    "cfg2": "Qwen3-MoE-like decode down-proj gather: 64 seqs x top-8 (640 rows padded), "
+    "tiny_gather_f32": "tiny gather fold f32: 4 tokens x top-2 of 4 experts, k_in 64, n_out 32, rank 8",
+    "decode_down_gather": "Qwen3-MoE-like decode down-proj gather: 64 seqs x top-8 (640 rows padded), "
             "128 experts (96 adapted), k_in 768, n_out 2048, rank 16, bf16",
-    "cfg3": "prefill grouped down fold: 4096 tokens x top-8 (32768 sorted rows), Zipf(1.1) "
+    "prefill_grouped_down": "prefill grouped down fold: 4096 tokens x top-8 (32768 sorted rows), Zipf(1.1) "
             "over 128 experts, k_in 768, n_out 2048, rank 32, bf16, windows of 8192",
-    "cfg4": "gate/up gather: 256 seqs x top-8 (2048 rows), 128 experts, k_in 2048, "
+    "gateup_gather": "gate/up gather: 256 seqs x top-8 (2048 rows), 128 experts, k_in 2048, "
             "n_out 768, rank 64, bf16",
-    "cfg5a": "router fold one-entry route: 8192 token rows, top_k 1, k_in 2048, n_out 128, "
+    "router_gather": "router fold one-entry route: 8192 token rows, top_k 1, k_in 2048, n_out 128, "
              "rank 16, bf16",
-    "cfg5b": "mixed prefill grouped fold: 16384 sorted rows, 256 experts (77 unadapted, "
+    "mixed_grouped": "mixed prefill grouped fold: 16384 sorted rows, 256 experts (77 unadapted, "
              "duplicate ids), k_in 1536, n_out 4096, rank 16, bf16, windows of 8192",
 }
 
@@ -307,7 +307,7 @@ def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     rows_f, rows_w = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     names = sorted({r["Kernel_Name"] for r in rows_f + rows_w if "mlora" in r["Kernel_Name"]})
     import workloads
-    case = workloads.CONFIGS[workload]()
+    case = workloads.WORKLOADS[workload]()
     launches = algorithmic_traffic(case, *_tables_and_map(case))[4]
 
     def per_launch(rows, counter):
@@ -387,7 +387,7 @@ def main():
         return
 
     t_gen = time.perf_counter()
-    case = workloads.CONFIGS[args.workload]()
+    case = workloads.WORKLOADS[args.workload]()
     t_gen = time.perf_counter() - t_gen
     cb = copy_bytes(case)
     copies = args.copies or max(2, min(64, math.ceil(640e6 / cb)))

@@ -31,7 +31,7 @@ def _need_gpu():
 @functools.lru_cache(maxsize=None)
 def staged(name):
     from tests.device import DeviceCase
-    case = workloads.CONFIGS[name]()
+    case = workloads.WORKLOADS[name]()
     return case, OracleView(case), DeviceCase(case, DEV)
 
 
@@ -59,7 +59,7 @@ def check(view, got, base, label):
     return rel, mx
 
 
-ALL = ["cfg1", "cfg2", "cfg3", "cfg4", "cfg5a", "cfg5b"]
+ALL = ["tiny_gather_f32", "decode_down_gather", "prefill_grouped_down", "gateup_gather", "router_gather", "mixed_grouped"]
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -107,7 +107,7 @@ def test_untouched_rows_sentinel(name):
     assert not np.any(np.isnan(to_f64(got[live], case.dtype)))
 
 
-@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg5b"])
+@pytest.mark.parametrize("name", ["decode_down_gather", "prefill_grouped_down", "mixed_grouped"])
 def test_deterministic(name):
     _need_gpu()
     case, view, dev = staged(name)
@@ -138,7 +138,7 @@ def test_grouped_equals_gather_permuted():
 
 def test_windows_equal_single_window():
     _need_gpu()
-    case, view, dev = staged("cfg3")
+    case, view, dev = staged("prefill_grouped_down")
     a = dev.run(windows=[(0, case.n_rows)])
     b = dev.run()  # four windows of 8192
     assert np.array_equal(a, b)
@@ -315,7 +315,7 @@ def test_small_cases(label, kw):
 GROUPED_SMALL = [s for s in SMALL if s[1]["kind"] == "grouped"]
 
 
-@pytest.mark.parametrize("label", ["cfg3", "cfg5b"] + [s[0] for s in GROUPED_SMALL])
+@pytest.mark.parametrize("label", ["prefill_grouped_down", "mixed_grouped"] + [s[0] for s in GROUPED_SMALL])
 def test_grouped_two_kernel_equals_one_kernel(label):
     """The workspace (shrink, then expand) form and the one-kernel form of the
     grouped fold give the same bits, and the one-kernel form passes the
@@ -333,7 +333,7 @@ def test_grouped_two_kernel_equals_one_kernel(label):
     assert np.array_equal(one.view(np.uint8), two.view(np.uint8))
 
 
-@pytest.mark.parametrize("label", ["cfg3", "cfg5b"] + [s[0] for s in GROUPED_SMALL])
+@pytest.mark.parametrize("label", ["prefill_grouped_down", "mixed_grouped"] + [s[0] for s in GROUPED_SMALL])
 def test_grouped_launch_shapes_give_the_same_bits(label, monkeypatch):
     """Shrink tiles of 16, 32 or 64 rows and expand waves of 16 or 32 rows
     (MLORA_SHRINK_MB / MLORA_EXPAND_MB) change which workgroup computes a row,
@@ -356,7 +356,7 @@ def test_grouped_launch_shapes_give_the_same_bits(label, monkeypatch):
 GATHER_SMALL = [s[0] for s in SMALL if s[1]["kind"] == "gather" and s[1].get("dtype") != "f32"]
 
 
-@pytest.mark.parametrize("label", ["cfg4", "cfg5a"] + GATHER_SMALL)
+@pytest.mark.parametrize("label", ["gateup_gather", "router_gather"] + GATHER_SMALL)
 def test_gather_one_kernel_form(label):
     """The gather fold without a workspace (one kernel) passes the oracle bar;
     the other tests give it a workspace, which large calls use for the
@@ -413,7 +413,7 @@ def test_gather_two_kernel_form(label, monkeypatch):
 
 
 @pytest.mark.parametrize("min_rows", [None, "1"], ids=["launch16k", "launch1win"])
-@pytest.mark.parametrize("label", ["cfg3", "cfg5b"] + [s[0] for s in GROUPED_SMALL])
+@pytest.mark.parametrize("label", ["prefill_grouped_down", "mixed_grouped"] + [s[0] for s in GROUPED_SMALL])
 def test_grouped_all_windows_pipelined_equals_per_window(label, min_rows, monkeypatch):
     """mlora_grouped_down_all (launch l + 1's windows shrunk in the launch that
     expands launch l's) equals one mlora_grouped_down call per window, bit for
@@ -471,7 +471,7 @@ def test_grouped_workspace_reused_across_windows_and_calls():
         check(OracleView(small), got_s, small.base, "small")
 
 
-@pytest.mark.parametrize("label", ["cfg2", "gather_r24_k72", "gather_slots_not_multiple",
+@pytest.mark.parametrize("label", ["decode_down_gather", "gather_r24_k72", "gather_slots_not_multiple",
                                    "gather_r16_ns4"])
 def test_resident_weights_path_equals_streaming_path(label, monkeypatch):
     """The decode path that holds a wave's weights in registers and the
@@ -479,7 +479,7 @@ def test_resident_weights_path_equals_streaming_path(label, monkeypatch):
     resident one passes the oracle bar on its own."""
     _need_gpu()
     from tests.device import DeviceCase
-    if label == "cfg2":
+    if label == "decode_down_gather":
         case, view, dev = staged(label)
     elif label == "gather_r16_ns4":
         case = workloads.make_gather_case(77, n_seq=40, padded_n=48, top_k=6, n_route=30,

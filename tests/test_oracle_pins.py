@@ -555,7 +555,7 @@ def test_bf16_store_alone_breaks_literal_max_abs():
     import workloads
     from tests.common import (MAX_ABS_TOL, REL_L2_TOL, max_abs, max_abs_excess, rel_l2,
                               to_f64)
-    c = workloads.cfg4()
+    c = workloads.gateup_gather()
     ref = OracleView(c).fold()
     best = to_f64(workloads.bf16_from_f32(ref.astype(np.float32)), "bf16")
     assert np.abs(ref).max() >= 8.0

@@ -273,31 +273,31 @@ def make_grouped_case(seed: int, *, stream_lens, top_k: int, n_route: int, k_in:
 
 
 # ----------------------------------------------------------------------------
-# the five workloads (config 5 has a router half "5a" and a mixed half "5b")
+# the workloads measured and checked at full size
 # ----------------------------------------------------------------------------
 
-def cfg1() -> FoldCase:
+def tiny_gather_f32() -> FoldCase:
     """Tiny fp32 gather: 4 tokens, top-2 of 4 experts, expert 3 packed with null
     cells, k_in=64, n_out=32, rank 8, sequence 1 is a Skip request."""
     rng_seed = 1
     c = make_gather_case(rng_seed, n_seq=4, padded_n=4, top_k=2, n_route=4, k_in=64,
                          n_out=32, max_rank=8, dtype="f32", adapted=np.array([0, 1, 2]),
-                         zero_ids=(3,), name="cfg1_tiny_gather_f32")
+                         zero_ids=(3,), name="tiny_gather_f32")
     # the recipe fixes the slots: [active, Skip, active, active]
     c.adapter_slots = np.array([1, -1, 1, 1], dtype=np.int32)
     return c
 
 
-def cfg2() -> FoldCase:
+def decode_down_gather() -> FoldCase:
     """Qwen3-MoE-like decode down-proj gather: 64 sequences x top-8 over 128
     experts, padded to 80 tokens (640 rows), 96 adapted experts, 6 Skip
     sequences, k_in=768, n_out=2048, rank 16, bf16."""
     return make_gather_case(2, n_seq=64, padded_n=80, top_k=8, n_route=128, k_in=768,
                             n_out=2048, max_rank=16, n_adapted=96, skip_seqs=6,
-                            name="cfg2_decode_down_gather")
+                            name="decode_down_gather")
 
 
-def cfg3_stream_lens(seed: int = 3) -> np.ndarray:
+def prefill_stream_lens(seed: int = 3) -> np.ndarray:
     rng = np.random.default_rng([seed, 1])
     while True:
         lens = rng.integers(256, 769, size=7)
@@ -306,29 +306,29 @@ def cfg3_stream_lens(seed: int = 3) -> np.ndarray:
             return np.concatenate([lens, [last]]).astype(np.int64)
 
 
-def cfg3() -> FoldCase:
+def prefill_grouped_down() -> FoldCase:
     """Prefill grouped down fold: 4096 tokens from 8 packed streams, top-8 of 128
     experts with Zipf(1.1) weights (32768 sorted rows), all adapted, k_in=768,
     n_out=2048, rank 32, bf16, window cap 8192."""
-    return make_grouped_case(3, stream_lens=cfg3_stream_lens(), top_k=8, n_route=128,
+    return make_grouped_case(3, stream_lens=prefill_stream_lens(), top_k=8, n_route=128,
                              k_in=768, n_out=2048, max_rank=32, routing="zipf",
-                             zipf_alpha=1.1, cap=8192, name="cfg3_prefill_grouped_down")
+                             zipf_alpha=1.1, cap=8192, name="prefill_grouped_down")
 
 
-def cfg4() -> FoldCase:
+def gateup_gather() -> FoldCase:
     """Gate/up gather (hidden -> intermediate): 256 sequences x top-8 (2048 rows),
     128 experts all adapted, k_in=2048, n_out=768, rank 64, scale U[0.25, 4]."""
     return make_gather_case(4, n_seq=256, padded_n=256, top_k=8, n_route=128, k_in=2048,
                             n_out=768, max_rank=64, scale=(0.25, 4.0),
-                            name="cfg4_gateup_gather")
+                            name="gateup_gather")
 
 
-def cfg5a() -> FoldCase:
+def router_gather() -> FoldCase:
     """Router fold as a one-entry route: expert 0 over 8192 token rows, top_k=1,
     k_in=2048, n_out=128, rank 16. The map comes from one prefill stream."""
     c = make_gather_case(51, n_seq=1, padded_n=8192, top_k=1, n_route=1, k_in=2048,
                          n_out=128, max_rank=16, adapted=np.array([0]), index_mode="zero",
-                         name="cfg5a_router_gather")
+                         name="router_gather")
     c.map_kind = "host"
     c.cu_seqlens = np.array([0, 8192], dtype=np.int32)
     c.stream_slots = np.array([1], dtype=np.int32)
@@ -336,7 +336,7 @@ def cfg5a() -> FoldCase:
     return c
 
 
-def cfg5b() -> FoldCase:
+def mixed_grouped() -> FoldCase:
     """Mixed prefill grouped fold: 2048 tokens x top-8 (16384 sorted rows) over
     256 experts, 77 unadapted (id 255 among them), about 10% of adapted ids
     packed twice (a decoy first, the real pair last), k_in=1536, n_out=4096,
@@ -344,14 +344,14 @@ def cfg5b() -> FoldCase:
     return make_grouped_case(52, stream_lens=[256] * 8, top_k=8, n_route=256, k_in=1536,
                              n_out=4096, max_rank=16, routing="uniform", n_unadapted=77,
                              force_unadapted=(255,), dup_frac=0.10, cap=8192,
-                             name="cfg5b_mixed_grouped")
+                             name="mixed_grouped")
 
 
-CONFIGS = {
-    "cfg1": cfg1,
-    "cfg2": cfg2,
-    "cfg3": cfg3,
-    "cfg4": cfg4,
-    "cfg5a": cfg5a,
-    "cfg5b": cfg5b,
+WORKLOADS = {
+    "tiny_gather_f32": tiny_gather_f32,
+    "decode_down_gather": decode_down_gather,
+    "prefill_grouped_down": prefill_grouped_down,
+    "gateup_gather": gateup_gather,
+    "router_gather": router_gather,
+    "mixed_grouped": mixed_grouped,
 }
