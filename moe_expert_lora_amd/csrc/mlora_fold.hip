@@ -1468,7 +1468,8 @@ __device__ __forceinline__ void grouped_shrink_unit(const GroupedArgs& p, int u,
   const int64_t r1 = min(r0 + kRows, p.row_end);
   const int tid = threadIdx.x;
 
-  // round 1: this thread's row id, and span + table cells of expert e = tid
+  // first request round: this thread's row id, and span + table cells of
+  // expert e = tid
   int id = -1;
   if (tid < kRows && r0 + tid < r1) id = p.sorted_ids[r0 + tid];
   if (tid == 0) s_nseg = 0;
@@ -1512,8 +1513,8 @@ __device__ __forceinline__ void grouped_shrink_unit(const GroupedArgs& p, int u,
     return;
   }
 
-  // round 2: the map entry of this thread's row; consumed after the shrink
-  // loads of the first pass are in flight
+  // second request round: the map entry of this thread's row; consumed after
+  // the shrink loads of the first pass are in flight
   int map = -1;
   if (tok >= 0) map = p.row_adapter[tok];
 
