@@ -322,7 +322,7 @@ def test_grouped_two_kernel_equals_one_kernel(label):
     oracle bar on its own (the other tests run the two-kernel form)."""
     _need_gpu()
     from tests.device import DeviceCase
-    if label.startswith("cfg"):
+    if label in workloads.WORKLOADS:
         case, view, dev = staged(label)
     else:
         case = build_small(label, dict(SMALL)[label])
@@ -340,7 +340,7 @@ def test_grouped_launch_shapes_give_the_same_bits(label, monkeypatch):
     not how: every shape gives the bits of the default per-window call."""
     _need_gpu()
     from tests.device import DeviceCase
-    if label.startswith("cfg"):
+    if label in workloads.WORKLOADS:
         case, view, dev = staged(label)
     else:
         case = build_small(label, dict(SMALL)[label])
@@ -363,7 +363,7 @@ def test_gather_one_kernel_form(label):
     two-kernel form."""
     _need_gpu()
     from tests.device import DeviceCase
-    if label.startswith("cfg"):
+    if label in workloads.WORKLOADS:
         case, view, dev = staged(label)
     else:
         case = build_small(label, dict(SMALL)[label])
@@ -422,7 +422,7 @@ def test_grouped_all_windows_pipelined_equals_per_window(label, min_rows, monkey
     if min_rows:
         monkeypatch.setenv("MLORA_ALL_MIN_ROWS", min_rows)
     from tests.device import DeviceCase
-    if label.startswith("cfg"):
+    if label in workloads.WORKLOADS:
         case, view, dev = staged(label)
     else:
         case = build_small(label, dict(SMALL)[label])
