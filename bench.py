@@ -21,6 +21,8 @@ Prints ONE JSON line (rank 0, N = 1):
              from the committed rocprofv3 summary when the kernel source still
              matches it, else null
   cpu_baseline  the fp64 CPU oracle timed on the host on a bounded sample
+  also       (default run) the prefill grouped workload measured the same way:
+             value, ms_per_step, config and roofline of its own
 """
 from __future__ import annotations
 
@@ -346,49 +348,14 @@ def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     print(json.dumps({workload: rec}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--one-kernel", action="store_true",
-                    help="run the folds without a workspace (one-kernel forms)")
-    ap.add_argument("--eager", action="store_true",
-                    help="time eager launches instead of graph replays")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run the plain copy used to scale HBM counters")
-    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
-                    help="rocprofv3 --pmc output dirs -> profiles/traffic.json (no GPU)")
-    args = ap.parse_args()
-
-    if args.traffic_from:
-        traffic_from(args.workload, *args.traffic_from)
-        return
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the fold needs no collective and this "
-              "build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
+def measure(workload, args, with_cpu):
+    """One workload: stage it, time `args.steps` graph-replayed steps, and
+    return the result record (the JSON line's fields)."""
     import torch
     import moe_expert_lora_amd as ml
     import workloads
 
-    ml.load()
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-
-    t_gen = time.perf_counter()
-    case = workloads.WORKLOADS[args.workload]()
-    t_gen = time.perf_counter() - t_gen
+    case = workloads.WORKLOADS[workload]()
     cb = copy_bytes(case)
     copies = args.copies or max(2, min(64, math.ceil(640e6 / cb)))
     st = Staged(case, copies, two_kernel=not args.one_kernel)
@@ -472,14 +439,14 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
-            rec = json.load(open(TRAFFIC_FILE)).get(args.workload)
+            rec = json.load(open(TRAFFIC_FILE)).get(workload)
             if rec and rec.get("kernel_sha256_16") == kernel_hash():
                 traffic = rec.get("hbm_bytes_per_launch")
         except Exception:
             traffic = None
 
     cpu = None
-    if not args.no_cpu:
+    if with_cpu:
         cpu = cpu_baseline(case, args.cpu_seconds)
 
     ms_per_step = wall / steps * 1e3
@@ -497,7 +464,7 @@ def main():
         "dtype": "bf16" if case.dtype == "bf16" else "f32",
         "data": "synthetic (seeded generators; random-init adapter weights)",
         "config": {
-            "workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
+            "workload": f"{workload}: {WORKLOAD_TEXT[workload]}",
             "path": case.path,
             "rows_per_step": rows,
             "folded_rows_per_step": folded,
@@ -525,6 +492,69 @@ def main():
         "eager_step_us": eager_us,
         "notes": "the pages quote no performance numbers; vs_baseline is null",
     }
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOAD_TEXT),
+                    help=f"default {DEFAULT_WORKLOAD}")
+    ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads measured after the main one and reported "
+                         "under 'also' (default: the prefill grouped workload when no "
+                         "--workload is given; 'none' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--one-kernel", action="store_true",
+                    help="run the folds without a workspace (one-kernel forms)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of graph replays")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the plain copy used to scale HBM counters")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="rocprofv3 --pmc output dirs -> profiles/traffic.json (no GPU)")
+    args = ap.parse_args()
+
+    if args.also is None:
+        args.also = "prefill_grouped_down" if args.workload is None else ""
+    elif args.also == "none":
+        args.also = ""
+    if args.workload is None:
+        args.workload = DEFAULT_WORKLOAD
+    if args.traffic_from:
+        traffic_from(args.workload, *args.traffic_from)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the fold needs no collective and this "
+              "build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_expert_lora_amd as ml
+
+    ml.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    out = measure(args.workload, args, with_cpu=not args.no_cpu)
+    # The metric covers both halves of the fold: the decode line above, and
+    # the prefill grouped workload beside it (same protocol, no CPU leg).
+    also = [w for w in (args.also.split(",") if args.also else []) if w and w != args.workload]
+    if also:
+        out["also"] = {}
+        for w in also:
+            r = measure(w, args, with_cpu=False)
+            out["also"][w] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps",
+                                                 "dtype", "config", "roofline")}
     print(json.dumps(out), flush=True)
 
 
