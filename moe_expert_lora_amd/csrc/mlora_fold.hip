@@ -2188,10 +2188,16 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   // The two-kernel form holds at most kWaves * kTwoSteps k steps per range.
   // It pays where an expert's A_e outweighs its rows' x (few rows per expert,
   // k_in split over several ranges); an expert with many rows streams x once
-  // per row in one kernel anyway.
+  // per row in one kernel anyway. With few rows per expert the second launch
+  // and its routing round cost more than the split saves, until some expert
+  // holds more than 16 rows and its one-kernel workgroup takes a second
+  // 16-row chunk (measured over 128 experts, top-8, k_in 1536-2048, ranks
+  // 16-64: one kernel 3-14% faster at 4-7 rows per expert on average, two
+  // kernels 14-36% faster from 8). At 7 the one-kernel form already risks
+  // that second chunk, so it is used up to 6.
   const bool two_fits = (K + 31) / 32 <= kMaxKc * kWaves * kTwoSteps;
   const int64_t rows_e_all = (n_slots + E - 1) / E;
-  const int two_default = (gather_kc(K) > 1 && rows_e_all <= 64) ? 1 : 0;
+  const int two_default = (gather_kc(K) > 1 && rows_e_all > 6 && rows_e_all <= 64) ? 1 : 0;
   if (workspace && !use_resident && two_fits &&
       env_int("MLORA_GATHER_TWO", two_default) != 0) {
     if (ws_need > (int64_t)kMaxBufBytes)

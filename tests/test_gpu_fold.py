@@ -500,6 +500,29 @@ def test_resident_weights_path_equals_streaming_path(label, monkeypatch):
     assert np.array_equal(res.view(np.uint8), stream.view(np.uint8))
 
 
+@pytest.mark.parametrize("n_seq,form", [(64, "one"), (96, "one"), (128, "two")])
+def test_gather_planner_default_form(n_seq, form, monkeypatch):
+    """With a workspace, a gather whose experts average at most 6 rows (k_in
+    2048, rank 16: no register-resident form) runs as one kernel, from 7 rows
+    on as the k-split pair. The two forms add the k ranges in different orders,
+    so the default call's bits show which one ran; both pass the oracle bar."""
+    _need_gpu()
+    from tests.device import DeviceCase
+    case = workloads.make_gather_case(90 + n_seq, n_seq=n_seq, padded_n=n_seq, top_k=8,
+                                      n_route=128, k_in=2048, n_out=768, max_rank=16,
+                                      name=f"planner_{n_seq}")
+    view, dev = OracleView(case), DeviceCase(case, DEV)
+    got = dev.run()
+    check(view, got, case.base, f"{case.name} default")
+    forced = {}
+    for f, two in (("one", "0"), ("two", "1")):
+        monkeypatch.setenv("MLORA_GATHER_TWO", two)
+        forced[f] = dev.run()
+    monkeypatch.delenv("MLORA_GATHER_TWO")
+    assert not np.array_equal(forced["one"], forced["two"])
+    assert np.array_equal(got.view(np.uint8), forced[form].view(np.uint8))
+
+
 def test_guard_bands_untouched():
     """Fold into a slice of a larger buffer: the bytes around it stay as they were."""
     _need_gpu()
