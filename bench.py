@@ -495,6 +495,23 @@ def measure(workload, args, with_cpu):
     return out
 
 
+def resolve_workloads(workload, also):
+    """(main workload, workloads reported under 'also') from the command line:
+    no --workload means the decode default with the prefill grouped workload
+    beside it; an explicit --workload runs alone unless --also names others;
+    --also none runs none."""
+    if also is None:
+        also = "prefill_grouped_down" if workload is None else ""
+    elif also == "none":
+        also = ""
+    workload = workload or DEFAULT_WORKLOAD
+    extra = [w for w in also.split(",") if w and w != workload]
+    for w in extra:
+        if w not in WORKLOAD_TEXT:
+            raise SystemExit(f"bench.py: unknown workload {w!r} in --also")
+    return workload, extra
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -519,12 +536,7 @@ def main():
                     help="rocprofv3 --pmc output dirs -> profiles/traffic.json (no GPU)")
     args = ap.parse_args()
 
-    if args.also is None:
-        args.also = "prefill_grouped_down" if args.workload is None else ""
-    elif args.also == "none":
-        args.also = ""
-    if args.workload is None:
-        args.workload = DEFAULT_WORKLOAD
+    args.workload, args.also = resolve_workloads(args.workload, args.also)
     if args.traffic_from:
         traffic_from(args.workload, *args.traffic_from)
         return
@@ -548,7 +560,7 @@ def main():
     out = measure(args.workload, args, with_cpu=not args.no_cpu)
     # The metric covers both halves of the fold: the decode line above, and
     # the prefill grouped workload beside it (same protocol, no CPU leg).
-    also = [w for w in (args.also.split(",") if args.also else []) if w and w != args.workload]
+    also = args.also
     if also:
         out["also"] = {}
         for w in also:
