@@ -132,6 +132,16 @@ __device__ __forceinline__ void bst16(rsrc_t r, uint32_t off, u32x4 v) {
       __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
 }
 
+// Non-temporal 16-byte access (base_out is read once and written once).
+constexpr int kNT = 2;
+__device__ __forceinline__ u32x4 bld16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
+}
+__device__ __forceinline__ void bst16_nt(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, kNT);
+}
+
 __device__ __forceinline__ bf16x8 as_bf(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // A value every lane of the wave holds, moved to scalar registers. Buffer
@@ -375,7 +385,7 @@ __device__ __forceinline__ void load_expand(ExpandBatch<NB, MB, UE>& eb, const B
     const bool cok = cs < ncs && col < n_hi;
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
-      eb.o[u][rb] = bld16(bf.out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
+      eb.o[u][rb] = bld16_nt(bf.out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
   }
 }
 
@@ -407,7 +417,7 @@ __device__ __forceinline__ void mma_store_expand(const ExpandBatch<NB, MB, UE>& 
         const uint32_t o1 = pack_bf16(lo_f(bq.y) + d0.z, hi_f(bq.y) + d0.w);
         const uint32_t o2 = pack_bf16(lo_f(bq.z) + d1.x, hi_f(bq.z) + d1.y);
         const uint32_t o3 = pack_bf16(lo_f(bq.w) + d1.z, hi_f(bq.w) + d1.w);
-        bst16(bf.out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB,
+        bst16_nt(bf.out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB,
               u32x4{o0, o1, o2, o3});
       }
     }
@@ -945,7 +955,7 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(
       const bool cok = cs < ncs && col < n_hi;
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb)
-        ov[t][rb] = bld16(r_out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
+        ov[t][rb] = bld16_nt(r_out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
     }
     if (first) request_b();
     __builtin_amdgcn_sched_barrier(0);
@@ -991,7 +1001,7 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(
             const uint32_t o1 = pack_bf16(lo_f(bq.y) + d0.z, hi_f(bq.y) + d0.w);
             const uint32_t o2 = pack_bf16(lo_f(bq.z) + d1.x, hi_f(bq.z) + d1.y);
             const uint32_t o3 = pack_bf16(lo_f(bq.w) + d1.z, hi_f(bq.w) + d1.w);
-            bst16(r_out, (rw.valid[rb] && col < n_hi) ? rw.ooff[rb] + 2u * col : kOOB,
+            bst16_nt(r_out, (rw.valid[rb] && col < n_hi) ? rw.ooff[rb] + 2u * col : kOOB,
                   u32x4{o0, o1, o2, o3});
           }
         }
@@ -1347,16 +1357,6 @@ __device__ __forceinline__ void load_half(rsrc_t r, bool ok, uint32_t off,
       w[q][3] = v.w;
     }
   }
-}
-
-// Non-temporal 16-byte access (base_out is read once and written once).
-constexpr int kNT = 2;
-__device__ __forceinline__ u32x4 bld16_nt(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
-}
-__device__ __forceinline__ void bst16_nt(rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(
-      __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, kNT);
 }
 
 // Orders one wave's LDS writes before its later LDS reads of other lanes'
