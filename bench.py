@@ -23,6 +23,8 @@ Prints ONE JSON line (rank 0, N = 1):
   cpu_baseline  the fp64 CPU oracle timed on the host on a bounded sample
   also       (default run) the prefill grouped workload measured the same way:
              value, ms_per_step, config and roofline of its own
+  hbm_copy_gbs  read + write GB/s of a plain 1 GiB device copy: a practical
+             HBM figure for context (the roofline uses the nominal 8 TB/s)
 """
 from __future__ import annotations
 
@@ -252,6 +254,29 @@ def calibrate_copy():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": CALIB_BYTES}), flush=True)
+
+
+def copy_bandwidth(n_bytes=1 << 30, reps=10):
+    """Read + write GB/s of a plain device copy of n_bytes (torch's copy kernel),
+    timed with HIP events on the current stream: a practical HBM figure beside
+    the nominal peak, reported for context and never used as the roofline."""
+    import torch
+    src = torch.empty(n_bytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * n_bytes / sec / 1e9
 
 
 def _pmc_rows(path):
@@ -558,6 +583,7 @@ def main():
         return
 
     out = measure(args.workload, args, with_cpu=not args.no_cpu)
+    out["hbm_copy_gbs"] = copy_bandwidth()
     # The metric covers both halves of the fold: the decode line above, and
     # the prefill grouped workload beside it (same protocol, no CPU leg).
     also = args.also
