@@ -23,6 +23,8 @@ Prints ONE JSON line (rank 0, N = 1):
   cpu_baseline  the fp64 CPU oracle timed on the host on a bounded sample
   also       (default run) the prefill grouped workload measured the same way:
              value, ms_per_step, config and roofline of its own
+  warm_launch_us  the same call replayed on one copy, inputs resident in L2 /
+             MALL (context only: every other figure is cold HBM)
   hbm_copy_gbs  read + write GB/s of a plain 1 GiB device copy: a practical
              HBM figure for context (the roofline uses the nominal 8 TB/s)
 """
@@ -460,6 +462,29 @@ def measure(workload, args, with_cpu):
     torch.cuda.synchronize()
     eager_us = (time.perf_counter() - t0) / copies * 1e6
 
+    # warm figure, for context: one copy's step, captured as many times as the
+    # cold graph holds steps (the same graph-launch cost per step) and
+    # replayed, its inputs resident in L2 / MALL after the first step
+    warm_us = None
+    if not args.eager:
+        wg = torch.cuda.CUDAGraph()
+        side2 = torch.cuda.Stream()
+        side2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side2):
+            with torch.cuda.graph(wg, stream=side2):
+                for _ in range(copies):
+                    st.step(0)
+        torch.cuda.current_stream().wait_stream(side2)
+        wg.replay()
+        torch.cuda.synchronize()
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for _ in range(replays):
+            wg.replay()
+        w1.record(stream)
+        torch.cuda.synchronize()
+        warm_us = w0.elapsed_time(w1) * 1e3 / (replays * copies) / launches
+
     achieved = alg_bytes / launches / per_launch_s / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -515,6 +540,7 @@ def measure(workload, args, with_cpu):
         "cpu_baseline": cpu,
         "host_setup_us": host_us,
         "eager_step_us": eager_us,
+        "warm_launch_us": warm_us,
         "notes": "the pages quote no performance numbers; vs_baseline is null",
     }
     return out
