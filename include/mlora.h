@@ -15,7 +15,8 @@
  * Conventions shared by every entry point:
  *   - Every buffer, host or device, belongs to the caller. The library never
  *     allocates, frees or synchronises, and keeps no state except a
- *     thread-local last-error message (mlora_last_error).
+ *     thread-local last-error message (mlora_last_error) and the launch-shape
+ *     overrides below.
  *   - Host outputs are written only when the call returns MLORA_OK (or, for
  *     sizes, MLORA_ERR_CAPACITY, which writes only the needed size).
  *   - The two fold calls enqueue kernels on the caller's stream and return at
@@ -23,9 +24,12 @@
  *     HIP graph. A device-side fault surfaces at the caller's next sync.
  *   - Layouts are row-major and contiguous. bf16 is stored as its 16 raw bits.
  *   - Environment variables named MLORA_* override launch shapes (rows and
- *     columns per workgroup, launches per call). They are read at each call
- *     and exist for measurement: no value changes what a call computes beyond
- *     the rounding differences documented for the two-kernel gather.
+ *     columns per workgroup, launches per call). They exist for measurement:
+ *     no value changes what a call computes beyond the rounding differences
+ *     documented for the two-kernel gather, and no value changes the size a
+ *     workspace query returns. They are read once per process, at the first
+ *     fold call, and again only by mlora_reload_launch_overrides; no fold
+ *     call reads the environment.
  */
 #ifndef MLORA_H_
 #define MLORA_H_
@@ -243,9 +247,9 @@ int32_t mlora_grouped_down(const mlora_expert_route* route, const void* x, int64
  * mlora_grouped_down_windows(n_rows, cap), and the result equals calling
  * mlora_grouped_down on each of them in order with a workspace, bit for bit
  * (rows are independent). Consecutive windows are launched together, in
- * launches of whole windows holding at least 16384 rows (the environment
- * variable MLORA_ALL_MIN_ROWS sets another minimum; 1 launches one window at
- * a time), and the launches are pipelined: one kernel expands launch l's rows
+ * launches of whole windows holding at least 16384 rows (the override
+ * MLORA_ALL_MIN_ROWS may lower the minimum to between 1 and 16384 rows; 1
+ * launches one window at a time), and the launches are pipelined: one kernel expands launch l's rows
  * while it shrinks launch l + 1's, so a shrink overlaps the previous rows'
  * base_out traffic. Arguments as for mlora_grouped_down; cap <= 0 ->
  * MLORA_ERR_INVALID [P2 grouped_down_windows]. The workspace is required for
@@ -259,14 +263,14 @@ int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x, i
                                const int32_t* row_adapter, int32_t top_k, int64_t cap,
                                void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* Bytes of workspace mlora_grouped_down_all needs: one launch slot (the
- * mlora_grouped_down_workspace_bytes of L = min(n_rows, cap * ceil(m / cap))
- * rows, m the launch minimum above, rounded up to 256) when L covers every
- * row, two slots otherwise; or, if larger, the same for launches of one
- * window (L = min(n_rows, cap)), which the call falls back to when a group
- * of windows of base_out would pass 4 GiB. Read the size under the same
- * MLORA_ALL_MIN_ROWS as the call. 0 for n_rows <= 0, cap <= 0 or max_rank
- * outside [1, 128]. */
+/* Bytes of workspace mlora_grouped_down_all needs, whatever launch minimum
+ * it runs with (the default, any override, or the one-window fallback taken
+ * when a group of windows of base_out would pass 4 GiB): the largest, over
+ * launches of m whole windows (m from 1 to ceil(16384 / cap)), of one slot
+ * when L = min(n_rows, m * cap) rows cover every row and two slots
+ * otherwise, a slot being mlora_grouped_down_workspace_bytes of L rows
+ * rounded up to 256. Reads no environment. 0 for n_rows <= 0, cap <= 0 or
+ * max_rank outside [1, 128]. */
 uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap, int32_t max_rank);
 
 /* Bytes of workspace mlora_grouped_down needs for its two-kernel form on the
@@ -277,6 +281,13 @@ uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap, int
  * max_rank outside [1, 128]). */
 uint64_t mlora_grouped_down_workspace_bytes(int64_t row_offset, int64_t row_end,
                                             int32_t max_rank);
+
+/* Reads the MLORA_* launch-shape overrides from the environment again (they
+ * are otherwise read once, at the first fold call). For measurement tools and
+ * tests that change the environment within one process. Not safe while
+ * another thread is inside a fold call; launches already enqueued or
+ * captured in a graph keep the shapes they were made with. */
+void mlora_reload_launch_overrides(void);
 
 #ifdef __cplusplus
 }  /* extern "C" */

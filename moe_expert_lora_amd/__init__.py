@@ -49,6 +49,7 @@ EXPORTS = (
     "mlora_gather_bgmv_workspace_bytes",
     "mlora_grouped_down_all",
     "mlora_grouped_down_all_workspace_bytes",
+    "mlora_reload_launch_overrides",
 )
 
 
@@ -120,6 +121,7 @@ def load() -> ctypes.CDLL:
         "mlora_grouped_down_all": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64, vp, i32,
                                          vp, vp, i32, i64, vp, ctypes.c_uint64, vp]),
         "mlora_grouped_down_all_workspace_bytes": (ctypes.c_uint64, [i64, i64, i32]),
+        "mlora_reload_launch_overrides": (None, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -249,6 +251,11 @@ def mlora_gather_row_token(row: int, top_k: int) -> int:
 
 def mlora_m_tile() -> int:
     return int(load().mlora_m_tile())
+
+
+def mlora_reload_launch_overrides() -> None:
+    """Re-read the MLORA_* launch-shape overrides from the environment."""
+    load().mlora_reload_launch_overrides()
 
 
 # ---------------------------------------------------------------------------

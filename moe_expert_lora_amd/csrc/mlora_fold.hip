@@ -42,6 +42,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "mlora.h"
 #include "mlora_internal.h"
@@ -1874,11 +1875,50 @@ __global__ __launch_bounds__(kThreads) void rowwise_f32_kernel(RowwiseArgs p) {
 // host side: validation, launch shape, dispatch
 // ---------------------------------------------------------------------------
 
-int env_int(const char* name, int dflt) {
+// Launch-shape overrides (MLORA_* environment variables), read once per
+// process at the first fold call and again only by
+// mlora_reload_launch_overrides: no fold call reads the environment. Every
+// value changes which workgroup computes what, never what a call computes
+// beyond the rounding differences of the two-kernel gather.
+struct Overrides {
+  int gather_rs, gather_ns, gather_small, gather_resident, gather_two, gather_two_ns;
+  int grouped_mb, grouped_ns, shrink_mb, expand_mb, expand_cw, all_min_rows;
+};
+constexpr int kUnset = -0x7fffffff;
+
+int read_env(const char* name) {
   const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
+  if (!v || !*v) return kUnset;
   return std::atoi(v);
 }
+
+Overrides read_overrides() {
+  Overrides o;
+  o.gather_rs = read_env("MLORA_GATHER_RS");
+  o.gather_ns = read_env("MLORA_GATHER_NS");
+  o.gather_small = read_env("MLORA_GATHER_SMALL");
+  o.gather_resident = read_env("MLORA_GATHER_RESIDENT");
+  o.gather_two = read_env("MLORA_GATHER_TWO");
+  o.gather_two_ns = read_env("MLORA_GATHER_TWO_NS");
+  o.grouped_mb = read_env("MLORA_GROUPED_MB");
+  o.grouped_ns = read_env("MLORA_GROUPED_NS");
+  o.shrink_mb = read_env("MLORA_SHRINK_MB");
+  o.expand_mb = read_env("MLORA_EXPAND_MB");
+  o.expand_cw = read_env("MLORA_EXPAND_CW");
+  o.all_min_rows = read_env("MLORA_ALL_MIN_ROWS");
+  return o;
+}
+
+Overrides g_overrides;
+std::once_flag g_overrides_once;
+
+const Overrides& overrides() {
+  std::call_once(g_overrides_once, [] { g_overrides = read_overrides(); });
+  return g_overrides;
+}
+
+// The override `v` when set, else `dflt`.
+int ov(int v, int dflt) { return v == kUnset ? dflt : v; }
 
 uint32_t magic_for(int32_t d) { return (uint32_t)(0xFFFFFFFFu / (uint32_t)d); }
 
@@ -2139,8 +2179,8 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   while ((int64_t)E * rs * ns < target && ns * 2 <= ns_max &&
          (ns * 2) * shrink_b <= 2.0 * (shrink_b + expand_b))
     ns *= 2;
-  rs = env_int("MLORA_GATHER_RS", rs);
-  ns = env_int("MLORA_GATHER_NS", ns);
+  rs = ov(overrides().gather_rs, rs);
+  ns = ov(overrides().gather_ns, ns);
   if (ns < 1) ns = 1;
   if (ns > ns_max) ns = ns_max;
   if (rs < 1) rs = 1;
@@ -2180,10 +2220,10 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   const int grid = a.per_xcd * kXcds;
   // one 16-row block per chunk when a slice is expected to hold few rows
   const int64_t rows_per_slice = (n_slots + (int64_t)E * rs - 1) / ((int64_t)E * rs);
-  const int small = env_int("MLORA_GATHER_SMALL", rows_per_slice <= 16 ? 1 : 0);
+  const int small = ov(overrides().gather_small, rows_per_slice <= 16 ? 1 : 0);
   // weights held in registers when a slice is expected to hold at most two
   // 16-row blocks (and the wave's share fits)
-  const int resident = env_int("MLORA_GATHER_RESIDENT", rows_per_slice <= 32 ? 1 : 0);
+  const int resident = ov(overrides().gather_resident, rows_per_slice <= 32 ? 1 : 0);
   const bool use_resident = resident != 0 && gather_resident_fits(a);
   // The two-kernel form holds at most kWaves * kTwoSteps k steps per range.
   // It pays where an expert's A_e outweighs its rows' x (few rows per expert,
@@ -2199,7 +2239,7 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   const int64_t rows_e_all = (n_slots + E - 1) / E;
   const int two_default = (gather_kc(K) > 1 && rows_e_all > 6 && rows_e_all <= 64) ? 1 : 0;
   if (workspace && !use_resident && two_fits &&
-      env_int("MLORA_GATHER_TWO", two_default) != 0) {
+      ov(overrides().gather_two, two_default) != 0) {
     if (ws_need > (int64_t)kMaxBufBytes)
       return fail(MLORA_ERR_INVALID, "%s: workspace above 4 GiB; split the call", who);
     // k-split shrink, then expand; slices of at most 64 rows of an expert
@@ -2217,7 +2257,7 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
     // one workgroup per CU
     int ns2 = (ns_max + kWaves * kTwoSteps - 1) / (kWaves * kTwoSteps);
     while ((int64_t)E * rs2 * ns2 < 256 && ns2 * 2 <= ns_max) ns2 *= 2;
-    ns2 = env_int("MLORA_GATHER_TWO_NS", ns2);
+    ns2 = ov(overrides().gather_two_ns, ns2);
     if (ns2 < 1) ns2 = 1;
     if (ns2 > ns_max) ns2 = ns_max;
     if (ns_cols_for(N, ns2) > kWaves * kTwoSteps * kColStep)
@@ -2349,14 +2389,14 @@ TwoPlan two_plan(int R, int N, int64_t rows, bool pipe) {
   // 64-row shrink tiles for at most 32 ranks: A_e is read once per 64 rows
   // (measured 3.5% faster per call than 32-row tiles, 15% than 16-row ones)
   t.smb = kernel_nb(R) <= 2 ? 4 : 1;
-  t.emb = expand_mb(R, env_int("MLORA_EXPAND_MB", small_full ? 2 : 1));
-  t.cw = expand_cw(R, env_int("MLORA_EXPAND_CW", 4));
+  t.emb = expand_mb(R, ov(overrides().expand_mb, small_full ? 2 : 1));
+  t.cw = expand_cw(R, ov(overrides().expand_cw, 4));
   if (pipe) {
     // the pipe kernel takes 1 expand row block, or 2 for full rank blocks of
     // at most 32 ranks, and always its default shrink tile
     t.emb = (t.emb >= 2 && small_full) ? 2 : 1;
   } else {
-    const int w = env_int("MLORA_SHRINK_MB", t.smb);
+    const int w = ov(overrides().shrink_mb, t.smb);
     t.smb = (w >= 4 && kernel_nb(R) <= 2) ? 4 : (w >= 2 && kernel_nb(R) <= 4 ? 2 : 1);
   }
   t.sunits = (rows + 16 * t.smb - 1) / (16 * t.smb);
@@ -2405,11 +2445,19 @@ void dispatch_pipe(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipSt
 // rows beat 4 of 8192 by 10%).
 constexpr int64_t kAllMinRows = 16384;
 
+// Windows per launch for a launch minimum of `min_rows` rows.
+int64_t windows_per_launch(int64_t cap, int64_t min_rows) {
+  return cap >= min_rows ? 1 : (min_rows + cap - 1) / cap;
+}
+
+// Rows per launch: whole windows, at least the launch minimum (an override
+// may only lower it, to between 1 and kAllMinRows rows, so the workspace
+// query below covers every value).
 int64_t all_chunk_rows(int64_t n_rows, int64_t cap) {
-  int64_t min_rows = env_int("MLORA_ALL_MIN_ROWS", (int)kAllMinRows);
+  int64_t min_rows = ov(overrides().all_min_rows, (int)kAllMinRows);
   if (min_rows < 1) min_rows = 1;
-  const int64_t m = cap >= min_rows ? 1 : (min_rows + cap - 1) / cap;
-  const int64_t chunk = m > 1 ? cap * m : cap;  // m > 1 only for cap < min_rows
+  if (min_rows > kAllMinRows) min_rows = kAllMinRows;
+  const int64_t chunk = cap * windows_per_launch(cap, min_rows);
   return chunk < n_rows ? chunk : n_rows;
 }
 
@@ -2555,8 +2603,8 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
   while (tiles * (4 / mb) * ns < 512 && ns * 2 <= ns_max &&
          (ns * 2) * shrink_b <= shrink_b + expand_b)
     ns *= 2;
-  mb = env_int("MLORA_GROUPED_MB", mb);
-  ns = env_int("MLORA_GROUPED_NS", ns);
+  mb = ov(overrides().grouped_mb, mb);
+  ns = ov(overrides().grouped_ns, ns);
   if (mb != 1 && mb != 2 && mb != 4) mb = 2;
   if (mb > grouped_mb_max(R)) mb = grouped_mb_max(R);
   if (ns < 1) ns = 1;
@@ -2577,14 +2625,27 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
 extern "C" uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap,
                                                            int32_t max_rank) {
   if (n_rows <= 0 || cap <= 0 || max_rank < 1 || max_rank > 128) return 0;
-  // The call launches groups of windows, or single windows where a group
-  // would pass the 4 GiB buffer range (which depends on n_out, not known
-  // here): the larger of the two needs.
-  const int64_t chunk = all_chunk_rows(n_rows, cap);
-  const int64_t win = cap < n_rows ? cap : n_rows;
-  const int64_t by_chunk = (n_rows > chunk ? 2 : 1) * pipe_slot_bytes(chunk, max_rank);
-  const int64_t by_win = (n_rows > win ? 2 : 1) * pipe_slot_bytes(win, max_rank);
-  return (uint64_t)(by_chunk > by_win ? by_chunk : by_win);
+  // The call launches m windows at a time, m from 1 (a launch minimum of one
+  // row, or the fallback where a group would pass the 4 GiB buffer range,
+  // which depends on n_out) up to the default minimum's m_max: the largest
+  // need over every such m, without reading any override. Two slots of m
+  // windows while they cover fewer than n_rows rows (largest at the largest
+  // such m), one slot of every row otherwise.
+  const int64_t m_max = windows_per_launch(cap, kAllMinRows);
+  const int64_t n_caps = (n_rows + cap - 1) / cap;  // windows
+  int64_t need = 0;
+  const int64_t m_two = m_max < n_caps - 1 ? m_max : n_caps - 1;  // m with m * cap < n_rows
+  if (m_two >= 1) need = 2 * pipe_slot_bytes(cap * m_two, max_rank);
+  if (m_max >= n_caps) {
+    const int64_t one = pipe_slot_bytes(n_rows, max_rank);
+    if (one > need) need = one;
+  }
+  return (uint64_t)need;
+}
+
+extern "C" void mlora_reload_launch_overrides(void) {
+  overrides();  // the first read, if it has not happened yet
+  g_overrides = read_overrides();
 }
 
 extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x,

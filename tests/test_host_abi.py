@@ -330,7 +330,9 @@ def test_grouped_all_workspace_bytes(lib):
     assert f(16384, 8192, 16) == g(0, 16384, 16)      # one launch, one slot
     assert f(40000, 8192, 16) == 2 * g(0, 16384, 16)
     assert f(5000, 8192, 32) == g(0, 5000, 32)
-    assert f(100, 30, 100) == g(0, 100, 100)          # 547 windows of 30 > 100 rows
+    # 547 windows of 30 > 100 rows by default; a lower launch minimum may
+    # launch 3 windows at a time (two slots of 90 rows)
+    assert f(100, 30, 100) == 2 * g(0, 90, 100)
     assert f(70000, 6000, 16) == 2 * g(0, 18000, 16)  # three windows per launch
     assert f(100000, 20000, 16) == 2 * g(0, 20000, 16)
     # 1.5 windows: one launch of 12288 rows, or two one-window slots when a
@@ -353,13 +355,39 @@ def test_grouped_all_window_fallback_needs_the_queried_size(lib):
     assert rc == ml.MLORA_ERR_CAPACITY
 
 
-def test_grouped_all_workspace_bytes_window_per_launch(lib, monkeypatch):
-    """MLORA_ALL_MIN_ROWS=1 launches one window at a time."""
-    monkeypatch.setenv("MLORA_ALL_MIN_ROWS", "1")
-    f, g = lib.mlora_grouped_down_all_workspace_bytes, lib.mlora_grouped_down_workspace_bytes
-    assert f(32768, 8192, 32) == 2 * g(0, 8192, 32)
-    assert f(100, 30, 100) == 2 * g(0, 30, 100)
-    assert f(30, 30, 100) == g(0, 30, 100)
+def _all_needed(lib, n_rows, cap, max_rank, n_out=64):
+    """What mlora_grouped_down_all asks for under the current overrides, read
+    from its capacity error (no workspace given: nothing is launched)."""
+    import re
+    r = _route(n_out=n_out, max_rank=max_rank)
+    rc = lib.mlora_grouped_down_all(ctypes.byref(r), FAKE, 4, FAKE, n_rows, FAKE, 4, FAKE,
+                                    FAKE, 2, cap, None, 0, None)
+    assert rc == ml.MLORA_ERR_CAPACITY
+    msg = lib.mlora_last_error().decode()
+    return int(re.search(r"(\d+) needed", msg).group(1))
+
+
+@pytest.mark.parametrize("n_rows,cap,max_rank", [(32768, 8192, 32), (16384, 8192, 16),
+                                                 (100, 30, 100), (12288, 8192, 16),
+                                                 (70000, 6000, 16), (1203, 40, 48),
+                                                 (5000, 8192, 32), (100000, 20000, 16)])
+def test_grouped_all_workspace_bytes_covers_every_override(lib, overrides, n_rows, cap,
+                                                           max_rank):
+    """The size query reads no environment and covers the call under every
+    launch minimum (MLORA_ALL_MIN_ROWS, clamped to 1 .. 16384 by the call):
+    the largest of those needs is exactly the queried size."""
+    query = lib.mlora_grouped_down_all_workspace_bytes(n_rows, cap, max_rank)
+    needs = []
+    n_caps = -(-n_rows // cap)
+    for m in [None, 1, 2, 7, 30, 90, 100, 1000, 8191, 8192, 8193, 16383, 16384, 16385,
+              100000] + [cap * k for k in range(1, n_caps + 1) if cap * k <= 16384]:
+        if m is None:
+            overrides.delete("MLORA_ALL_MIN_ROWS")
+        else:
+            overrides.set("MLORA_ALL_MIN_ROWS", m)
+        assert lib.mlora_grouped_down_all_workspace_bytes(n_rows, cap, max_rank) == query
+        needs.append(_all_needed(lib, n_rows, cap, max_rank))
+    assert max(needs) == query
 
 
 def test_gather_workspace_bytes(lib):
