@@ -19,7 +19,12 @@ A row folds nothing (it is returned exactly as given) when
 * its expert id is negative or at/after the table length, or the expert's
   ``a_table`` or ``b_table`` cell is 0 (the invariant on the "moe_lora_grouped"
   index page),
-* (grouped) it lies in no span, or outside the window.
+* (grouped) it lies in no span, or outside the window, or its sorted id does
+  not name a token of ``x``: a negative id (a padding row of the router's
+  sorted output) or an id whose token ``id // top_k`` is at/after the last
+  row of ``x``. The pages do not name the sorted-row map; reading it as the
+  flat ``(token, slot)`` id, an id that names no token has no ``x`` row to
+  fold, so the row is left as given.
 
 Shapes (a reading stated with the route fields ``k_in``, ``n_out``,
 ``max_rank``): ``x [n_tokens, k_in]``, ``A_e [max_rank, k_in]``,
@@ -99,6 +104,15 @@ def _owner(r: int, offsets: Sequence[int]) -> int:
     return -1
 
 
+def _sorted_token(row_id: int, top_k: int, n_tokens: int) -> int:
+    """Token of a sorted row's flat ``(token, slot)`` id, or -1 when the id
+    names no row of ``x`` (negative, or its token is ``n_tokens`` or more)."""
+    if row_id < 0:
+        return -1
+    t = row_id // top_k
+    return t if t < n_tokens else -1
+
+
 def fold_grouped_scalar(x: np.ndarray, a_table, b_table, scale_table, mats,
                         base: np.ndarray, expert_offsets, sorted_ids, row_adapter,
                         top_k: int, row_offset: int, row_end: int) -> np.ndarray:
@@ -109,7 +123,9 @@ def fold_grouped_scalar(x: np.ndarray, a_table, b_table, scale_table, mats,
         e = _owner(r, offsets)
         if e < 0:
             continue
-        t = int(sorted_ids[r]) // top_k
+        t = _sorted_token(int(sorted_ids[r]), top_k, x.shape[0])
+        if t < 0:
+            continue
         if row_adapter[t] < 0:
             continue
         if not _cell_live(e, a_table, b_table):
@@ -136,7 +152,9 @@ def fold_grouped(x: np.ndarray, a_table, b_table, scale_table, mats, base: np.nd
         if not _cell_live(e, a_table, b_table):
             continue
         rows = np.arange(lo, hi)
-        tok = sorted_ids[rows] // top_k
+        ids = sorted_ids[rows]
+        named = (ids >= 0) & (ids // top_k < x.shape[0])
+        rows, tok = rows[named], ids[named] // top_k
         keep = row_adapter[tok] >= 0
         rows, tok = rows[keep], tok[keep]
         if rows.size == 0:

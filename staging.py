@@ -1,4 +1,5 @@
-"""Stage a seeded FoldCase on the GPU and run it through libmlora.
+"""Stage a seeded FoldCase on the GPU and run it through libmlora (used by the
+GPU tests, the smoke check and the benchmark).
 
 The tables and the per-row adapter map are built by the library's own host
 functions (so the fold runs on exactly what the boundary produces); the
@@ -64,6 +65,7 @@ class DeviceCase:
         b_addrs = np.array([addr(self.b_pool, b_stride, b) for (_, _, b, _) in c.entries],
                            dtype=np.uint64)
         scales = np.array([s for (_, _, _, s) in c.entries], dtype=np.float32)
+        self.entries_host = (ids, a_addrs, b_addrs, scales)
         packed = ml.mlora_pack_expert_tables(ids, a_addrs, b_addrs, scales)
         if packed is None:
             at, bt, st, n = (np.zeros(0, np.uint64), np.zeros(0, np.uint64),

@@ -1,20 +1,25 @@
-"""Shared test helpers: turn a seeded FoldCase into oracle inputs and results,
-and the parity metrics used by every fold comparison."""
+"""Shared test helpers: the oracle view of a seeded workload, golden fixtures,
+and the parity metrics and bound used by every fold comparison."""
 from __future__ import annotations
 
 import json
+import math
 import os
 
 import numpy as np
 
-import oracle
-from workloads import NULL_HANDLE, FoldCase
+from oracle.case import OracleView, oracle_addr, to_f64  # noqa: F401
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 # Tolerance for the bf16-in / fp32-accumulate fold against the fp64 oracle.
 REL_L2_TOL = 2e-3
 MAX_ABS_TOL = 3e-2
+
+# Arithmetic model of the fold's evaluation error (the max-abs reading):
+U32 = 2.0 ** -24    # fp32 unit roundoff
+HILO = 2.0 ** -18   # relative error of scale*H carried as bf16 hi + lo halves
+LAMBDA = 10.0       # probabilistic rounding-error bound parameter (see eval_margin)
 
 
 def golden_lines(name):
@@ -32,84 +37,6 @@ def golden_json(name):
         return json.load(f)
 
 
-def oracle_addr(kind: str, handle: int) -> int:
-    """Opaque, non-zero, distinct addresses for the oracle's tables."""
-    if handle == NULL_HANDLE:
-        return 0
-    return 2 * (handle + 1) + (0 if kind == "a" else 1)
-
-
-def to_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
-    if dtype == "bf16":
-        return oracle.bf16_to_f64(arr)
-    return np.asarray(arr, dtype=np.float32).astype(np.float64)
-
-
-class OracleView:
-    """fp64 view of a FoldCase, with the tables and maps built by the oracle."""
-
-    def __init__(self, case: FoldCase):
-        self.case = case
-        self.x = to_f64(case.x, case.dtype)
-        self.entries = [(e, oracle_addr("a", a), oracle_addr("b", b), s)
-                        for (e, a, b, s) in case.entries]
-        packed = oracle.pack_expert_tables(self.entries)
-        if packed is None:
-            self.a_table, self.b_table, self.scale_table, self.n_experts = [], [], [], 0
-        else:
-            self.a_table, self.b_table, self.scale_table, self.n_experts = packed
-        self.mats = {}
-        handles = {a for (_, a, _, _) in case.entries} | {b for (_, _, b, _) in case.entries}
-        for h in handles:
-            if h == NULL_HANDLE:
-                continue
-            self.mats[oracle_addr("a", h)] = to_f64(case.a_pool[h], case.dtype)
-            self.mats[oracle_addr("b", h)] = to_f64(case.b_pool[h], case.dtype)
-        if case.map_kind == "decode":
-            self.row_adapter = np.asarray(oracle.build_moe_row_adapter_decode(
-                case.adapter_slots, case.padded_n, case.active, case.has_moe_lora),
-                dtype=np.int32)
-        else:
-            m = oracle.build_moe_row_adapter_host(case.cu_seqlens, case.stream_slots)
-            assert m is not None
-            self.row_adapter = np.asarray(m, dtype=np.int32)
-
-    def fold(self, base=None, windows=None) -> np.ndarray:
-        c = self.case
-        base64 = to_f64(c.base if base is None else base, c.dtype)
-        if c.path == "gather":
-            return oracle.fold_gather(self.x, self.a_table, self.b_table, self.scale_table,
-                                      self.mats, base64, c.indices, self.row_adapter, c.top_k)
-        if windows is None:
-            windows = oracle.grouped_down_windows(c.n_rows, c.cap)
-        return oracle.fold_grouped_windows(self.x, self.a_table, self.b_table,
-                                           self.scale_table, self.mats, base64,
-                                           c.expert_offsets, c.sorted_ids, self.row_adapter,
-                                           c.top_k, windows)
-
-    def live_rows(self) -> np.ndarray:
-        """Boolean mask of rows that the fold writes."""
-        c = self.case
-        n = self.n_experts
-
-        def cell(e):
-            return 0 <= e < n and self.a_table[e] != 0 and self.b_table[e] != 0
-
-        live = np.zeros(c.n_rows, dtype=bool)
-        if c.path == "gather":
-            for row in range(c.n_rows):
-                live[row] = (self.row_adapter[row // c.top_k] >= 0) and cell(int(c.indices[row]))
-        else:
-            off = c.expert_offsets
-            for e in range(len(off) - 1):
-                if not cell(e):
-                    continue
-                for r in range(int(off[e]), int(off[e + 1])):
-                    if 0 <= r < c.n_rows:
-                        live[r] = self.row_adapter[int(c.sorted_ids[r]) // c.top_k] >= 0
-        return live
-
-
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     den = float(np.linalg.norm(ref))
     num = float(np.linalg.norm(got - ref))
@@ -120,21 +47,75 @@ def max_abs(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref))) if got.size else 0.0
 
 
-def ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
-    """Spacing of the output format at |ref| (bf16: 8 significant bits, fp32: 24)."""
+def ulp(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the output format at |v| (bf16: 8 significant bits, fp32: 24)."""
     bits = 8 if dtype == "bf16" else 24
-    _, e = np.frexp(np.abs(ref))  # |ref| = m * 2**e, m in [0.5, 1)
+    _, e = np.frexp(np.abs(v))  # |v| = m * 2**e, m in [0.5, 1)
     e = np.maximum(e, -125)
     return np.ldexp(1.0, e - bits)
 
 
-def max_abs_excess(got: np.ndarray, ref: np.ndarray, dtype: str) -> float:
-    """Largest ratio |got - ref| / max(MAX_ABS_TOL, ulp(ref)); <= 1 passes.
+def eval_margin(mag: np.ndarray, ref: np.ndarray, k_in: int, max_rank: int) -> np.ndarray:
+    """Bound on the evaluation error of one output element before its final
+    rounding to the output format, for a bf16-in / fp32-accumulate fold.
 
-    Reading of the max-abs bound: a value stored in bf16 can be off from the
-    exact result by half an ulp, which exceeds 3e-2 once |value| >= 8, so the
-    bound allows one output ulp where that is larger than 3e-2."""
+    The products are exact in fp32 (bf16 x bf16 has 16 significant bits).
+    The shrink sums k_in of them, the expand 2 * max_rank (hi and lo halves of
+    scale * H, which together carry H to within 2**-18 relatively), and the
+    base add is one more fp32 rounding. For a sum of n products the fp32 error
+    is at most gamma(n) times the sum of the products' absolute values; with
+    the probabilistic bound of Higham and Mary ("A new approach to
+    probabilistic rounding error analysis", SIAM J. Sci. Comput. 41(5), 2019)
+    gamma(n) <= LAMBDA * sqrt(n) * u, which fails with probability at most
+    2n exp(-LAMBDA**2 / 2) per element (below 1e-18 here) instead of the
+    deterministic n * u, which no summation of this size comes near.
+    ``mag`` is that sum of absolute values per element (oracle magnitude
+    fold); the last term covers the base add and the fp32 value's own
+    rounding before the output rounding."""
+    gam = LAMBDA * (math.sqrt(k_in) + math.sqrt(2 * max_rank)) * U32
+    return (gam + HILO + 2 * U32) * mag + 2 * U32 * np.abs(ref)
+
+
+def max_abs_limit(ref: np.ndarray, eps: np.ndarray, dtype: str) -> np.ndarray:
+    """Per element: max(3e-2, half an output ulp at |ref| + eps, plus eps).
+
+    Reading of the max-abs bound: a correctly rounded bf16 output is off from
+    the exact result by up to half an ulp, which exceeds 3e-2 once |ref| >= 8
+    (gate/up outputs reach |ref| ~ 10); a device result is rounded from an
+    fp32 value within eps of the exact one, so it may be off by half an ulp of
+    that value plus eps."""
+    return np.maximum(MAX_ABS_TOL, 0.5 * ulp(np.abs(ref) + eps, dtype) + eps)
+
+
+def max_abs_excess(got: np.ndarray, ref: np.ndarray, dtype: str, eps: np.ndarray) -> float:
+    """Largest ratio |got - ref| / max_abs_limit(ref, eps); <= 1 passes."""
     if not got.size:
         return 0.0
-    lim = np.maximum(MAX_ABS_TOL, ulp(ref, dtype))
-    return float(np.max(np.abs(got - ref) / lim))
+    return float(np.max(np.abs(got - ref) / max_abs_limit(ref, eps, dtype)))
+
+
+def view_margin(view, ref: np.ndarray, windows=None) -> np.ndarray:
+    """eval_margin for an OracleView's case (its magnitude fold, which does not
+    depend on the base and is kept on the view)."""
+    c = view.case
+    key = "_mag" if windows is None else None
+    mag = getattr(view, key, None) if key else None
+    if mag is None:
+        mag = view.magnitude(windows=windows)
+        if key:
+            setattr(view, key, mag)
+    return eval_margin(mag, ref, c.k_in, c.max_rank)
+
+
+# Observed parity figures of this process: (label, rel_l2, max_abs,
+# max_abs / limit). conftest writes them out when MLORA_PARITY_LOG is set.
+PARITY_LOG = []
+
+
+def parity_figures(view, got_f64: np.ndarray, ref: np.ndarray, label: str, windows=None):
+    """(rel_l2, max_abs, max_abs / limit) of one comparison, recorded."""
+    eps = view_margin(view, ref, windows)
+    rel, mx = rel_l2(got_f64, ref), max_abs(got_f64, ref)
+    ex = max_abs_excess(got_f64, ref, view.case.dtype, eps)
+    PARITY_LOG.append((label, rel, mx, ex))
+    return rel, mx, ex

@@ -13,8 +13,7 @@ import numpy as np
 import pytest
 
 import workloads
-from tests.common import (REL_L2_TOL, OracleView, max_abs, max_abs_excess, rel_l2,
-                          to_f64)
+from tests.common import REL_L2_TOL, OracleView, parity_figures, to_f64
 
 torch = pytest.importorskip("torch")
 
@@ -30,7 +29,7 @@ def _need_gpu():
 
 @functools.lru_cache(maxsize=None)
 def staged(name):
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     case = workloads.WORKLOADS[name]()
     return case, OracleView(case), DeviceCase(case, DEV)
 
@@ -44,11 +43,10 @@ def put_sentinel(base, rows, dtype):
         base.view(np.uint32)[rows] = 0x7F800001
 
 
-def check(view, got, base, label):
-    ref = view.fold(base=base)
+def check(view, got, base, label, windows=None):
+    ref = view.fold(base=base, windows=windows)
     g = to_f64(got, view.case.dtype)
-    rel, mx = rel_l2(g, ref), max_abs(g, ref)
-    ex = max_abs_excess(g, ref, view.case.dtype)
+    rel, mx, ex = parity_figures(view, g, ref, label, windows)
     print(f"{label}: rel_l2={rel:.3e} max_abs={mx:.3e} max_abs/limit={ex:.3f}", flush=True)
     assert rel <= REL_L2_TOL, f"{label}: rel L2 {rel}"
     assert ex <= 1.0, f"{label}: max abs {mx} (ratio to limit {ex})"
@@ -64,17 +62,30 @@ ALL = ["tiny_gather_f32", "decode_down_gather", "prefill_grouped_down", "gateup_
 
 @pytest.mark.parametrize("name", ALL)
 def test_integer_maps_and_tables_bit_exact(name):
+    """The map and windows from the library equal the oracle's; the device
+    tables hold, cell for cell, the oracle's packing of the same entries with
+    the real device addresses of the weights (address and scale bits)."""
+    import oracle
     _need_gpu()
     case, view, dev = staged(name)
     assert dev.row_adapter_host.tolist() == view.row_adapter.tolist()
+    ids, a_addrs, b_addrs, scales = dev.entries_host
+    packed = oracle.pack_expert_tables(
+        [(int(e), int(a), int(b), float(s)) for e, a, b, s in zip(ids, a_addrs, b_addrs, scales)])
+    oa, ob, os_, on = packed
     at, bt, st, n = dev.tables_host
-    assert n == view.n_experts
-    # same cells null / non-null, same scales bit for bit
+    assert n == on == view.n_experts
+    dev_a = dev.a_table.cpu().numpy().view(np.uint64)[:n]
+    dev_b = dev.b_table.cpu().numpy().view(np.uint64)[:n]
+    dev_s = dev.scale_table.cpu().numpy()[:n]
+    assert dev_a.tolist() == at.tolist() == [int(v) for v in oa]
+    assert dev_b.tolist() == bt.tolist() == [int(v) for v in ob]
+    want_s = np.asarray(os_, dtype=np.float32).view(np.uint32).tolist()
+    assert dev_s.view(np.uint32).tolist() == st.view(np.uint32).tolist() == want_s
+    # null cells where the oracle's own view (opaque addresses) has them
     assert [int(v != 0) for v in at] == [int(v != 0) for v in view.a_table]
     assert [int(v != 0) for v in bt] == [int(v != 0) for v in view.b_table]
-    assert st.view(np.uint32).tolist() == np.asarray(view.scale_table, np.float32).view(np.uint32).tolist()
     if case.path == "grouped":
-        import oracle
         assert dev.windows == oracle.grouped_down_windows(case.n_rows, case.cap)
 
 
@@ -119,7 +130,7 @@ def test_deterministic(name):
 def test_grouped_equals_gather_permuted():
     """Grouped row r equals gather row sorted_ids[r], bit for bit (same inputs)."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     g = workloads.make_grouped_case(71, stream_lens=[300, 97, 211], top_k=4, n_route=24,
                                     k_in=256, n_out=512, max_rank=32, routing="zipf",
                                     n_unadapted=4, cap=200, stream_slot_values=[1, -1, 1])
@@ -149,7 +160,7 @@ def test_windows_equal_single_window():
 def test_scale_power_of_two_is_exact():
     """Z run: scaling every scale by 4 scales every output by 4, bit for bit."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     c1 = workloads.make_gather_case(72, n_seq=40, padded_n=48, top_k=4, n_route=16, k_in=320,
                                     n_out=384, max_rank=16, skip_seqs=3)
     c1.base = np.zeros_like(c1.base)
@@ -163,7 +174,7 @@ def test_scale_power_of_two_is_exact():
 
 def test_b_zero_leaves_base():
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     c = workloads.make_grouped_case(73, stream_lens=[90, 70], top_k=2, n_route=8, k_in=128,
                                     n_out=256, max_rank=16, cap=64)
     c.b_pool = np.zeros_like(c.b_pool)
@@ -175,7 +186,7 @@ def test_integer_inputs_bit_exact():
     """Inputs in {-1, 0, 1}, scales in {1/2, 1, 2}: every partial sum is exact
     in fp32 and bf16, so the device result equals the oracle exactly."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     rng = np.random.default_rng(74)
     for path in ("gather", "grouped"):
         if path == "gather":
@@ -213,7 +224,7 @@ def test_integer_inputs_bit_exact():
 def test_rank1_onehot_closed_form():
     """One-hot x rows and rank 1: delta = scale * A[0, i] * B[:, 0]."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     c = workloads.make_gather_case(77, n_seq=20, padded_n=20, top_k=2, n_route=5, k_in=64,
                                    n_out=96, max_rank=1)
     hot = np.random.default_rng(78).integers(0, 64, size=c.x.shape[0])
@@ -297,7 +308,7 @@ def build_small(label, kw):
 @pytest.mark.parametrize("label,kw", SMALL, ids=[s[0] for s in SMALL])
 def test_small_cases(label, kw):
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     c = build_small(label, kw)
     view = OracleView(c)
     dev = DeviceCase(c, DEV)
@@ -321,7 +332,7 @@ def test_grouped_two_kernel_equals_one_kernel(label):
     grouped fold give the same bits, and the one-kernel form passes the
     oracle bar on its own (the other tests run the two-kernel form)."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     if label in workloads.WORKLOADS:
         case, view, dev = staged(label)
     else:
@@ -334,12 +345,12 @@ def test_grouped_two_kernel_equals_one_kernel(label):
 
 
 @pytest.mark.parametrize("label", ["prefill_grouped_down", "mixed_grouped"] + [s[0] for s in GROUPED_SMALL])
-def test_grouped_launch_shapes_give_the_same_bits(label, monkeypatch):
+def test_grouped_launch_shapes_give_the_same_bits(label, overrides):
     """Shrink tiles of 16, 32 or 64 rows and expand waves of 16 or 32 rows
     (MLORA_SHRINK_MB / MLORA_EXPAND_MB) change which workgroup computes a row,
     not how: every shape gives the bits of the default per-window call."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     if label in workloads.WORKLOADS:
         case, view, dev = staged(label)
     else:
@@ -347,8 +358,8 @@ def test_grouped_launch_shapes_give_the_same_bits(label, monkeypatch):
         view, dev = OracleView(case), DeviceCase(case, DEV)
     ref = dev.run(two_kernel=True, pipelined=False)
     for smb, emb in [("1", "1"), ("2", "2"), ("4", "1"), ("1", "2")]:
-        monkeypatch.setenv("MLORA_SHRINK_MB", smb)
-        monkeypatch.setenv("MLORA_EXPAND_MB", emb)
+        overrides.set("MLORA_SHRINK_MB", smb)
+        overrides.set("MLORA_EXPAND_MB", emb)
         got = dev.run(two_kernel=True, pipelined=False)
         assert np.array_equal(ref.view(np.uint8), got.view(np.uint8)), (smb, emb)
 
@@ -362,7 +373,7 @@ def test_gather_one_kernel_form(label):
     the other tests give it a workspace, which large calls use for the
     two-kernel form."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     if label in workloads.WORKLOADS:
         case, view, dev = staged(label)
     else:
@@ -391,14 +402,14 @@ def _two_gather_case(label):
 
 
 @pytest.mark.parametrize("label", TWO_GATHER)
-def test_gather_two_kernel_form(label, monkeypatch):
+def test_gather_two_kernel_form(label, overrides):
     """The two-kernel gather (k-split shrink into the workspace, then expand),
     forced on: oracle bar on a random and a zero base, untouched rows bit
     for bit. k_in 1000 and 2048 split into 2 and 4 k ranges."""
     _need_gpu()
-    from tests.device import DeviceCase
-    monkeypatch.setenv("MLORA_GATHER_TWO", "1")
-    monkeypatch.setenv("MLORA_GATHER_RESIDENT", "0")
+    from staging import DeviceCase
+    overrides.set("MLORA_GATHER_TWO", "1")
+    overrides.set("MLORA_GATHER_RESIDENT", "0")
     case = _two_gather_case(label)
     view, dev = OracleView(case), DeviceCase(case, DEV)
     check(view, dev.run(two_kernel=True), case.base, f"{label} two-kernel")
@@ -414,14 +425,14 @@ def test_gather_two_kernel_form(label, monkeypatch):
 
 @pytest.mark.parametrize("min_rows", [None, "1"], ids=["launch16k", "launch1win"])
 @pytest.mark.parametrize("label", ["prefill_grouped_down", "mixed_grouped"] + [s[0] for s in GROUPED_SMALL])
-def test_grouped_all_windows_pipelined_equals_per_window(label, min_rows, monkeypatch):
+def test_grouped_all_windows_pipelined_equals_per_window(label, min_rows, overrides):
     """mlora_grouped_down_all (launch l + 1's windows shrunk in the launch that
     expands launch l's) equals one mlora_grouped_down call per window, bit for
     bit, with launches of >= 16384 rows (the default) and of one window."""
     _need_gpu()
     if min_rows:
-        monkeypatch.setenv("MLORA_ALL_MIN_ROWS", min_rows)
-    from tests.device import DeviceCase
+        overrides.set("MLORA_ALL_MIN_ROWS", min_rows)
+    from staging import DeviceCase
     if label in workloads.WORKLOADS:
         case, view, dev = staged(label)
     else:
@@ -433,13 +444,13 @@ def test_grouped_all_windows_pipelined_equals_per_window(label, min_rows, monkey
 
 
 @pytest.mark.parametrize("min_rows", ["1", "120", None])
-def test_grouped_all_many_small_windows(min_rows, monkeypatch):
+def test_grouped_all_many_small_windows(min_rows, overrides):
     """Many windows (cap 40 over 1203 rows), launched one window at a time,
     three windows at a time, or all at once: both workspace slots alternate."""
     _need_gpu()
     if min_rows:
-        monkeypatch.setenv("MLORA_ALL_MIN_ROWS", min_rows)
-    from tests.device import DeviceCase
+        overrides.set("MLORA_ALL_MIN_ROWS", min_rows)
+    from staging import DeviceCase
     case = workloads.make_grouped_case(95, stream_lens=[200, 101], top_k=4, n_route=9,
                                        k_in=320, n_out=264, max_rank=24, routing="zipf",
                                        n_unadapted=2, cap=40, stream_slot_values=[1, 1])
@@ -450,11 +461,49 @@ def test_grouped_all_many_small_windows(min_rows, monkeypatch):
                           dev.run(two_kernel=True, pipelined=False).view(np.uint8))
 
 
+UNNAMED = [
+    ("bf16_r32", dict(stream_lens=[300, 211, 97], top_k=4, n_route=24, k_in=320, n_out=272,
+                      max_rank=32, routing="zipf", n_unadapted=4, cap=256)),
+    ("bf16_r16", dict(stream_lens=[150, 77], top_k=8, n_route=40, k_in=256, n_out=520,
+                      max_rank=16, n_unadapted=9, cap=300)),
+    ("bf16_r48", dict(stream_lens=[64, 65], top_k=2, n_route=9, k_in=136, n_out=96,
+                      max_rank=48, n_unadapted=2, cap=100)),
+    ("f32", dict(stream_lens=[31, 20], top_k=4, n_route=12, k_in=64, n_out=40, max_rank=8,
+                 dtype="f32", n_unadapted=2, cap=64)),
+]
+
+
+@pytest.mark.parametrize("form", ["one_kernel", "two_kernel", "pipelined", "pipelined_1win"])
+@pytest.mark.parametrize("label,kw", UNNAMED, ids=[u[0] for u in UNNAMED])
+def test_grouped_unnamed_rows(label, kw, form, overrides):
+    """Sorted rows that name no token (id -1, an id at/after n_tokens * top_k)
+    inside spans, and rows before the first span and after the last one, fold
+    nothing in every grouped form: they keep a signalling-NaN sentinel bit
+    for bit, and every other row meets the bound."""
+    from staging import DeviceCase
+    _need_gpu()
+    c = workloads.make_grouped_case(71, **kw)
+    u = workloads.with_unnamed_rows(c, 71, lead=37, tail=29, bad_frac=0.15)
+    assert (u.sorted_ids < 0).any() and (u.sorted_ids >= u.n_tokens * u.top_k).any()
+    view, dev = OracleView(u), DeviceCase(u, DEV)
+    if form == "pipelined_1win":
+        overrides.set("MLORA_ALL_MIN_ROWS", 1)
+    two = form != "one_kernel"
+    pipe = form.startswith("pipelined")
+    live = view.live_rows()
+    assert (~live).sum() > 66
+    base = u.base.copy()
+    put_sentinel(base, ~live, u.dtype)
+    got = dev.run(base, two_kernel=two, pipelined=pipe)
+    assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
+    check(view, dev.run(two_kernel=two, pipelined=pipe), u.base, f"{label} unnamed {form}")
+
+
 def test_grouped_workspace_reused_across_windows_and_calls():
     """One workspace serves successive windows and calls; stale contents from a
     larger call never leak into a smaller one."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     big = workloads.make_grouped_case(91, stream_lens=[300, 211], top_k=4, n_route=12,
                                       k_in=256, n_out=384, max_rank=32, routing="zipf",
                                       n_unadapted=2, cap=256)
@@ -473,12 +522,12 @@ def test_grouped_workspace_reused_across_windows_and_calls():
 
 @pytest.mark.parametrize("label", ["decode_down_gather", "gather_r24_k72", "gather_slots_not_multiple",
                                    "gather_r16_ns4"])
-def test_resident_weights_path_equals_streaming_path(label, monkeypatch):
+def test_resident_weights_path_equals_streaming_path(label, overrides):
     """The decode path that holds a wave's weights in registers and the
     streaming path fold in the same order: outputs equal bit for bit, and the
     resident one passes the oracle bar on its own."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     if label == "decode_down_gather":
         case, view, dev = staged(label)
     elif label == "gather_r16_ns4":
@@ -491,23 +540,23 @@ def test_resident_weights_path_equals_streaming_path(label, monkeypatch):
         view, dev = OracleView(case), None
     dev = dev or DeviceCase(case, DEV)
     if label == "gather_r16_ns4":
-        monkeypatch.setenv("MLORA_GATHER_NS", "4")
-    monkeypatch.setenv("MLORA_GATHER_RESIDENT", "1")
+        overrides.set("MLORA_GATHER_NS", "4")
+    overrides.set("MLORA_GATHER_RESIDENT", "1")
     res = dev.run()
     check(view, res, case.base, f"{label} resident")
-    monkeypatch.setenv("MLORA_GATHER_RESIDENT", "0")
+    overrides.set("MLORA_GATHER_RESIDENT", "0")
     stream = dev.run(two_kernel=False)
     assert np.array_equal(res.view(np.uint8), stream.view(np.uint8))
 
 
 @pytest.mark.parametrize("n_seq,form", [(64, "one"), (96, "one"), (128, "two")])
-def test_gather_planner_default_form(n_seq, form, monkeypatch):
+def test_gather_planner_default_form(n_seq, form, overrides):
     """With a workspace, a gather whose experts average at most 6 rows (k_in
     2048, rank 16: no register-resident form) runs as one kernel, from 7 rows
     on as the k-split pair. The two forms add the k ranges in different orders,
     so the default call's bits show which one ran; both pass the oracle bar."""
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     case = workloads.make_gather_case(90 + n_seq, n_seq=n_seq, padded_n=n_seq, top_k=8,
                                       n_route=128, k_in=2048, n_out=768, max_rank=16,
                                       name=f"planner_{n_seq}")
@@ -516,9 +565,9 @@ def test_gather_planner_default_form(n_seq, form, monkeypatch):
     check(view, got, case.base, f"{case.name} default")
     forced = {}
     for f, two in (("one", "0"), ("two", "1")):
-        monkeypatch.setenv("MLORA_GATHER_TWO", two)
+        overrides.set("MLORA_GATHER_TWO", two)
         forced[f] = dev.run()
-    monkeypatch.delenv("MLORA_GATHER_TWO")
+    overrides.delete("MLORA_GATHER_TWO")
     assert not np.array_equal(forced["one"], forced["two"])
     assert np.array_equal(got.view(np.uint8), forced[form].view(np.uint8))
 
@@ -526,7 +575,7 @@ def test_gather_planner_default_form(n_seq, form, monkeypatch):
 def test_guard_bands_untouched():
     """Fold into a slice of a larger buffer: the bytes around it stay as they were."""
     _need_gpu()
-    from tests.device import DeviceCase, from_torch, to_torch
+    from staging import DeviceCase, from_torch, to_torch
     c = workloads.make_grouped_case(79, stream_lens=[120], top_k=4, n_route=10, k_in=128,
                                     n_out=256, max_rank=32, cap=100)
     dev = DeviceCase(c, DEV)
@@ -546,7 +595,7 @@ def test_guard_bands_untouched():
 
 def test_empty_calls_enqueue_nothing():
     _need_gpu()
-    from tests.device import DeviceCase
+    from staging import DeviceCase
     c = workloads.make_grouped_case(81, stream_lens=[40], top_k=2, n_route=4, k_in=64,
                                     n_out=64, max_rank=16, cap=64)
     dev = DeviceCase(c, DEV)
@@ -559,7 +608,7 @@ def test_graph_replay_reads_routing_on_device():
     replay after the routing (indices, map) and table cells are rewritten in
     place uses the new contents: the host never reads routing data."""
     _need_gpu()
-    from tests.device import DeviceCase, from_torch, to_torch
+    from staging import DeviceCase, from_torch, to_torch
     c = workloads.make_gather_case(82, n_seq=48, padded_n=56, top_k=4, n_route=16, k_in=256,
                                    n_out=320, max_rank=16, n_adapted=12, skip_seqs=4)
     dev = DeviceCase(c, DEV)
@@ -603,16 +652,16 @@ def test_graph_replay_reads_routing_on_device():
 
 @pytest.mark.parametrize("form", ["grouped_all", "grouped_all_per_window", "grouped_window",
                                   "gather_two"])
-def test_graph_replay_workspace_forms(form, monkeypatch):
+def test_graph_replay_workspace_forms(form, overrides):
     """The workspace forms captured in a HIP graph: every replay (with eager
     work and syncs between) equals the eager fold bit for bit, and a replay
     after the map and one table cell are rewritten in place folds by the new
     contents."""
     _need_gpu()
-    from tests.device import DeviceCase, from_torch, to_torch
+    from staging import DeviceCase, from_torch, to_torch
     if form == "gather_two":
-        monkeypatch.setenv("MLORA_GATHER_TWO", "1")
-        monkeypatch.setenv("MLORA_GATHER_RESIDENT", "0")
+        overrides.set("MLORA_GATHER_TWO", "1")
+        overrides.set("MLORA_GATHER_RESIDENT", "0")
         c = workloads.make_gather_case(86, n_seq=40, padded_n=48, top_k=4, n_route=10,
                                        k_in=1024, n_out=256, max_rank=32, n_adapted=8,
                                        skip_seqs=3)
@@ -623,7 +672,7 @@ def test_graph_replay_workspace_forms(form, monkeypatch):
                                         n_unadapted=2, cap=300, stream_slot_values=[1, 1, 1])
         if form == "grouped_all_per_window":
             # one window per launch: the pipe kernel runs inside the graph
-            monkeypatch.setenv("MLORA_ALL_MIN_ROWS", "1")
+            overrides.set("MLORA_ALL_MIN_ROWS", "1")
         dev = DeviceCase(c, DEV, pipelined=form.startswith("grouped_all"))
         assert len(dev.windows) > 1
     dev.workspace_for(getattr(dev, "windows", None))   # allocated before capture

@@ -272,6 +272,38 @@ def make_grouped_case(seed: int, *, stream_lens, top_k: int, n_route: int, k_in:
     return c
 
 
+def with_unnamed_rows(case: FoldCase, seed: int, lead: int, tail: int,
+                      bad_frac: float) -> FoldCase:
+    """A grouped case whose sorted rows also hold rows that name no token, as a
+    router's padded sorted output does: ``lead`` rows before the first span and
+    ``tail`` rows after the last one (ids drawn from -1, a valid id, or an id
+    past the last token), and a ``bad_frac`` share of the rows inside the
+    spans whose id is replaced by -1 or by an id at/after
+    ``n_tokens * top_k``. Offsets shift by ``lead``; base_out grows to match
+    (fresh draws for the new rows). Only routing and base rows change."""
+    assert case.path == "grouped"
+    rng = np.random.default_rng([seed, 7])
+    n_flat = case.n_tokens * case.top_k
+    ids = case.sorted_ids.astype(np.int64).copy()
+    bad = rng.random(ids.shape[0]) < bad_frac
+    wild = rng.choice(np.array([-1, n_flat, n_flat + case.top_k, n_flat + 12345]),
+                      size=ids.shape[0])
+    ids = np.where(bad, wild, ids)
+    pool = np.array([-1, 0, n_flat - 1, n_flat, 2 ** 30])
+    lead_ids = rng.choice(pool, size=lead)
+    tail_ids = rng.choice(pool, size=tail)
+    new_ids = np.concatenate([lead_ids, ids, tail_ids]).astype(np.int32)
+    offsets = (case.expert_offsets.astype(np.int64) + lead).astype(np.int32)
+    extra_lead = _values(rng, (lead, case.n_out), 1.0, case.dtype)
+    extra_tail = _values(rng, (tail, case.n_out), 1.0, case.dtype)
+    base = np.concatenate([extra_lead, case.base, extra_tail], axis=0)
+    c = case.with_base(base)
+    c.sorted_ids = new_ids
+    c.expert_offsets = offsets
+    c.name = case.name + "_unnamed"
+    return c
+
+
 # ----------------------------------------------------------------------------
 # the workloads measured and checked at full size
 # ----------------------------------------------------------------------------
