@@ -2,31 +2,37 @@
 
 One step = one pass of the fold over one synthetic batch: for the decode
 workloads one mlora_gather_bgmv call, for the prefill workloads one
-mlora_grouped_down call per window of grouped_down_windows. The host-side
-integer work (tables, maps, windows) is done once before timing, as an engine
-does at adapter install / batch setup; its cost is reported separately.
-Steps are captured in a HIP graph and replayed (the fold reads its routing on
-the device precisely so that it can be captured); eager launch cost, which
-the host launch path dominates for the small decode calls, is reported too.
+mlora_grouped_down_all call over every window of grouped_down_windows (with
+--one-kernel: one mlora_grouped_down call per window). The host-side integer
+work (tables, maps, windows) is done once before timing, as an engine does at
+adapter install / batch setup; its cost is reported separately. Steps are
+captured in HIP graphs and replayed (the fold reads its routing on the device
+precisely so that it can be captured); eager launch cost is reported too.
 
-Inputs are resident in HBM before timing starts. The step cycles through
+Inputs are resident in HBM before timing starts. The steps cycle through
 `copies` independent copies of x, A, B, base_out and the tables, so each step
-reads data that no recent step touched (more bytes than L2 + MALL hold):
-the figures are cold-cache HBM figures.
+reads data that no recent step touched (more bytes than L2 + MALL hold): the
+figures are cold-cache HBM figures. Exactly --steps steps are timed.
 
-Prints ONE JSON line (rank 0, N = 1):
-  value      rows folded per second (rows covered by the calls / wall time)
-  roofline   algorithmic bytes per launch / mean launch duration (HIP events)
-             against the 8 TB/s HBM peak; traffic = counter-measured HBM bytes
-             from the committed rocprofv3 summary when the kernel source still
-             matches it, else null
-  cpu_baseline  the fp64 CPU oracle timed on the host on a bounded sample
-  also       (default run) the prefill grouped workload measured the same way:
-             value, ms_per_step, config and roofline of its own
-  warm_launch_us  the same call replayed on one copy, inputs resident in L2 /
-             MALL (context only: every other figure is cold HBM)
+Prints ONE JSON line (rank 0, N = 1) for the decode workload, with every other
+full-size workload measured the same way under "also":
+  value         rows covered per second (rows covered by the calls / wall time)
+  roofline      algorithmic bytes per step / mean step time (HIP events on the
+                replay stream) against the 8 TB/s HBM peak; a grouped step's
+                bytes are counted per launch group of the all-windows call
+                (also given per window); traffic = counter-measured HBM bytes
+                per step from profiles/traffic.json when the kernel source
+                still matches it, else null
+  cpu_baseline  the fp64 CPU oracle timed on the host on a bounded sample,
+                with the threads it used, the CPUs available and the model
+  config        workload, rows, windows, kernel dispatches per step (counted
+                in a captured step), copies
+  copy_floor    torch's device copy moving the same bytes in one launch,
+                replayed the same way: what one launch of that size streams
+  warm_step_us  the same step replayed on one copy, inputs resident in L2 /
+                MALL (context only: every other figure is cold HBM)
   hbm_copy_gbs  read + write GB/s of a plain 1 GiB device copy: a practical
-             HBM figure for context (the roofline uses the nominal 8 TB/s)
+                HBM figure for context (the roofline uses the nominal 8 TB/s)
 """
 from __future__ import annotations
 
@@ -47,6 +53,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-LoRA fold rows/s + achieved HBM GB/s (decode gather, prefill grouped)"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "decode_down_gather"
+# the workloads a default run measures: the decode line and, beside it, every
+# other full-size workload (the tiny fp32 one is a parity case only)
+MEASURED = ["decode_down_gather", "prefill_grouped_down", "gateup_gather", "router_gather",
+            "mixed_grouped"]
 KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_lora_amd", "csrc", "mlora_fold.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -81,13 +91,26 @@ def kernel_hash() -> str:
 # algorithmic bytes: what the fold must move, counted from the inputs
 # ---------------------------------------------------------------------------
 
-def algorithmic_traffic(case, tables, row_adapter):
-    """(bytes, flops, rows, folded_rows) per step, summed over launches.
+def all_windows_groups(n_rows, cap, min_rows=16384):
+    """Row ranges of the launches of mlora_grouped_down_all (its header): whole
+    windows of `cap` rows, at least `min_rows` rows per launch."""
+    m = 1 if cap >= min_rows else -(-min_rows // cap)
+    chunk = cap * m
+    return [(s, min(s + chunk, n_rows)) for s in range(0, n_rows, chunk)]
 
+
+def algorithmic_traffic(case, tables, row_adapter, groups=None):
+    """(bytes, flops, rows, folded_rows, units) per step, summed over units.
+
+    A unit is one call's worth of rows that reads its own operands: the whole
+    call for a gather, and for a grouped step each row range of `groups`
+    (default: the windows of grouped_down_windows). Per unit:
     bytes = unique tokens * k_in * 2 + unique experts * (r*k_in + n_out*r) * 2
           + folded rows * n_out * 2 * 2 (base_out read + write)
           + 4 * rows (indices / sorted_ids) + 4 * tokens (map)
           + 4 * (n_route + 1) (offsets, grouped) + 20 * n_experts (tables)
+    A grouped row folds when it lies in an adapted expert's span and its
+    sorted id names a token whose map entry is >= 0.
     """
     at, bt, _, n_exp = tables
     elt = 2 if case.dtype == "bf16" else 4
@@ -100,29 +123,33 @@ def algorithmic_traffic(case, tables, row_adapter):
     def cell_ok(e):
         return (e >= 0) & (e < n_exp) & live_cell[np.clip(e, 0, max(n_exp - 1, 0))]
 
-    launches = []
+    units = []
     if case.path == "gather":
         rows = np.arange(case.n_rows)
         tok = rows // case.top_k
         e = case.indices.astype(np.int64)
         live = (ra[tok] >= 0) & cell_ok(e)
-        launches.append((case.n_rows, tok[live], e[live], 0))
+        units.append((case.n_rows, tok[live], e[live], 0))
     else:
         off = case.expert_offsets.astype(np.int64)
         owner = np.searchsorted(off, np.arange(case.n_rows), side="right") - 1
-        tok_all = case.sorted_ids.astype(np.int64) // case.top_k
+        ids = case.sorted_ids.astype(np.int64)
+        named = (ids >= 0) & (ids // case.top_k < case.n_tokens)
+        tok_all = np.where(named, ids // case.top_k, 0)
         inside = (owner >= 0) & (owner < len(off) - 1)
-        import moe_expert_lora_amd as ml
-        for (s, t) in ml.mlora_grouped_down_windows(case.n_rows, case.cap):
+        if groups is None:
+            import moe_expert_lora_amd as ml
+            groups = ml.mlora_grouped_down_windows(case.n_rows, case.cap)
+        for (s, t) in groups:
             o = owner[s:t]
             tk = tok_all[s:t]
-            live = inside[s:t] & cell_ok(o) & (ra[np.clip(tk, 0, len(ra) - 1)] >= 0)
-            launches.append((t - s, tk[live], o[live], case.n_route + 1))
+            live = inside[s:t] & named[s:t] & cell_ok(o) & (ra[np.clip(tk, 0, len(ra) - 1)] >= 0)
+            units.append((t - s, tk[live], o[live], case.n_route + 1))
     total_b = 0
     flops = 0
     folded = 0
     rows_total = 0
-    for (rows, toks, exps, n_off) in launches:
+    for (rows, toks, exps, n_off) in units:
         f = toks.shape[0]
         b = (np.unique(toks).size * K * elt + np.unique(exps).size * (R * K + N * R) * elt
              + f * N * elt * 2 + 4 * rows + 4 * case.n_tokens + 4 * n_off + 20 * n_exp)
@@ -130,7 +157,7 @@ def algorithmic_traffic(case, tables, row_adapter):
         flops += 2 * f * R * (K + N)
         folded += f
         rows_total += rows
-    return total_b, flops, rows_total, folded, len(launches)
+    return total_b, flops, rows_total, folded, len(units)
 
 
 # ---------------------------------------------------------------------------
@@ -140,7 +167,7 @@ def algorithmic_traffic(case, tables, row_adapter):
 class Staged:
     def __init__(self, case, copies, device="cuda", two_kernel=True):
         import torch
-        from tests.device import DeviceCase
+        from staging import DeviceCase
         self.case = case
         self.primary = DeviceCase(case, device, two_kernel=two_kernel)
         if two_kernel:
@@ -156,7 +183,7 @@ class Staged:
         """Same data at new addresses (weights, x, base_out and the tables)."""
         import copy
         import moe_expert_lora_amd as ml
-        from tests.device import u64_to_device
+        from staging import u64_to_device
         p = self.primary
         c = copy.copy(p)
         c.x = p.x.clone()
@@ -189,52 +216,75 @@ def copy_bytes(case):
 # CPU baseline: the fp64 oracle on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(case, budget_s=10.0):
-    from tests.common import OracleView
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    view = OracleView(case)
-    base64 = None
-    from tests.common import to_f64
-    base64 = to_f64(case.base, case.dtype)
-    import oracle
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
+
+def cpu_threads():
+    """Host threads the CPU leg uses: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS when that is set (the host's share of cores)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return n
+
+
+def cpu_baseline(case, budget_s=10.0):
+    """The fp64 oracle (per-expert NumPy matmuls) timed on the host: rows
+    covered per second and the algorithmic bytes of the sample per second."""
+    import oracle
+    from oracle.case import OracleView, to_f64
+    from threadpoolctl import threadpool_limits
+
+    threads = cpu_threads()
+    view = OracleView(case)
+    base64 = to_f64(case.base, case.dtype)
+    tables = (np.asarray(view.a_table, np.uint64), np.asarray(view.b_table, np.uint64),
+              None, view.n_experts)
     if case.path == "gather":
         def run():
             return oracle.fold_gather(view.x, view.a_table, view.b_table, view.scale_table,
                                       view.mats, base64, case.indices, view.row_adapter,
                                       case.top_k)
         rows_per = case.n_rows
-        sample = f"full {case.name} fold ({rows_per} rows) repeated"
+        groups = None
+        sample = f"the full {case.name} call ({rows_per} rows)"
     else:
         # bounded sample: the first window
-        import moe_expert_lora_amd as ml
-        s, e = ml.mlora_grouped_down_windows(case.n_rows, case.cap)[0]
+        s, e = oracle.grouped_down_windows(case.n_rows, case.cap)[0]
 
         def run():
             return oracle.fold_grouped(view.x, view.a_table, view.b_table, view.scale_table,
                                        view.mats, base64, case.expert_offsets, case.sorted_ids,
                                        view.row_adapter, case.top_k, s, e)
         rows_per = e - s
-        sample = f"first window [{s}, {e}) of {case.name}, repeated"
-    run()  # warm-up
-    t0 = time.perf_counter()
-    iters = 0
-    while True:
-        run()
-        iters += 1
-        el = time.perf_counter() - t0
-        if (el >= budget_s and iters >= 3) or el >= 3 * budget_s:
-            break
+        groups = [(s, e)]
+        sample = f"the first window [{s}, {e}) of {case.name}"
+    sample_bytes = algorithmic_traffic(case, tables, view.row_adapter, groups)[0]
+    with threadpool_limits(limits=threads):
+        run()  # warm-up
+        t0 = time.perf_counter()
+        iters = 0
+        while True:
+            run()
+            iters += 1
+            el = time.perf_counter() - t0
+            if (el >= budget_s and iters >= 3) or el >= 3 * budget_s:
+                break
     return {"value": rows_per * iters / el, "unit": "rows/s", "cores": int(threads),
-            "kind": "oracle", "sample": f"{sample} {iters}x in {el:.1f} s (fp64 NumPy, "
-                                         "per-expert matmuls)"}
-
-
-# ---------------------------------------------------------------------------
+            "kind": "oracle",
+            "sample": f"{sample}, {iters}x in {el:.1f} s (fp64 NumPy, per-expert matmuls, "
+                      f"BLAS limited to {threads} threads)",
+            "gbs": sample_bytes * iters / el / 1e9,
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
 
 
 # ---------------------------------------------------------------------------
@@ -323,31 +373,30 @@ def _tables_and_map(case):
 
 
 def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
-    """Per-launch HBM bytes of the fold from FETCH_SIZE / WRITE_SIZE runs (KiB per
-    dispatch), each scaled by what the counter reads for the plain copy of
-    CALIB_BYTES; recorded in profiles/traffic.json with the kernel hash.
+    """Per-step HBM bytes of the fold from FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch) of `bench.py --counters`, each scaled by what the counter reads
+    for the plain copy of CALIB_BYTES; recorded in profiles/traffic.json with
+    the kernel hash.
 
-    A step is one or more fold kernels (a shrink and an expand; the pipelined
-    grouped call adds one launch per later group of windows). Every kernel runs at least
-    once per step, so the least frequent one counts the steps, and the
-    per-launch figure is the counters summed over all fold dispatches divided
-    by steps x launches per step (windows, for grouped workloads)."""
+    A step runs one or more fold kernels (a shrink and an expand; the
+    pipelined grouped call adds one launch per later group of windows).
+    Every kernel runs at least once per step, so the least frequent one
+    counts the steps, and the per-step figure is the counters summed over all
+    fold dispatches divided by that count."""
     is_copy = lambda n: "mlora" not in n  # noqa: E731
     rows_f, rows_w = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     names = sorted({r["Kernel_Name"] for r in rows_f + rows_w if "mlora" in r["Kernel_Name"]})
-    import workloads
-    case = workloads.WORKLOADS[workload]()
-    launches = algorithmic_traffic(case, *_tables_and_map(case))[4]
 
-    def per_launch(rows, counter):
+    def per_step(rows, counter):
         vals = {n: [float(r["Counter_Value"]) for r in rows
                     if r["Counter_Name"] == counter and r["Kernel_Name"] == n] for n in names}
+        vals = {n: v for n, v in vals.items() if v}
         steps = min(len(v) for v in vals.values())
         total = sum(sum(v) for v in vals.values())
-        return total / (steps * launches), [len(v) for v in vals.values()]
+        return total / steps, [len(v) for v in vals.values()]
 
-    f_kib, nf = per_launch(rows_f, "FETCH_SIZE")
-    w_kib, nw = per_launch(rows_w, "WRITE_SIZE")
+    f_kib, nf = per_step(rows_f, "FETCH_SIZE")
+    w_kib, nw = per_step(rows_w, "WRITE_SIZE")
     cal_rows_f = _pmc_rows(cal_fetch_dir)
     cal_rows_w = _pmc_rows(cal_write_dir)
     # the copy dispatch is the largest FETCH_SIZE / WRITE_SIZE in the calibration runs
@@ -359,13 +408,12 @@ def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     kw = CALIB_BYTES / (cw * 1024.0)
     rec = {
         "kernel_sha256_16": kernel_hash(),
-        "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+        "fetch_kib_per_step": f_kib, "write_kib_per_step": w_kib,
         "kernels": [re.sub(r"(?<=>)\(.*$", "", n.replace("void mlora::(anonymous namespace)::", ""))
                     for n in names],
         "dispatches": [nf, nw],
-        "launches_per_step": launches,
         "copy_scale_fetch": kf, "copy_scale_write": kw,
-        "hbm_bytes_per_launch": f_kib * 1024.0 * kf + w_kib * 1024.0 * kw,
+        "hbm_bytes_per_step": f_kib * 1024.0 * kf + w_kib * 1024.0 * kw,
     }
     data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
     data[workload] = rec
@@ -375,9 +423,133 @@ def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     print(json.dumps({workload: rec}))
 
 
-def measure(workload, args, with_cpu):
-    """One workload: stage it, time `args.steps` graph-replayed steps, and
-    return the result record (the JSON line's fields)."""
+# ---------------------------------------------------------------------------
+# HIP graphs: capture, and the kernel dispatches one captured step holds
+# ---------------------------------------------------------------------------
+
+def _hip_runtime():
+    """The HIP runtime library this process already loaded (PyTorch's)."""
+    import ctypes
+    with open("/proc/self/maps") as f:
+        paths = {l.split()[-1] for l in f if "libamdhip64" in l}
+    if not paths:
+        return None
+    lib = ctypes.CDLL(sorted(paths)[0])
+    lib.hipGraphGetNodes.restype = ctypes.c_int
+    lib.hipGraphGetNodes.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.hipGraphNodeGetType.restype = ctypes.c_int
+    lib.hipGraphNodeGetType.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
+    return lib
+
+
+def _new_graph(keep=False):
+    import torch
+    if keep:
+        try:
+            return torch.cuda.CUDAGraph(keep_graph=True)
+        except TypeError:
+            return None
+    return torch.cuda.CUDAGraph()
+
+
+def capture(fn, keep=False):
+    """A HIP graph of whatever `fn` enqueues on the current stream (captured
+    on a side stream, as torch requires)."""
+    import torch
+    g = _new_graph(keep)
+    if g is None:
+        return None
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return g
+
+
+def kernel_nodes(g):
+    """Kernel nodes of a captured graph (hipGraphNodeTypeKernel == 0), or None
+    when the runtime or torch does not expose the graph."""
+    import ctypes
+    try:
+        lib = _hip_runtime()
+        raw = g.raw_cuda_graph()
+        n = ctypes.c_size_t(0)
+        if lib is None or lib.hipGraphGetNodes(ctypes.c_void_p(raw), None, ctypes.byref(n)):
+            return None
+        nodes = (ctypes.c_void_p * n.value)()
+        if lib.hipGraphGetNodes(ctypes.c_void_p(raw), nodes, ctypes.byref(n)):
+            return None
+        kinds = ctypes.c_int(-1)
+        count = 0
+        for i in range(n.value):
+            if lib.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(kinds)) == 0 \
+                    and kinds.value == 0:
+                count += 1
+        return count
+    except Exception:  # pragma: no cover - depends on the runtime
+        return None
+
+
+class Rotation:
+    """`steps` steps of a rotation over `copies` copies as HIP graphs: one
+    graph of a whole rotation, replayed, and one of the remaining steps (the
+    first `steps % copies` copies), so exactly `steps` steps run."""
+
+    def __init__(self, step, copies, steps, eager=False):
+        self.full = steps // copies
+        self.rem = steps % copies
+        self.eager = eager
+        self.step, self.copies = step, copies
+        if not eager:
+            self.g_full = capture(lambda: [step(i) for i in range(copies)]) if self.full else None
+            self.g_rem = capture(lambda: [step(i) for i in range(self.rem)]) if self.rem else None
+
+    def run(self):
+        if self.eager:
+            for _ in range(self.full):
+                for i in range(self.copies):
+                    self.step(i)
+            for i in range(self.rem):
+                self.step(i)
+            return
+        for _ in range(self.full):
+            self.g_full.replay()
+        if self.g_rem is not None:
+            self.g_rem.replay()
+
+
+def copy_floor(n_bytes, steps, device="cuda"):
+    """A plain device copy that moves `n_bytes` (half read, half written) in
+    one launch: torch's copy kernel, graph-replayed over enough rotating
+    buffer pairs that every copy reads cold HBM. Returns (us per copy, GB/s)."""
+    import torch
+    half = max(256, (int(n_bytes) // 2 + 255) // 256 * 256)
+    pairs = max(2, min(256, math.ceil(640e6 / (2 * half))))
+    src = [torch.ones(half // 2, dtype=torch.bfloat16, device=device) for _ in range(pairs)]
+    dst = [torch.empty_like(t) for t in src]
+    torch.cuda.synchronize()
+    rot = Rotation(lambda i: dst[i].copy_(src[i]), pairs, steps)
+    rot.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    rot.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del src, dst, rot
+    torch.cuda.empty_cache()
+    return us, 2 * half / (us * 1e-6) / 1e9
+
+
+def measure(workload, args, cpu_seconds):
+    """One workload: stage it, time exactly `args.steps` graph-replayed steps,
+    and return the result record (the JSON line's fields)."""
     import torch
     import moe_expert_lora_amd as ml
     import workloads
@@ -388,7 +560,14 @@ def measure(workload, args, with_cpu):
     st = Staged(case, copies, two_kernel=not args.one_kernel)
     tables = st.primary.tables_host
     ra = st.primary.row_adapter_host
-    alg_bytes, flops, rows, folded, launches = algorithmic_traffic(case, tables, ra)
+    windows = 1
+    groups = None
+    if case.path == "grouped":
+        windows = len(ml.mlora_grouped_down_windows(case.n_rows, case.cap))
+        if not args.one_kernel and case.dtype == "bf16":
+            groups = all_windows_groups(case.n_rows, case.cap)
+    alg_bytes, flops, rows, folded, units = algorithmic_traffic(case, tables, ra, groups)
+    win_bytes = algorithmic_traffic(case, tables, ra)[0]
 
     # host-side integer work of one batch, timed for the record
     t0 = time.perf_counter()
@@ -402,104 +581,91 @@ def measure(workload, args, with_cpu):
             ml.mlora_grouped_down_windows(case.n_rows, case.cap)
     host_us = (time.perf_counter() - t0) / 50 * 1e6
 
-    # The fold reads its routing on the device, so a step is captured once in a
-    # HIP graph and replayed, as a decode loop runs it. One graph holds one step
-    # per rotating copy; K steps are K / copies replays (K rounded up).
     for i in range(args.warmup):
         st.step(i)
     torch.cuda.synchronize()
-    if args.eager:
-        class _Eager:
-            def replay(self):
-                for i in range(copies):
-                    st.step(i)
-        graph = _Eager()
-    else:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(graph, stream=side):
-                for i in range(copies):
-                    st.step(i)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-    replays = max(1, math.ceil(args.steps / copies))
-    steps = replays * copies
-    for _ in range(max(1, math.ceil(args.warmup / copies))):
-        graph.replay()
+    dispatches = None
+    if not args.eager:
+        one = capture(lambda: st.step(0), keep=True)
+        dispatches = kernel_nodes(one) if one is not None else None
+        del one
+    # The fold reads its routing on the device, so a step is captured in a
+    # HIP graph and replayed, as a decode loop runs it; the steps cycle
+    # through the copies so that each one reads cold HBM.
+    steps = args.steps
+    rot = Rotation(st.step, copies, steps, eager=args.eager)
+    rot.run()  # one untimed pass of the graphs themselves
     torch.cuda.synchronize()
 
-    # timed region: `steps` steps, wall clock and HIP events on the replay stream
+    # timed region: exactly `steps` steps, wall clock and HIP events on the
+    # stream the graphs replay on
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    per_replay = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(replays):
-        graph.replay()
+    rot.run()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = e0.elapsed_time(e1) / steps
-    per_launch_s = step_ms / 1e3 / launches
+    step_us = e0.elapsed_time(e1) * 1e3 / steps
 
-    # spread of the per-replay duration (a second, separately timed pass)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(replays)]
-    for r in range(replays):
-        ev[r][0].record(stream)
-        graph.replay()
-        ev[r][1].record(stream)
-    torch.cuda.synchronize()
-    dur_ms = np.array([a.elapsed_time(b) for a, b in ev]) / copies
-
-    # eager launches (host launch path included), for the record
-    t0 = time.perf_counter()
-    for i in range(copies):
-        st.step(i)
-    torch.cuda.synchronize()
-    eager_us = (time.perf_counter() - t0) / copies * 1e6
-
-    # warm figure, for context: one copy's step, captured as many times as the
-    # cold graph holds steps (the same graph-launch cost per step) and
-    # replayed, its inputs resident in L2 / MALL after the first step
-    warm_us = None
-    if not args.eager:
-        wg = torch.cuda.CUDAGraph()
-        side2 = torch.cuda.Stream()
-        side2.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side2):
-            with torch.cuda.graph(wg, stream=side2):
-                for _ in range(copies):
-                    st.step(0)
-        torch.cuda.current_stream().wait_stream(side2)
-        wg.replay()
+    out_extra = {}
+    if not args.counters:
+        # spread: per-rotation duration over a second pass of whole rotations
+        if not args.eager and rot.full:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(max(3, rot.full))]
+            for a, b in ev:
+                a.record(stream)
+                rot.g_full.replay()
+                b.record(stream)
+            torch.cuda.synchronize()
+            dur = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3 / copies
+            out_extra["step_us_p10_p50_p90"] = [float(np.percentile(dur, q)) for q in (10, 50, 90)]
+        # eager launches (host launch path included), for the record
+        t1 = time.perf_counter()
+        for i in range(copies):
+            st.step(i)
         torch.cuda.synchronize()
-        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        w0.record(stream)
-        for _ in range(replays):
+        out_extra["eager_step_us"] = (time.perf_counter() - t1) / copies * 1e6
+        # warm figure, for context: one copy's step, captured as many times
+        # as a rotation holds steps and replayed, inputs resident in L2 / MALL
+        if not args.eager:
+            wg = capture(lambda: [st.step(0) for _ in range(copies)])
             wg.replay()
-        w1.record(stream)
-        torch.cuda.synchronize()
-        warm_us = w0.elapsed_time(w1) * 1e3 / (replays * copies) / launches
+            torch.cuda.synchronize()
+            w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(1, math.ceil(steps / copies))
+            w0.record(stream)
+            for _ in range(reps):
+                wg.replay()
+            w1.record(stream)
+            torch.cuda.synchronize()
+            out_extra["warm_step_us"] = w0.elapsed_time(w1) * 1e3 / (reps * copies)
+            del wg
+        fl_us, fl_gbs = copy_floor(alg_bytes, steps)
+        out_extra["copy_floor"] = {
+            "us": fl_us, "gbs": fl_gbs,
+            "what": "torch's device copy moving the step's algorithmic bytes (half read, "
+                    "half written) in one launch, graph-replayed over rotating buffers"}
+    del rot, st
+    torch.cuda.empty_cache()
 
-    achieved = alg_bytes / launches / per_launch_s / 1e9
+    achieved = alg_bytes / (step_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
             rec = json.load(open(TRAFFIC_FILE)).get(workload)
             if rec and rec.get("kernel_sha256_16") == kernel_hash():
-                traffic = rec.get("hbm_bytes_per_launch")
+                traffic = rec.get("hbm_bytes_per_step")
         except Exception:
             traffic = None
 
-    cpu = None
-    if with_cpu:
-        cpu = cpu_baseline(case, args.cpu_seconds)
-
-    ms_per_step = wall / steps * 1e3
+    cpu = cpu_baseline(case, cpu_seconds) if cpu_seconds > 0 else None
+    unit = ("one mlora_gather_bgmv call" if case.path == "gather" else
+            f"one mlora_grouped_down_all call over {windows} windows"
+            if groups is not None else f"{windows} mlora_grouped_down calls (one per window)")
     out = {
         "metric": METRIC,
         "value": rows * steps / wall,
@@ -507,7 +673,7 @@ def measure(workload, args, with_cpu):
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": wall / steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -518,11 +684,13 @@ def measure(workload, args, with_cpu):
             "path": case.path,
             "rows_per_step": rows,
             "folded_rows_per_step": folded,
-            "launches_per_step": launches,
+            "windows_per_step": windows,
+            "kernel_dispatches_per_step": dispatches,
             "workspace": not args.one_kernel,
             "rotating_copies": copies,
             "timing": ("eager launches" if args.eager else
-                       "HIP graph of one step per copy, replayed"),
+                       "HIP graphs of whole rotations over the copies plus the remainder, "
+                       "replayed; HIP events on the replay stream"),
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -532,27 +700,31 @@ def measure(workload, args, with_cpu):
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": alg_bytes / launches,
-            "flops_per_launch": flops / launches,
-            "launch_us_mean": per_launch_s * 1e6,
-            "step_us_p10_p50_p90": [float(np.percentile(dur_ms, q)) * 1e3 for q in (10, 50, 90)],
+            "unit_of_work": unit,
+            "algorithmic_bytes": alg_bytes,
+            "bytes_counted_by": ("the call" if case.path == "gather" else
+                                 f"{units} launch groups" if groups is not None else
+                                 f"{units} windows"),
+            "algorithmic_bytes_by_window": win_bytes,
+            "flops": flops,
+            "step_us_mean": step_us,
         },
         "cpu_baseline": cpu,
         "host_setup_us": host_us,
-        "eager_step_us": eager_us,
-        "warm_launch_us": warm_us,
         "notes": "the pages quote no performance numbers; vs_baseline is null",
     }
+    out["roofline"].update({k: v for k, v in out_extra.items() if k == "step_us_p10_p50_p90"})
+    out.update({k: v for k, v in out_extra.items() if k != "step_us_p10_p50_p90"})
     return out
 
 
 def resolve_workloads(workload, also):
     """(main workload, workloads reported under 'also') from the command line:
-    no --workload means the decode default with the prefill grouped workload
+    no --workload means the decode default with every other measured workload
     beside it; an explicit --workload runs alone unless --also names others;
     --also none runs none."""
     if also is None:
-        also = "prefill_grouped_down" if workload is None else ""
+        also = ",".join(w for w in MEASURED if w != DEFAULT_WORKLOAD) if workload is None else ""
     elif also == "none":
         also = ""
     workload = workload or DEFAULT_WORKLOAD
@@ -571,16 +743,22 @@ def main():
     ap.add_argument("--workload", default=None, choices=sorted(WORKLOAD_TEXT),
                     help=f"default {DEFAULT_WORKLOAD}")
     ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--also", default=None,
                     help="comma-separated workloads measured after the main one and reported "
-                         "under 'also' (default: the prefill grouped workload when no "
+                         "under 'also' (default: every other measured workload when no "
                          "--workload is given; 'none' for none)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle budget of the main workload (each 'also' one: 60%%)")
     ap.add_argument("--one-kernel", action="store_true",
                     help="run the folds without a workspace (one-kernel forms)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of graph replays")
+    ap.add_argument("--counters", action="store_true",
+                    help="counter runs: warm-up and the timed steps only (cold inputs), no "
+                         "CPU leg, no warm or spread passes")
+    ap.add_argument("--floor-copy", action="store_true",
+                    help="only time the plain-copy floor of the workload's algorithmic bytes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain copy used to scale HBM counters")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
@@ -596,6 +774,9 @@ def main():
         print("bench.py measures one GPU only: the fold needs no collective and this "
               "build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1:
+        print("bench.py: --steps must be at least 1", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     import moe_expert_lora_amd as ml
@@ -607,18 +788,36 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.floor_copy:
+        import workloads
+        case = workloads.WORKLOADS[args.workload]()
+        tables, ra = _tables_and_map(case)
+        groups = (all_windows_groups(case.n_rows, case.cap)
+                  if case.path == "grouped" and not args.one_kernel else None)
+        n = algorithmic_traffic(case, tables, ra, groups)[0]
+        us, gbs = copy_floor(n, args.steps)
+        print(json.dumps({"workload": args.workload, "copy_bytes": n, "steps": args.steps,
+                          "copy_us": us, "copy_gbs": gbs}), flush=True)
+        return
 
-    out = measure(args.workload, args, with_cpu=not args.no_cpu)
-    out["hbm_copy_gbs"] = copy_bandwidth()
-    # The metric covers both halves of the fold: the decode line above, and
-    # the prefill grouped workload beside it (same protocol, no CPU leg).
-    also = args.also
-    if also:
+    if args.counters:
+        args.no_cpu = True
+    main_cpu = 0.0 if args.no_cpu else args.cpu_seconds
+    out = measure(args.workload, args, main_cpu)
+    if not args.counters:
+        out["hbm_copy_gbs"] = copy_bandwidth()
+    # The metric covers the decode and the prefill halves of the fold: the
+    # main line, and every other workload beside it, measured the same way.
+    if args.also:
         out["also"] = {}
-        for w in also:
-            r = measure(w, args, with_cpu=False)
+        for w in args.also:
+            r = measure(w, args, 0.0 if args.no_cpu else 0.6 * args.cpu_seconds)
             out["also"][w] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps",
-                                                 "dtype", "config", "roofline")}
+                                                 "dtype", "config", "roofline",
+                                                 "cpu_baseline") if k in r}
+            for k in ("warm_step_us", "copy_floor", "eager_step_us"):
+                if k in r:
+                    out["also"][w][k] = r[k]
     print(json.dumps(out), flush=True)
 
 

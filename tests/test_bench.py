@@ -27,7 +27,8 @@ def test_more_than_one_gpu_is_refused():
 
 
 @pytest.mark.parametrize("workload,also,want", [
-    (None, None, ("decode_down_gather", ["prefill_grouped_down"])),
+    (None, None, ("decode_down_gather", ["prefill_grouped_down", "gateup_gather",
+                                          "router_gather", "mixed_grouped"])),
     ("router_gather", None, ("router_gather", [])),
     ("prefill_grouped_down", None, ("prefill_grouped_down", [])),
     (None, "none", ("decode_down_gather", [])),
@@ -87,6 +88,54 @@ def test_algorithmic_bytes_grouped_hand_count():
     assert got == (w1 + w2, 2 * 4 * R * (K + N), 5, 4, 2)
 
 
+def test_algorithmic_bytes_grouped_by_launch_group():
+    """The same 5 rows counted as one launch group [0, 5): tokens {0, 1} and
+    experts {0, 2} are read once for the group."""
+    case = SimpleNamespace(path="grouped", dtype="bf16", k_in=K, n_out=N, max_rank=R, top_k=2,
+                           n_rows=5, n_tokens=3, n_route=3, cap=3,
+                           expert_offsets=np.array([0, 2, 2, 5], dtype=np.int32),
+                           sorted_ids=np.array([0, 3, 1, 2, 4], dtype=np.int32))
+    tables = (np.array([16, 0, 48], np.uint64), np.array([16, 0, 48], np.uint64),
+              np.ones(3, np.float32), 3)
+    ra = np.array([1, 1, -1], dtype=np.int32)
+    got = bench.algorithmic_traffic(case, tables, ra, groups=[(0, 5)])
+    meta = 4 * 3 + 4 * 4 + 20 * 3
+    want = 2 * PER_TOKEN + 2 * PER_EXPERT + 4 * PER_ROW + 4 * 5 + meta
+    assert got == (want, 2 * 4 * R * (K + N), 5, 4, 1)
+
+
+def test_algorithmic_bytes_grouped_unnamed_ids():
+    """Sorted ids of -1 or past the last token fold nothing and read no x row."""
+    case = SimpleNamespace(path="grouped", dtype="bf16", k_in=K, n_out=N, max_rank=R, top_k=2,
+                           n_rows=4, n_tokens=2, n_route=2, cap=4,
+                           expert_offsets=np.array([0, 2, 4], dtype=np.int32),
+                           sorted_ids=np.array([0, -1, 4, 3], dtype=np.int32))
+    tables = (np.array([16, 48], np.uint64), np.array([16, 48], np.uint64),
+              np.ones(2, np.float32), 2)
+    ra = np.array([1, 1], dtype=np.int32)
+    got = bench.algorithmic_traffic(case, tables, ra, groups=[(0, 4)])
+    want = 2 * PER_TOKEN + 2 * PER_EXPERT + 2 * PER_ROW + 4 * 4 + 4 * 2 + 4 * 3 + 20 * 2
+    assert got == (want, 2 * 2 * R * (K + N), 4, 2, 1)
+
+
+@pytest.mark.parametrize("n_rows,cap,want", [
+    (32768, 8192, [(0, 16384), (16384, 32768)]),
+    (16384, 8192, [(0, 16384)]),
+    (12288, 8192, [(0, 12288)]),
+    (50000, 20000, [(0, 20000), (20000, 40000), (40000, 50000)]),
+    (100, 30, [(0, 100)]),
+])
+def test_all_windows_groups(n_rows, cap, want):
+    assert bench.all_windows_groups(n_rows, cap) == want
+
+
+def test_cpu_threads_respects_omp(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert bench.cpu_threads() == min(3, len(os.sched_getaffinity(0)))
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.cpu_threads() == len(os.sched_getaffinity(0))
+
+
 def _write_counters(d, rows):
     os.makedirs(d, exist_ok=True)
     with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
@@ -98,7 +147,7 @@ def _write_counters(d, rows):
 
 def test_traffic_from_scales_counters_by_the_copy(tmp_path, monkeypatch):
     """Two steps of a two-kernel fold: counters are summed over the fold's
-    kernels, divided by steps x launches per step, and scaled by what the
+    kernels, divided by the steps, and scaled by what the
     same counter reads for the plain copy of CALIB_BYTES (FETCH_SIZE reading
     half the copied bytes gives a factor 2)."""
     out = tmp_path / "traffic.json"
@@ -116,12 +165,11 @@ def test_traffic_from_scales_counters_by_the_copy(tmp_path, monkeypatch):
     bench.traffic_from("decode_down_gather", str(tmp_path / "f"), str(tmp_path / "w"),
                        str(tmp_path / "cf"), str(tmp_path / "cw"))
     rec = json.load(open(out))["decode_down_gather"]
-    assert rec["launches_per_step"] == 1
-    assert rec["fetch_kib_per_launch"] == pytest.approx(400.0)
-    assert rec["write_kib_per_launch"] == pytest.approx(60.0)
+    assert rec["fetch_kib_per_step"] == pytest.approx(400.0)
+    assert rec["write_kib_per_step"] == pytest.approx(60.0)
     assert rec["copy_scale_fetch"] == pytest.approx(2.0)
     assert rec["copy_scale_write"] == pytest.approx(1.0)
-    assert rec["hbm_bytes_per_launch"] == pytest.approx((400.0 * 2 + 60.0) * 1024)
+    assert rec["hbm_bytes_per_step"] == pytest.approx((400.0 * 2 + 60.0) * 1024)
     assert rec["kernel_sha256_16"] == bench.kernel_hash()
 
 
