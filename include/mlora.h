@@ -282,6 +282,35 @@ uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap, int
 uint64_t mlora_grouped_down_workspace_bytes(int64_t row_offset, int64_t row_end,
                                             int32_t max_rank);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the fold of
+ * mlora_grouped_down_all, with the same arguments and the same bits, but no
+ * workspace. Its two launch slots live in a static device array of
+ * MLORA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per device, held
+ * until the process ends; its address is looked up once per device, at the
+ * first call with that device current. The call allocates nothing.
+ *   - A call needing more than MLORA_NOALLOC_SCRATCH_BYTES (the
+ *     mlora_grouped_down_all_workspace_bytes figure of its launches; 32 MiB
+ *     holds two slots of 16384 rows at max_rank 128) returns
+ *     MLORA_ERR_CAPACITY, enqueues nothing and reads no device memory.
+ *   - The stream (NULL = the default stream) must belong to the current
+ *     device: otherwise MLORA_ERR_INVALID.
+ *   - Every call on one device shares that device's array, and the array
+ *     keeps the last call's contents; the fold needs no initialised contents
+ *     (each launch writes every scratch entry it reads). Calls that overlap
+ *     on one device, on different streams or from different threads without
+ *     ordering, race on it and give undefined results.
+ * Other errors are those of mlora_grouped_down_all. An f32 route uses no
+ * scratch.
+ */
+#define MLORA_NOALLOC_SCRATCH_BYTES (32ull << 20)
+int32_t mlora_grouped_down_all_noalloc(const mlora_expert_route* route, const void* x,
+                                       int64_t n_tokens, void* base_out, int64_t n_rows,
+                                       const int32_t* expert_offsets, int32_t n_route,
+                                       const int32_t* sorted_ids, const int32_t* row_adapter,
+                                       int32_t top_k, int64_t cap, void* stream);
+
 /* Reads the MLORA_* launch-shape overrides from the environment again (they
  * are otherwise read once, at the first fold call). For measurement tools and
  * tests that change the environment within one process. Not safe while

@@ -50,6 +50,7 @@ EXPORTS = (
     "mlora_grouped_down_all",
     "mlora_grouped_down_all_workspace_bytes",
     "mlora_reload_launch_overrides",
+    "mlora_grouped_down_all_noalloc",
 )
 
 
@@ -122,6 +123,8 @@ def load() -> ctypes.CDLL:
                                          vp, vp, i32, i64, vp, ctypes.c_uint64, vp]),
         "mlora_grouped_down_all_workspace_bytes": (ctypes.c_uint64, [i64, i64, i32]),
         "mlora_reload_launch_overrides": (None, []),
+        "mlora_grouped_down_all_noalloc": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64,
+                                                 vp, i32, vp, vp, i32, i64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -419,3 +422,36 @@ def mlora_grouped_down_all(route: ExpertRoute, x, base_out, expert_offsets, sort
         _stream_handle(stream))
     if rc != MLORA_OK:
         raise _err(rc)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MLORA_NOALLOC_SCRATCH_BYTES
+
+
+def mlora_grouped_down_all_noalloc(route: ExpertRoute, x, base_out, expert_offsets, sorted_ids,
+                                   row_adapter, top_k: int, cap: int, stream=None) -> None:
+    """mlora_grouped_down_all without a workspace: the library's static device
+    scratch holds the launch slots (for callers that cannot allocate)."""
+    import torch
+    if _dtype_code(x) != route.dtype or _dtype_code(base_out) != route.dtype:
+        raise TypeError("x / base_out dtype differs from the route's")
+    if x.dim() != 2 or base_out.dim() != 2:
+        raise ValueError("x and base_out must be 2-D")
+    if x.shape[1] != route.k_in or base_out.shape[1] != route.n_out:
+        raise ValueError("x / base_out widths differ from the route's k_in / n_out")
+    n_rows = base_out.shape[0]
+    if sorted_ids.numel() != n_rows:
+        raise ValueError("sorted_ids must have one entry per base_out row")
+    if row_adapter.numel() < x.shape[0]:
+        raise ValueError("row_adapter must cover every x row")
+    n_route = expert_offsets.numel() - 1
+    if n_route < 0:
+        raise ValueError("expert_offsets needs at least one entry")
+    rc = load().mlora_grouped_down_all_noalloc(
+        ctypes.byref(route), _dev(x, "x"), x.shape[0], _dev(base_out, "base_out"), n_rows,
+        _dev(expert_offsets, "expert_offsets", torch.int32), int(n_route),
+        _dev(sorted_ids, "sorted_ids", torch.int32),
+        _dev(row_adapter, "row_adapter", torch.int32), int(top_k), int(cap),
+        _stream_handle(stream))
+    if rc != MLORA_OK:
+        raise _err(rc)
+

@@ -2648,13 +2648,59 @@ extern "C" void mlora_reload_launch_overrides(void) {
   g_overrides = read_overrides();
 }
 
-extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x,
-                                          int64_t n_tokens, void* base_out, int64_t n_rows,
-                                          const int32_t* expert_offsets, int32_t n_route,
-                                          const int32_t* sorted_ids, const int32_t* row_adapter,
-                                          int32_t top_k, int64_t cap, void* workspace,
-                                          uint64_t workspace_bytes, void* stream) {
-  const char* who = "mlora_grouped_down_all";
+// ---- the all-windows call without a caller workspace ----
+
+// Scratch of mlora_grouped_down_all_noalloc: the two launch slots of the
+// all-windows call live here instead of in a caller workspace. Each device
+// the library runs on holds its own copy until the process ends; host code
+// never uses the name itself as an address, only the per-device address
+// looked up below.
+constexpr uint64_t kScratchBytes = MLORA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept. The caller's stream must belong
+// to the current device.
+static int32_t scratch_address(hipStream_t s, void** out, const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLORA_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MLORA_ERR_INVALID, "%s: device %d outside 0..%d", who, dev, kMaxDevices - 1);
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess)
+      return fail(MLORA_ERR_HIP, "%s: hipStreamGetDevice: %s", who, hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(MLORA_ERR_INVALID, "%s: the stream belongs to device %d, device %d is current",
+                  who, (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MLORA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLORA_OK;
+}
+
+static int32_t grouped_down_all_impl(const mlora_expert_route* route, const void* x,
+                                     int64_t n_tokens,
+                              void* base_out, int64_t n_rows, const int32_t* expert_offsets,
+                              int32_t n_route, const int32_t* sorted_ids,
+                              const int32_t* row_adapter, int32_t top_k, int64_t cap,
+                              void* workspace, uint64_t workspace_bytes, void* stream,
+                              bool use_scratch) {
+  const char* who = use_scratch ? "mlora_grouped_down_all_noalloc" : "mlora_grouped_down_all";
   if (int32_t rc = check_route(route, who)) return rc;
   if (top_k <= 0) return fail(MLORA_ERR_INVALID, "%s: top_k=%d must be positive", who, top_k);
   if (n_route < 0) return fail(MLORA_ERR_INVALID, "%s: n_route < 0", who);
@@ -2681,10 +2727,19 @@ extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const
   const int64_t n_win = (n_rows + chunk - 1) / chunk;
   const int64_t slot = pipe_slot_bytes(chunk, R);
   const int64_t need = (n_win > 1 ? 2 : 1) * slot;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (use_scratch && route->dtype == MLORA_BF16) {
+    if ((uint64_t)need > kScratchBytes)
+      return fail(MLORA_ERR_CAPACITY,
+                  "%s: needs %lld bytes of scratch, more than the %llu bytes it holds; lower "
+                  "cap or max_rank, or pass a workspace to mlora_grouped_down_all",
+                  who, (long long)need, (unsigned long long)kScratchBytes);
+    if (int32_t rc = scratch_address(s, &workspace, who)) return rc;
+    workspace_bytes = kScratchBytes;
+  }
   if (route->dtype == MLORA_BF16 && (!workspace || (uint64_t)need > workspace_bytes))
     return fail(MLORA_ERR_CAPACITY, "%s: workspace of %llu bytes, %lld needed", who,
                 (unsigned long long)workspace_bytes, (long long)need);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
 
   if (route->dtype == MLORA_F32) {
@@ -2775,4 +2830,26 @@ extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const
   last.per_xcd = (int32_t)((last.units + kXcds - 1) / kXcds);
   dispatch_expand(last, last.per_xcd * kXcds, s, emb, cw);
   return launched(who);
+}
+
+extern "C" int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x,
+                                          int64_t n_tokens, void* base_out, int64_t n_rows,
+                                          const int32_t* expert_offsets, int32_t n_route,
+                                          const int32_t* sorted_ids, const int32_t* row_adapter,
+                                          int32_t top_k, int64_t cap, void* workspace,
+                                          uint64_t workspace_bytes, void* stream) {
+  return grouped_down_all_impl(route, x, n_tokens, base_out, n_rows, expert_offsets, n_route,
+                               sorted_ids, row_adapter, top_k, cap, workspace, workspace_bytes,
+                               stream, false);
+}
+
+extern "C" int32_t mlora_grouped_down_all_noalloc(const mlora_expert_route* route,
+                                                  const void* x, int64_t n_tokens,
+                                                  void* base_out, int64_t n_rows,
+                                                  const int32_t* expert_offsets, int32_t n_route,
+                                                  const int32_t* sorted_ids,
+                                                  const int32_t* row_adapter, int32_t top_k,
+                                                  int64_t cap, void* stream) {
+  return grouped_down_all_impl(route, x, n_tokens, base_out, n_rows, expert_offsets, n_route,
+                               sorted_ids, row_adapter, top_k, cap, nullptr, 0, stream, true);
 }

@@ -390,6 +390,25 @@ def test_grouped_all_workspace_bytes_covers_every_override(lib, overrides, n_row
     assert max(needs) == query
 
 
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """The no-allocation all-windows call refuses a call whose launch slots
+    exceed its static scratch before touching the device (no HIP call is
+    made, so this runs without a GPU); the limit is the header's."""
+    assert ml.NOALLOC_SCRATCH_BYTES == 32 << 20
+    r = _route(n_out=8, max_rank=128)
+    n_rows = cap = 72000
+    need = lib.mlora_grouped_down_all_workspace_bytes(n_rows, cap, 128)
+    assert need > ml.NOALLOC_SCRATCH_BYTES
+    rc = lib.mlora_grouped_down_all_noalloc(ctypes.byref(r), FAKE, 9000, FAKE, n_rows, FAKE, 4,
+                                            FAKE, FAKE, 8, cap, None)
+    assert rc == ml.MLORA_ERR_CAPACITY
+    msg = lib.mlora_last_error().decode()
+    assert "scratch" in msg and str(need) in msg
+    # argument errors come first, as for the workspace form
+    assert lib.mlora_grouped_down_all_noalloc(ctypes.byref(r), FAKE, 9000, FAKE, n_rows, FAKE,
+                                              4, FAKE, FAKE, 8, 0, None) == ml.MLORA_ERR_INVALID
+
+
 def test_gather_workspace_bytes(lib):
     f = lib.mlora_gather_bgmv_workspace_bytes
     # KC k ranges (16 k steps each, at most 4) x n_slots x 64 x NB bytes,
