@@ -200,6 +200,7 @@ class Staged:
         c.scale_table = p.scale_table.clone()
         c.route = ml.make_route(c.a_table, c.b_table, c.scale_table, n, self.case.k_in,
                                 self.case.n_out, self.case.max_rank, p.tdtype)
+        c.tables_host = (at2, bt2, st, n)
         return c
 
     def step(self, i):
@@ -547,6 +548,46 @@ def copy_floor(n_bytes, steps, device="cuda"):
     return us, 2 * half / (us * 1e-6) / 1e9
 
 
+def host_loop(st, steps):
+    """The host-loop baseline on a staged grouped workload: each step copies
+    expert_offsets to the host (a synchronisation) and makes one grouped
+    launch per adapted expert's span (mlora_apply_expert_lora_sorted), cycling
+    through the same rotating copies. Eager by nature; wall clock per step."""
+    import torch
+    import moe_expert_lora_amd as ml
+    case = st.case
+    off0 = st.primary.offsets.cpu().numpy().astype(np.int64)
+    ws = None
+    if st.primary.two_kernel and case.dtype == "bf16":
+        need = ml.mlora_grouped_down_workspace_bytes(0, int(np.diff(off0).max()), case.max_rank)
+        ws = torch.empty(max(256, need), dtype=torch.uint8, device="cuda")
+    at0, bt0, _, n = st.primary.tables_host
+    launched = sum(1 for e in range(min(len(off0) - 1, n))
+                   if off0[e + 1] > off0[e] and at0[e] != 0 and bt0[e] != 0)
+
+    def step(i):
+        c = st.copies[i % len(st.copies)]
+        off_h = c.offsets.cpu().numpy()  # the device-to-host copy: waits for the stream
+        at, bt, _, _ = c.tables_host
+        ml.mlora_apply_expert_lora_sorted(c.route, c.x, st.bases[i % len(st.copies)], c.offsets,
+                                          off_h, at, bt, c.sorted_ids, c.row_adapter,
+                                          case.top_k, workspace=ws)
+
+    for i in range(min(3, steps)):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    return {"us_per_step": us, "rows_per_s": case.n_rows / (us * 1e-6),
+            "kernel_launches_per_step": launched * (2 if ws is not None else 1),
+            "what": "mlora_apply_expert_lora_sorted: offsets copied to the host each step, "
+                    "then one grouped launch per adapted expert's span (eager, wall clock); "
+                    "a baseline for what device-side routing buys, not a target"}
+
+
 def measure(workload, args, cpu_seconds):
     """One workload: stage it, time exactly `args.steps` graph-replayed steps,
     and return the result record (the JSON line's fields)."""
@@ -644,6 +685,8 @@ def measure(workload, args, cpu_seconds):
             torch.cuda.synchronize()
             out_extra["warm_step_us"] = w0.elapsed_time(w1) * 1e3 / (reps * copies)
             del wg
+        if case.path == "grouped" and not args.eager:
+            out_extra["host_loop_baseline"] = host_loop(st, min(steps, 50))
         fl_us, fl_gbs = copy_floor(alg_bytes, steps)
         out_extra["copy_floor"] = {
             "us": fl_us, "gbs": fl_gbs,
@@ -815,7 +858,7 @@ def main():
             out["also"][w] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps",
                                                  "dtype", "config", "roofline",
                                                  "cpu_baseline") if k in r}
-            for k in ("warm_step_us", "copy_floor", "eager_step_us"):
+            for k in ("warm_step_us", "copy_floor", "eager_step_us", "host_loop_baseline"):
                 if k in r:
                     out["also"][w][k] = r[k]
     print(json.dumps(out), flush=True)

@@ -273,6 +273,31 @@ int32_t mlora_grouped_down_all(const mlora_expert_route* route, const void* x, i
  * max_rank outside [1, 128]. */
 uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap, int32_t max_rank);
 
+/*
+ * [P2 module doc: the host-loop fold the device-routed launchers replace]
+ * The sorted fold driven from the host: with the expert spans copied to the
+ * host beforehand (expert_offsets_host, the caller's device-to-host copy of
+ * expert_offsets) and the host copies of the packed tables, one
+ * mlora_grouped_down launch per expert that has rows and both table cells,
+ * over exactly its span. The result equals mlora_grouped_down over every row,
+ * bit for bit (rows are independent). It exists as the baseline that shows
+ * what reading the routing on the device buys: it needs the host copy (a
+ * synchronisation of the caller's stream) and up to n_route launches, and
+ * cannot be captured once for every routing. The workspace, if given, must
+ * hold mlora_grouped_down_workspace_bytes of the largest span (the per-call
+ * form's workspace rules apply). Spans outside [0, n_rows] or decreasing ->
+ * MLORA_ERR_INVALID before any launch; other errors as mlora_grouped_down
+ * (launches made before a failing one stay enqueued).
+ */
+int32_t mlora_apply_expert_lora_sorted(const mlora_expert_route* route, const void* x,
+                                       int64_t n_tokens, void* base_out, int64_t n_rows,
+                                       const int32_t* expert_offsets,
+                                       const int32_t* expert_offsets_host, int32_t n_route,
+                                       const uint64_t* a_table_host,
+                                       const uint64_t* b_table_host, const int32_t* sorted_ids,
+                                       const int32_t* row_adapter, int32_t top_k,
+                                       void* workspace, uint64_t workspace_bytes, void* stream);
+
 /* Bytes of workspace mlora_grouped_down needs for its two-kernel form on the
  * window [row_offset, row_end) at this max_rank: (row_end - row_offset) rows
  * of 64 * NB bytes, NB = ceil(max_rank / 16) rounded up to 1, 2, 4 or 8,

@@ -51,6 +51,7 @@ EXPORTS = (
     "mlora_grouped_down_all_workspace_bytes",
     "mlora_reload_launch_overrides",
     "mlora_grouped_down_all_noalloc",
+    "mlora_apply_expert_lora_sorted",
 )
 
 
@@ -125,6 +126,9 @@ def load() -> ctypes.CDLL:
         "mlora_reload_launch_overrides": (None, []),
         "mlora_grouped_down_all_noalloc": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64,
                                                  vp, i32, vp, vp, i32, i64, vp]),
+        "mlora_apply_expert_lora_sorted": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64,
+                                                 vp, _i32p, i32, _u64p, _u64p, vp, vp, i32, vp,
+                                                 ctypes.c_uint64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -451,6 +455,41 @@ def mlora_grouped_down_all_noalloc(route: ExpertRoute, x, base_out, expert_offse
         _dev(expert_offsets, "expert_offsets", torch.int32), int(n_route),
         _dev(sorted_ids, "sorted_ids", torch.int32),
         _dev(row_adapter, "row_adapter", torch.int32), int(top_k), int(cap),
+        _stream_handle(stream))
+    if rc != MLORA_OK:
+        raise _err(rc)
+
+
+def mlora_apply_expert_lora_sorted(route: ExpertRoute, x, base_out, expert_offsets,
+                                   expert_offsets_host, a_table_host, b_table_host, sorted_ids,
+                                   row_adapter, top_k: int, workspace=None, stream=None) -> None:
+    """The host-loop sorted fold: one grouped launch per adapted expert's span,
+    the spans and table cells given as host arrays (the caller copied the
+    offsets to the host)."""
+    import torch
+    if _dtype_code(x) != route.dtype or _dtype_code(base_out) != route.dtype:
+        raise TypeError("x / base_out dtype differs from the route's")
+    n_rows = base_out.shape[0]
+    if sorted_ids.numel() != n_rows:
+        raise ValueError("sorted_ids must have one entry per base_out row")
+    off_h = _arr(expert_offsets_host, np.int32)
+    n_route = off_h.shape[0] - 1
+    if n_route < 0 or expert_offsets.numel() != off_h.shape[0]:
+        raise ValueError("host and device offsets differ in length")
+    at = _arr(a_table_host, np.uint64)
+    bt = _arr(b_table_host, np.uint64)
+    if at.shape[0] < route.n_experts or bt.shape[0] < route.n_experts:
+        raise ValueError("host tables shorter than n_experts")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load().mlora_apply_expert_lora_sorted(
+        ctypes.byref(route), _dev(x, "x"), x.shape[0], _dev(base_out, "base_out"), n_rows,
+        _dev(expert_offsets, "expert_offsets", torch.int32), _ptr(off_h, ctypes.c_int32),
+        int(n_route), _ptr(at, ctypes.c_uint64), _ptr(bt, ctypes.c_uint64),
+        _dev(sorted_ids, "sorted_ids", torch.int32),
+        _dev(row_adapter, "row_adapter", torch.int32), int(top_k), ws_ptr, ws_bytes,
         _stream_handle(stream))
     if rc != MLORA_OK:
         raise _err(rc)

@@ -2622,6 +2622,42 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
   return launched(who);
 }
 
+extern "C" int32_t mlora_apply_expert_lora_sorted(
+    const mlora_expert_route* route, const void* x, int64_t n_tokens, void* base_out,
+    int64_t n_rows, const int32_t* expert_offsets, const int32_t* expert_offsets_host,
+    int32_t n_route, const uint64_t* a_table_host, const uint64_t* b_table_host,
+    const int32_t* sorted_ids, const int32_t* row_adapter, int32_t top_k, void* workspace,
+    uint64_t workspace_bytes, void* stream) {
+  const char* who = "mlora_apply_expert_lora_sorted";
+  if (int32_t rc = check_route(route, who)) return rc;
+  if (n_route < 0) return fail(MLORA_ERR_INVALID, "%s: n_route < 0", who);
+  if (n_route > 0 && !expert_offsets_host)
+    return fail(MLORA_ERR_INVALID, "%s: NULL host offsets", who);
+  if (route->n_experts > 0 && (!a_table_host || !b_table_host))
+    return fail(MLORA_ERR_INVALID, "%s: NULL host table", who);
+  // the spans come from the host copy: check them all before any launch
+  for (int32_t e = 0; e < n_route; ++e) {
+    const int64_t lo = expert_offsets_host[e], hi = expert_offsets_host[e + 1];
+    if (lo < 0 || hi < lo || hi > n_rows)
+      return fail(MLORA_ERR_INVALID, "%s: span %d = [%lld, %lld) outside [0, %lld]", who, e,
+                  (long long)lo, (long long)hi, (long long)n_rows);
+  }
+  // one grouped launch per adapted expert with rows: its span is the window
+  int64_t launched_rows = 0;
+  for (int32_t e = 0; e < n_route && e < route->n_experts; ++e) {
+    const int64_t lo = expert_offsets_host[e], hi = expert_offsets_host[e + 1];
+    if (hi == lo || a_table_host[e] == 0 || b_table_host[e] == 0) continue;
+    if (int32_t rc = mlora_grouped_down(route, x, n_tokens, base_out, n_rows, expert_offsets,
+                                        n_route, sorted_ids, row_adapter, top_k, lo, hi,
+                                        workspace, workspace_bytes, stream))
+      return rc;
+    launched_rows += hi - lo;
+  }
+  (void)launched_rows;
+  clear_error();
+  return MLORA_OK;
+}
+
 extern "C" uint64_t mlora_grouped_down_all_workspace_bytes(int64_t n_rows, int64_t cap,
                                                            int32_t max_rank) {
   if (n_rows <= 0 || cap <= 0 || max_rank < 1 || max_rank > 128) return 0;

@@ -499,6 +499,38 @@ def test_grouped_unnamed_rows(label, kw, form, overrides):
     check(view, dev.run(two_kernel=two, pipelined=pipe), u.base, f"{label} unnamed {form}")
 
 
+@pytest.mark.parametrize("label", ["prefill_grouped_down", "mixed_grouped", "unnamed"])
+@pytest.mark.parametrize("two", [True, False], ids=["two_kernel", "one_kernel"])
+def test_host_loop_baseline_equals_device_routed(label, two):
+    """mlora_apply_expert_lora_sorted (spans copied to the host, one launch per
+    adapted expert) gives the bits of the device-routed fold over every row."""
+    import moe_expert_lora_amd as ml
+    from staging import DeviceCase, from_torch
+    _need_gpu()
+    if label == "unnamed":
+        case = workloads.with_unnamed_rows(
+            workloads.make_grouped_case(72, **UNNAMED[0][1]), 72, lead=11, tail=5,
+            bad_frac=0.1)
+    else:
+        case = workloads.WORKLOADS[label]()
+    dev = DeviceCase(case, DEV)
+    want = dev.run(windows=[(0, case.n_rows)], two_kernel=two)
+    off_h = dev.offsets.cpu().numpy()
+    at, bt, _, _ = dev.tables_host
+    spans = np.diff(off_h.astype(np.int64))
+    ws = None
+    if two:
+        ws = torch.empty(max(256, ml.mlora_grouped_down_workspace_bytes(0, int(spans.max()),
+                                                                        case.max_rank)),
+                         dtype=torch.uint8, device=DEV)
+    out = dev.base0.clone()
+    ml.mlora_apply_expert_lora_sorted(dev.route, dev.x, out, dev.offsets, off_h, at, bt,
+                                      dev.sorted_ids, dev.row_adapter, case.top_k, workspace=ws)
+    torch.cuda.synchronize()
+    got = from_torch(out)
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
 def test_grouped_workspace_reused_across_windows_and_calls():
     """One workspace serves successive windows and calls; stale contents from a
     larger call never leak into a smaller one."""

@@ -409,6 +409,20 @@ def test_noalloc_rejects_calls_beyond_its_scratch(lib):
                                               4, FAKE, FAKE, 8, 0, None) == ml.MLORA_ERR_INVALID
 
 
+def test_host_loop_rejects_bad_host_spans(lib):
+    """The host-loop baseline checks every host span before launching
+    anything (no HIP call is made here)."""
+    r = _route()
+    u64 = ctypes.c_uint64 * 4
+    at, bt = u64(16, 32, 48, 64), u64(16, 32, 48, 64)
+    for spans in ([0, 3, 2, 4, 6], [0, 2, 4, 6, 99], [-1, 2, 4, 6, 8]):
+        off = (ctypes.c_int32 * 5)(*spans)
+        rc = lib.mlora_apply_expert_lora_sorted(ctypes.byref(r), FAKE, 4, FAKE, 8, FAKE, off, 4,
+                                                at, bt, FAKE, FAKE, 2, None, 0, None)
+        assert rc == ml.MLORA_ERR_INVALID, spans
+        assert "span" in lib.mlora_last_error().decode()
+
+
 def test_gather_workspace_bytes(lib):
     f = lib.mlora_gather_bgmv_workspace_bytes
     # KC k ranges (16 k steps each, at most 4) x n_slots x 64 x NB bytes,
