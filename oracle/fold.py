@@ -55,8 +55,12 @@ def _cell_live(e: int, a_table, b_table) -> bool:
 def fold_gather_scalar(x: np.ndarray, a_table: Sequence[int], b_table: Sequence[int],
                        scale_table: Sequence[float], mats: Dict[int, np.ndarray],
                        base: np.ndarray, indices: Sequence[int], row_adapter: Sequence[int],
-                       top_k: int) -> np.ndarray:
-    """Gather fold, one row at a time."""
+                       top_k: int, x_rows: str = "token") -> np.ndarray:
+    """Gather fold, one row at a time. ``x_rows`` says which x row a flat row
+    reads: "token" (x[row // top_k], token-major x, the page's x[token(row)])
+    or "row" (x[row], slot-major x with one row per (token, slot) row, the
+    page's x[x_row] read as the down projection's per-slot input). The
+    adapter map is indexed by the token either way."""
     out = np.array(base, dtype=np.float64, copy=True)
     for row in range(len(indices)):
         t = row // top_k
@@ -67,16 +71,20 @@ def fold_gather_scalar(x: np.ndarray, a_table: Sequence[int], b_table: Sequence[
             continue
         a = mats[a_table[e]]
         b = mats[b_table[e]]
-        h = a @ x[t]                       # [max_rank]
+        xr = x[t] if x_rows == "token" else x[row]
+        h = a @ xr                         # [max_rank]
         delta = float(scale_table[e]) * (b @ h)  # [n_out]
         out[row] = base[row] + delta
     return out
 
 
 def fold_gather(x: np.ndarray, a_table, b_table, scale_table, mats, base: np.ndarray,
-                indices, row_adapter, top_k: int) -> np.ndarray:
+                indices, row_adapter, top_k: int, x_rows: str = "token") -> np.ndarray:
     """Gather fold, one expert at a time: the live rows of each packed expert
-    are gathered and folded with two matrix products."""
+    are gathered and folded with two matrix products. ``x_rows`` as for
+    :func:`fold_gather_scalar`."""
+    if x_rows not in ("token", "row"):
+        raise ValueError(x_rows)
     out = np.array(base, dtype=np.float64, copy=True)
     indices = np.asarray(indices, dtype=np.int64)
     row_adapter = np.asarray(row_adapter, dtype=np.int64)
@@ -92,7 +100,8 @@ def fold_gather(x: np.ndarray, a_table, b_table, scale_table, mats, base: np.nda
             continue
         a = mats[a_table[e]]
         b = mats[b_table[e]]
-        h = x[tok[sel]] @ a.T              # [m, max_rank]
+        xs = x[tok[sel]] if x_rows == "token" else x[sel]
+        h = xs @ a.T                       # [m, max_rank]
         out[sel] = base[sel] + float(scale_table[e]) * (h @ b.T)
     return out
 

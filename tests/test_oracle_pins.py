@@ -166,6 +166,45 @@ def pin_grouped_hand(grouped):
     return True
 
 
+def pin_gather_x_by_row_hand(gather_rows):
+    """Hand-worked folds in the slot-major x mode (fold_hand.json,
+    gather_x_by_row): each flat row reads x at its own index."""
+    g, _, mats, a_t, b_t, s_t, base = _hand()
+    for c in g["gather_x_by_row"]:
+        x = np.array(c["x"], dtype=np.float64)
+        got = gather_rows(x, a_t, b_t, s_t, mats, base, c["indices"], c["row_adapter"],
+                          g["top_k"])
+        if not np.array_equal(got, np.array(c["expect"], dtype=np.float64)):
+            return False
+    return True
+
+
+def test_gather_x_by_row_pin():
+    for fold in (oracle.fold_gather, oracle.fold_gather_scalar):
+        assert pin_gather_x_by_row_hand(
+            lambda *a: fold(*a, x_rows="row"))
+
+
+def test_gather_x_by_row_token_mutant_is_caught():
+    """Reading x at the token (the default mode) in the slot-major mode fails
+    the hand-worked pin."""
+    assert not pin_gather_x_by_row_hand(lambda *a: oracle.fold_gather(*a, x_rows="token"))
+
+
+def test_gather_x_by_row_equals_token_mode_on_repeated_rows():
+    """Slot-major x that repeats each token's row top_k times folds exactly as
+    token-major x."""
+    v = _small_gather(seed=14)
+    c = v.case
+    x_slot = np.repeat(v.x, c.top_k, axis=0)[: c.n_rows]
+    base = np.random.default_rng(8).standard_normal((c.n_rows, 4))
+    a = oracle.fold_gather(v.x, v.a_table, v.b_table, v.scale_table, v.mats, base, c.indices,
+                           v.row_adapter, c.top_k)
+    b = oracle.fold_gather(x_slot, v.a_table, v.b_table, v.scale_table, v.mats, base, c.indices,
+                           v.row_adapter, c.top_k, x_rows="row")
+    assert np.array_equal(a, b)
+
+
 def _small_gather(seed=11, **kw):
     args = dict(n_seq=6, padded_n=8, top_k=3, n_route=7, k_in=5, n_out=4, max_rank=2,
                 dtype="f32", n_adapted=5, skip_seqs=1)
