@@ -56,7 +56,7 @@ DEFAULT_WORKLOAD = "decode_down_gather"
 # the workloads a default run measures: the decode line and, beside it, every
 # other full-size workload (the tiny fp32 one is a parity case only)
 MEASURED = ["decode_down_gather", "prefill_grouped_down", "gateup_gather", "router_gather",
-            "mixed_grouped"]
+            "mixed_grouped", "decode_layer"]
 KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_lora_amd", "csrc", "mlora_fold.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -72,6 +72,10 @@ WORKLOAD_TEXT = {
              "rank 16, bf16",
     "mixed_grouped": "mixed prefill grouped fold: 16384 sorted rows, 256 experts (77 unadapted, "
              "duplicate ids), k_in 1536, n_out 4096, rank 16, bf16, windows of 8192",
+    "decode_layer": "Qwen3-MoE-like decode layer, 64 seqs x top-8 (640 rows, 80 tokens), 128 "
+             "experts (96 adapted): router one-entry route (k_in 2048, n_out 128), gate and up "
+             "(k_in 2048, n_out 768, fused output) in one set, down on slot-major x (k_in 768, "
+             "n_out 2048); rank 16, bf16",
 }
 
 
@@ -99,11 +103,12 @@ def all_windows_groups(n_rows, cap, min_rows=16384):
     return [(s, min(s + chunk, n_rows)) for s in range(0, n_rows, chunk)]
 
 
-def algorithmic_traffic(case, tables, row_adapter, groups=None):
+def algorithmic_traffic(case, tables, row_adapter, groups=None, x_by_row=False):
     """(bytes, flops, rows, folded_rows, units) per step, summed over units.
 
     A unit is one call's worth of rows that reads its own operands: the whole
-    call for a gather, and for a grouped step each row range of `groups`
+    call for a gather (x_by_row: each row reads its own x row, so x counts per
+    folded row), and for a grouped step each row range of `groups`
     (default: the windows of grouped_down_windows). Per unit:
     bytes = unique tokens * k_in * 2 + unique experts * (r*k_in + n_out*r) * 2
           + folded rows * n_out * 2 * 2 (base_out read + write)
@@ -129,7 +134,9 @@ def algorithmic_traffic(case, tables, row_adapter, groups=None):
         tok = rows // case.top_k
         e = case.indices.astype(np.int64)
         live = (ra[tok] >= 0) & cell_ok(e)
-        units.append((case.n_rows, tok[live], e[live], 0))
+        # x rows read: the tokens', or (slot-major x) the rows' own
+        xrow = rows if x_by_row else tok
+        units.append((case.n_rows, xrow[live], e[live], 0))
     else:
         off = case.expert_offsets.astype(np.int64)
         owner = np.searchsorted(off, np.arange(case.n_rows), side="right") - 1
@@ -152,7 +159,7 @@ def algorithmic_traffic(case, tables, row_adapter, groups=None):
     for (rows, toks, exps, n_off) in units:
         f = toks.shape[0]
         b = (np.unique(toks).size * K * elt + np.unique(exps).size * (R * K + N * R) * elt
-             + f * N * elt * 2 + 4 * rows + 4 * case.n_tokens + 4 * n_off + 20 * n_exp)
+             + f * N * elt * 2 + 4 * rows + 4 * len(ra) + 4 * n_off + 20 * n_exp)
         total_b += int(b)
         flops += 2 * f * R * (K + N)
         folded += f
@@ -761,6 +768,128 @@ def measure(workload, args, cpu_seconds):
     return out
 
 
+def measure_layer(args, cpu_seconds):
+    """A decode layer's LoRA folds at the decode batch (workloads.
+    decode_layer_cases): the router's one-entry route, gate and up into the
+    two halves of one fused output, and down on slot-major x. The layer step
+    is three launches, as an engine orders them (router fold before the
+    top-k; gate and up in one projection set after their base product; down
+    after the activation); the same folds as four separate calls are timed
+    beside it, and each fold alone."""
+    import torch
+    import moe_expert_lora_amd as ml
+    import workloads
+
+    cases = workloads.decode_layer_cases()
+    router, gate, up, down = cases
+    tot = sum(copy_bytes(c) for c in cases)
+    copies = args.copies or max(2, min(64, math.ceil(640e6 / tot)))
+    st = {c.name: Staged(c, copies, two_kernel=False) for c in cases}
+    inter = gate.n_out
+    fused = [torch.cat([st["gate"].bases[k], st["up"].bases[k]], dim=1).contiguous()
+             for k in range(copies)]
+
+    def proj(name, k, out, x_by_row=False):
+        c = st[name].copies[k]
+        return ml.make_projection(c.route, c.x, out, c.indices, c.row_adapter,
+                                  st[name].case.top_k, x_by_row=x_by_row)
+
+    P = {"router": [proj("router", k, st["router"].bases[k]) for k in range(copies)],
+         "gate": [proj("gate", k, fused[k][:, :inter]) for k in range(copies)],
+         "up": [proj("up", k, fused[k][:, inter:]) for k in range(copies)],
+         "down": [proj("down", k, st["down"].bases[k], True) for k in range(copies)]}
+    torch.cuda.synchronize()
+    steps = args.steps
+    stream = torch.cuda.current_stream()
+
+    def timed(step):
+        rot = Rotation(step, copies, steps)
+        rot.run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        rot.run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del rot
+        return e0.elapsed_time(e1) * 1e3 / steps, wall / steps * 1e3
+
+    def layer_step(k):
+        ml.mlora_gather_bgmv_set([P["router"][k]])
+        ml.mlora_gather_bgmv_set([P["gate"][k], P["up"][k]])
+        ml.mlora_gather_bgmv_set([P["down"][k]])
+
+    def calls_step(k):
+        for n in ("router", "gate", "up", "down"):
+            ml.mlora_gather_bgmv_set([P[n][k]])
+
+    layer_us, layer_ms = timed(layer_step)
+    calls_us, _ = timed(calls_step)
+    alone = {n: timed(lambda k, n=n: ml.mlora_gather_bgmv_set([P[n][k]]))[0]
+             for n in ("router", "gate", "up", "down")}
+    nbytes = {}
+    rows = 0
+    for c in cases:
+        tables, ra = _tables_and_map(c)
+        b, _, r, _, _ = algorithmic_traffic(c, tables, ra, x_by_row=c.notes.get("x_rows") == "row")
+        nbytes[c.name] = b
+        rows += r
+    total = sum(nbytes.values())
+    del st, fused, P
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if cpu_seconds > 0:
+        import oracle
+        from oracle.case import OracleView, to_f64
+        from threadpoolctl import threadpool_limits
+        views = [(OracleView(c), to_f64(c.base, c.dtype), c) for c in cases]
+        threads = cpu_threads()
+
+        def run():
+            for v, b, c in views:
+                oracle.fold_gather(v.x, v.a_table, v.b_table, v.scale_table, v.mats, b,
+                                   c.indices, v.row_adapter, c.top_k,
+                                   x_rows=c.notes.get("x_rows", "token"))
+        with threadpool_limits(limits=threads):
+            run()
+            t0 = time.perf_counter()
+            it = 0
+            while True:
+                run()
+                it += 1
+                el = time.perf_counter() - t0
+                if (el >= cpu_seconds and it >= 3) or el >= 3 * cpu_seconds:
+                    break
+        cpu = {"value": rows * it / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+               "sample": f"the four folds of one decode layer, {it}x in {el:.1f} s (fp64 NumPy)",
+               "gbs": total * it / el / 1e9, "affinity_cpus": len(os.sched_getaffinity(0)),
+               "cpu_model": cpu_model()}
+    achieved = total / (layer_us * 1e-6) / 1e9
+    return {
+        "value": rows * 1e3 / layer_ms, "unit": "rows/s", "ms_per_step": layer_ms,
+        "steps": steps, "dtype": "bf16",
+        "config": {"workload": f"decode_layer: {WORKLOAD_TEXT['decode_layer']}",
+                   "path": "gather (projection sets)", "rows_per_step": rows,
+                   "kernel_dispatches_per_step": 3, "rotating_copies": copies,
+                   "timing": "HIP graphs of whole rotations over the copies plus the remainder, "
+                             "replayed; HIP events on the replay stream"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit_of_work": "one decode layer: router fold, gate/up set, down fold",
+                     "algorithmic_bytes": total, "algorithmic_bytes_per_fold": nbytes,
+                     "step_us_mean": layer_us},
+        "per_call": {"four_calls_us": calls_us,
+                     "four_calls_frac": total / (calls_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "alone_us": alone,
+                     "alone_frac": {n: nbytes[n] / (alone[n] * 1e-6) / 1e9 / HBM_PEAK_GBS
+                                    for n in alone}},
+        "cpu_baseline": cpu,
+    }
+
+
 def resolve_workloads(workload, also):
     """(main workload, workloads reported under 'also') from the command line:
     no --workload means the decode default with every other measured workload
@@ -846,6 +975,10 @@ def main():
     if args.counters:
         args.no_cpu = True
     main_cpu = 0.0 if args.no_cpu else args.cpu_seconds
+    if args.workload == "decode_layer":
+        print("bench.py: decode_layer is reported under 'also' of another workload "
+              "(e.g. --workload decode_down_gather --also decode_layer)", file=sys.stderr)
+        sys.exit(2)
     out = measure(args.workload, args, main_cpu)
     if not args.counters:
         out["hbm_copy_gbs"] = copy_bandwidth()
@@ -854,6 +987,10 @@ def main():
     if args.also:
         out["also"] = {}
         for w in args.also:
+            if w == "decode_layer":
+                out["also"][w] = measure_layer(args, 0.0 if args.no_cpu else
+                                               0.6 * args.cpu_seconds)
+                continue
             r = measure(w, args, 0.0 if args.no_cpu else 0.6 * args.cpu_seconds)
             out["also"][w] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps",
                                                  "dtype", "config", "roofline",

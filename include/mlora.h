@@ -197,6 +197,54 @@ int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void* x, int64_
                           int64_t n_slots, int32_t top_k, void* workspace,
                           uint64_t workspace_bytes, void* stream);
 
+/*
+ * [P2 MoeExpertRoute, moe_lora_gather_bgmv] One gather call of a set: a
+ * projection's route and its operands. A MoE layer builds one route per
+ * projection (gate, up, down) and the router fold a one-entry route; a set
+ * folds several such projections in one launch.
+ *   x          device, x_rows rows of x_ld elements (x_ld >= k_in, a multiple
+ *              of 8). With x_by_row == 0, flat row r reads x[r / top_k]
+ *              (token-major, as mlora_gather_bgmv); with x_by_row == 1 it
+ *              reads x[r] (slot-major: one row per (token, slot) row, the
+ *              down projection's input), and x_rows must be >= n_slots.
+ *   base_out   device, n_slots rows of out_ld elements (out_ld >= n_out, a
+ *              multiple of 8): e.g. the gate and up halves of one
+ *              [n_slots, 2 * n_out] tensor, each with out_ld = 2 * n_out.
+ *   indices    device [n_slots] expert ids; row_adapter device [map_len]
+ *              per-token map (map_len >= ceil(n_slots / top_k)); the skip
+ *              rules of mlora_gather_bgmv apply, the map indexed by
+ *              r / top_k in both x modes.
+ * x and base_out must be 16-byte aligned.
+ */
+typedef struct mlora_projection {
+  const mlora_expert_route* route;  /* host pointer                        */
+  const void* x;
+  int64_t x_rows;
+  int64_t x_ld;
+  int32_t x_by_row;
+  void* base_out;
+  int64_t out_ld;
+  const int32_t* indices;
+  const int32_t* row_adapter;
+  int64_t map_len;
+  int64_t n_slots;
+  int32_t top_k;
+} mlora_projection;
+
+/*
+ * [P2 MoeExpertRoute, moe_lora_gather_bgmv] The gather fold of 1 to 4
+ * projections in one launch (the per-layer projection set): every
+ * projection's rows are folded exactly as a mlora_gather_bgmv call without a
+ * workspace would fold them, bit for bit, whatever the other projections in
+ * the set. All projections must be bf16 and use the same number of rank
+ * blocks (ceil(max_rank / 16) rounded up to 1, 2, 4 or 8); k_in, n_out,
+ * routing and row counts may differ. Projections with no rows or no experts
+ * contribute nothing. Their base_out regions must not overlap (one launch
+ * writes them all). Returns MLORA_OK, MLORA_ERR_INVALID (nothing enqueued)
+ * or MLORA_ERR_HIP.
+ */
+int32_t mlora_gather_bgmv_set(const mlora_projection* projs, int32_t n_proj, void* stream);
+
 /* Bytes of workspace mlora_gather_bgmv may use: KC * n_slots * 64 * NB, KC =
  * clamp(ceil(ceil(k_in / 32) / 16), 1, 4) k ranges, NB = ceil(max_rank / 16)
  * rounded up to 1, 2, 4 or 8, rounded up to 256. 0 for n_slots <= 0 or invalid

@@ -52,6 +52,7 @@ EXPORTS = (
     "mlora_reload_launch_overrides",
     "mlora_grouped_down_all_noalloc",
     "mlora_apply_expert_lora_sorted",
+    "mlora_gather_bgmv_set",
 )
 
 
@@ -75,6 +76,25 @@ class ExpertRoute(ctypes.Structure):
         ("n_out", ctypes.c_int32),
         ("max_rank", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+    ]
+
+
+class Projection(ctypes.Structure):
+    """``mlora_projection``: one gather call of a projection set."""
+
+    _fields_ = [
+        ("route", ctypes.POINTER(ExpertRoute)),
+        ("x", ctypes.c_void_p),
+        ("x_rows", ctypes.c_int64),
+        ("x_ld", ctypes.c_int64),
+        ("x_by_row", ctypes.c_int32),
+        ("base_out", ctypes.c_void_p),
+        ("out_ld", ctypes.c_int64),
+        ("indices", ctypes.c_void_p),
+        ("row_adapter", ctypes.c_void_p),
+        ("map_len", ctypes.c_int64),
+        ("n_slots", ctypes.c_int64),
+        ("top_k", ctypes.c_int32),
     ]
 
 
@@ -126,6 +146,7 @@ def load() -> ctypes.CDLL:
         "mlora_reload_launch_overrides": (None, []),
         "mlora_grouped_down_all_noalloc": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64,
                                                  vp, i32, vp, vp, i32, i64, vp]),
+        "mlora_gather_bgmv_set": (i32, [ctypes.POINTER(Projection), i32, vp]),
         "mlora_apply_expert_lora_sorted": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64,
                                                  vp, _i32p, i32, _u64p, _u64p, vp, vp, i32, vp,
                                                  ctypes.c_uint64, vp]),
@@ -491,6 +512,51 @@ def mlora_apply_expert_lora_sorted(route: ExpertRoute, x, base_out, expert_offse
         _dev(sorted_ids, "sorted_ids", torch.int32),
         _dev(row_adapter, "row_adapter", torch.int32), int(top_k), ws_ptr, ws_bytes,
         _stream_handle(stream))
+    if rc != MLORA_OK:
+        raise _err(rc)
+
+
+def _rows_2d(t, name):
+    """(data pointer, rows, row stride in elements) of a 2-D device tensor
+    whose rows are contiguous (a column slice of a wider tensor is fine)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[0] == 0:  # no rows: the strides say nothing
+        return t.data_ptr(), 0, t.shape[1]
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows")
+    return t.data_ptr(), t.shape[0], (t.stride(0) if t.shape[0] > 1 else t.shape[1])
+
+
+def make_projection(route: ExpertRoute, x, base_out, indices, row_adapter, top_k: int,
+                    x_by_row: bool = False) -> Projection:
+    """One projection of a set: `x` and `base_out` are 2-D bf16 device tensors
+    with contiguous rows (their row strides become x_ld / out_ld), `indices`
+    one int32 per base_out row, `row_adapter` the int32 per-token map. The
+    caller keeps the tensors and the route alive while the set is used."""
+    import torch
+    if x.dtype != torch.bfloat16 or base_out.dtype != torch.bfloat16:
+        raise TypeError("a projection set is bf16")
+    if x.shape[1] != route.k_in or base_out.shape[1] != route.n_out:
+        raise ValueError("x / base_out widths differ from the route's k_in / n_out")
+    xp, x_rows, x_ld = _rows_2d(x, "x")
+    op, n_slots, out_ld = _rows_2d(base_out, "base_out")
+    if indices.numel() != n_slots:
+        raise ValueError("indices must have one entry per base_out row")
+    p = Projection(ctypes.pointer(route), xp, x_rows, x_ld, int(bool(x_by_row)), op, out_ld,
+                   _dev(indices, "indices", torch.int32),
+                   _dev(row_adapter, "row_adapter", torch.int32), row_adapter.numel(),
+                   n_slots, int(top_k))
+    p._keep = (route, x, base_out, indices, row_adapter)
+    return p
+
+
+def mlora_gather_bgmv_set(projections, stream=None) -> None:
+    """Gather folds of 1 to 4 projections (make_projection) in one launch."""
+    arr = (Projection * len(projections))(*projections)
+    rc = load().mlora_gather_bgmv_set(arr, len(projections), _stream_handle(stream))
     if rc != MLORA_OK:
         raise _err(rc)
 

@@ -518,8 +518,9 @@ __device__ __forceinline__ void reduce_split(const f32x4 (&hacc)[MB][NB], float*
 // Lane state of row blocks 0..MB-1 of a row list: rows 0..nrows-1, row m of
 // base_out row (s_row ? s_row[m] : row_base + m), token s_tok[m] (negative:
 // a dead row, neither read nor written).
+// x_ld / out_ld: elements from one x / base_out row to the next.
 template <int MB>
-__device__ __forceinline__ Rows<MB> rows_of(int K, int N, const int* s_row, int row_base,
+__device__ __forceinline__ Rows<MB> rows_of(int x_ld, int out_ld, const int* s_row, int row_base,
                                             const int* s_tok, int nrows, int li) {
   Rows<MB> rw;
 #pragma unroll
@@ -531,8 +532,8 @@ __device__ __forceinline__ Rows<MB> rows_of(int K, int N, const int* s_row, int 
       r = s_row ? s_row[m] : row_base + m;
     }
     rw.valid[rb] = t >= 0;
-    rw.xoff[rb] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)K * 2u;
-    rw.ooff[rb] = (uint32_t)r * (uint32_t)N * 2u;
+    rw.xoff[rb] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)x_ld * 2u;
+    rw.ooff[rb] = (uint32_t)r * (uint32_t)out_ld * 2u;
   }
   return rw;
 }
@@ -565,15 +566,15 @@ __device__ __forceinline__ void expand_rows(const Bufs& bf, int R, const Rows<MB
 }
 
 template <int NB, int MB, bool FULL_R>
-__device__ void fold_rows(const Bufs& bf, int K, int N, int R, float scale, const int* s_row,
-                          int row_base, const int* s_tok, int nrows, int n_lo, int n_hi,
-                          float* s_part) {
+__device__ void fold_rows(const Bufs& bf, int K, int R, int x_ld, int out_ld, float scale,
+                          const int* s_row, int row_base, const int* s_tok, int nrows, int n_lo,
+                          int n_hi, float* s_part) {
   constexpr int UE = Batch<NB, MB>::UE;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
   const int nrb = (nrows + 15) >> 4;
-  const Rows<MB> rw = rows_of<MB>(K, N, s_row, row_base, s_tok, nrows, li);
+  const Rows<MB> rw = rows_of<MB>(x_ld, out_ld, s_row, row_base, s_tok, nrows, li);
 
   // The first expand batch is requested once the shrink's loads are in and
   // multiplied, so the shrink's loads never queue behind it; the reduction
@@ -605,6 +606,8 @@ struct GatherArgs {
   const float* scale_table;
   uint32_t x_bytes, out_bytes;
   int32_t n_experts, K, N, R, n_slots, top_k, n_tokens;
+  int32_t x_ld, out_ld;  // elements from one x / base_out row to the next
+  int32_t x_by_row;      // 1: row r reads x[r] (slot-major x); 0: x[r / top_k]
   uint32_t top_k_magic;  // floor((2^32 - 1) / top_k)
   int32_t rs_count;      // row slices per expert
   int32_t ns_count;      // column slices per expert
@@ -619,20 +622,19 @@ struct GatherArgs {
   int32_t kc_steps;      // 32-wide k steps per range
 };
 
+// The one-kernel gather fold of work unit u (an expert's row slice and column
+// slice) of the call `p`; all threads of the workgroup call it with the same
+// unit.
 template <int NB, int MB, bool FULL_R>
-__global__ __launch_bounds__(kThreads) void gather_fold_kernel(
-    const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
-    const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
-    GatherArgs p) {
+__device__ __forceinline__ void gather_fold_unit(const uint64_t* __restrict__ a_table,
+                                                 const uint64_t* __restrict__ b_table,
+                                                 const float* __restrict__ scale_table, int u,
+                                                 int per_e, int inner, const GatherArgs& p) {
   __shared__ float s_part[kWaves * MB * 64 * 4 * NB];
   __shared__ int s_rows[kScanMax];
   __shared__ int s_toks[kScanMax];
   __shared__ int s_cnt;
 
-  // XCD-aware unit: consecutive units (the slices of one expert) on one XCD.
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int u = xcd * per_xcd + slot;
-  if (u >= units) return;
   const int e = u / per_e;
   const int within = u - e * per_e;
   const int rs = within / inner, ns = within - rs * inner;
@@ -678,19 +680,31 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(
     const int row = start + i * kThreads + (int)threadIdx.x;
     const bool hit = row < end && iv[i] == e && mv[i] >= 0;
     const int tok = (int)udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
-    wave_append(hit, row, tok, &s_cnt, s_rows, s_toks, kScanMax);
+    wave_append(hit, row, p.x_by_row ? row : tok, &s_cnt, s_rows, s_toks, kScanMax);
   }
   lds_barrier();
   const int n = __builtin_amdgcn_readfirstlane(s_cnt);
   // The first row block runs outside the loop (a loop header would make its
   // loads wait for the weight-line requests above).
   if (n > 0)
-    fold_rows<NB, MB, FULL_R>(bf, p.K, p.N, p.R, scale, s_rows, 0, s_toks, min(16 * MB, n),
+    fold_rows<NB, MB, FULL_R>(bf, p.K, p.R, p.x_ld, p.out_ld, scale, s_rows, 0, s_toks,
+                              min(16 * MB, n),
                               n_lo, n_hi, s_part);
   for (int c = 16 * MB; c < n; c += 16 * MB)
-    fold_rows<NB, MB, FULL_R>(bf, p.K, p.N, p.R, scale, s_rows + c, 0, s_toks + c,
+    fold_rows<NB, MB, FULL_R>(bf, p.K, p.R, p.x_ld, p.out_ld, scale, s_rows + c, 0, s_toks + c,
                               min(16 * MB, n - c), n_lo, n_hi, s_part);
+}
 
+template <int NB, int MB, bool FULL_R>
+__global__ __launch_bounds__(kThreads) void gather_fold_kernel(
+    const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
+    const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
+    GatherArgs p) {
+  // XCD-aware unit: consecutive units (the slices of one expert) on one XCD.
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * per_xcd + slot;
+  if (u >= units) return;
+  gather_fold_unit<NB, MB, FULL_R>(a_table, b_table, scale_table, u, per_e, inner, p);
 }
 
 
@@ -741,7 +755,7 @@ __device__ __forceinline__ int finish_scan(const GatherArgs& p, int e, int start
     const int row = start + i * kThreads + (int)threadIdx.x;
     const bool hit = row < end && sl.iv[i] == e && sl.mv[i] >= 0;
     const int tok = (int)udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
-    wave_append(hit, row, tok, s_cnt, s_rows, s_toks, kScanMax);
+    wave_append(hit, row, p.x_by_row ? row : tok, s_cnt, s_rows, s_toks, kScanMax);
   }
   lds_barrier();
   return __builtin_amdgcn_readfirstlane(*s_cnt);
@@ -813,7 +827,7 @@ __global__ __launch_bounds__(kThreads) void gather_shrink_kernel(
 
   auto block = [&](int c, bool first) {
     const int nrows = min(16 * MB, n - c), nrb = (nrows + 15) >> 4;
-    const Rows<MB> rw = rows_of<MB>(K, p.N, s_rows + c, 0, s_toks + c, nrows, li);
+    const Rows<MB> rw = rows_of<MB>(p.x_ld, p.out_ld, s_rows + c, 0, s_toks + c, nrows, li);
     u32x4 xv[kTwoSteps][MB];
 #pragma unroll
     for (int t = 0; t < kTwoSteps; ++t) {
@@ -933,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(
 
   auto block = [&](int c, bool first) {
     const int nrows = min(16 * MB, n - c), nrb = (nrows + 15) >> 4;
-    const Rows<MB> rw = rows_of<MB>(p.K, p.N, s_rows + c, 0, s_toks + c, nrows, li);
+    const Rows<MB> rw = rows_of<MB>(p.x_ld, p.out_ld, s_rows + c, 0, s_toks + c, nrows, li);
     // partial sums of every k range and the base_out fragments, requested together
     u32x4 pv[kMaxKc][MB][NB];
 #pragma unroll
@@ -1109,7 +1123,7 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
     const int row = start + i * kThreads + (int)threadIdx.x;
     const bool hit = row < end && iv[i] == e && mv[i] >= 0;
     const int tok = (int)udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
-    wave_append(hit, row, tok, &s_cnt, s_rows, s_toks, kScanMax);
+    wave_append(hit, row, p.x_by_row ? row : tok, &s_cnt, s_rows, s_toks, kScanMax);
   }
   lds_barrier();
   const int n = __builtin_amdgcn_readfirstlane(s_cnt);
@@ -1126,8 +1140,8 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
       r = s_rows[m];
     }
     const bool valid = t >= 0;
-    const uint32_t xoff = (uint32_t)(valid ? t : 0) * (uint32_t)K * 2u;
-    const uint32_t ooff = (uint32_t)r * (uint32_t)N * 2u;
+    const uint32_t xoff = (uint32_t)(valid ? t : 0) * (uint32_t)p.x_ld * 2u;
+    const uint32_t ooff = (uint32_t)r * (uint32_t)p.out_ld * 2u;
     u32x4 xv[kResSteps], ov[kResSteps];
 #pragma unroll
     for (int u = 0; u < kResSteps; ++u) {
@@ -1209,6 +1223,56 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
   if (n > 0) chunk(0, true);
   for (int c = 16; c < n; c += 16) chunk(c, false);
 }
+
+// ---------------------------------------------------------------------------
+// gather, several projections in one launch
+// ---------------------------------------------------------------------------
+
+// A set of up to kMaxProj gather calls (projections), each with its own
+// tables, x, base_out and routing, run by one launch: the units of call i
+// are first[i] .. first[i+1]-1 of one unit range, mapped to XCDs as one
+// call's units are, so each call's consecutive units still share an XCD.
+constexpr int kMaxProj = 4;
+
+struct GatherSet {
+  GatherArgs a[kMaxProj];
+  int32_t first[kMaxProj + 1];
+  int32_t n;
+  int32_t total;  // units of every call (first[n]; kept apart so that no
+                  // argument is indexed at run time)
+  int32_t per_xcd;
+};
+
+// The call that unit u (wave-uniform) belongs to.
+__device__ __forceinline__ int set_member(const GatherSet& s, int u) {
+  return (s.n > 1 && u >= s.first[1] ? 1 : 0) + (s.n > 2 && u >= s.first[2] ? 1 : 0) +
+         (s.n > 3 && u >= s.first[3] ? 1 : 0);
+}
+
+// The unit body with member m's arguments read at constant offsets: one
+// inlined copy per member. (Picking the arguments field by field with
+// selects instead measured 2.2x slower on the same unit; copying the
+// picked struct goes through private memory.)
+#define MLORA_SET_DISPATCH(BODY)                             \
+  switch (set_member(s, u)) {                                \
+    case 0: { const GatherArgs& g = s.a[0]; BODY(0); break; } \
+    case 1: { const GatherArgs& g = s.a[1]; BODY(1); break; } \
+    case 2: { const GatherArgs& g = s.a[2]; BODY(2); break; } \
+    default: { const GatherArgs& g = s.a[3]; BODY(3); break; } \
+  }
+
+template <int NB, int MB, bool FULL_R>
+__global__ __launch_bounds__(kThreads) void gather_fold_set_kernel(GatherSet s) {
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * s.per_xcd + slot;
+  if (u >= s.total) return;
+#define MLORA_FOLD_BODY(m)                                                              \
+  gather_fold_unit<NB, MB, FULL_R>(g.a_table, g.b_table, g.scale_table, u - s.first[m], \
+                                   g.rs_count * g.ns_count, g.ns_count, g)
+  MLORA_SET_DISPATCH(MLORA_FOLD_BODY)
+#undef MLORA_FOLD_BODY
+}
+#undef MLORA_SET_DISPATCH
 
 // ---------------------------------------------------------------------------
 // grouped (prefill) kernel
@@ -1305,7 +1369,7 @@ __global__ __launch_bounds__(kThreads) void grouped_fold_kernel(GroupedArgs p) {
     const int lo = __builtin_amdgcn_readfirstlane(s_seg_lo[sg]);
     const int hi = __builtin_amdgcn_readfirstlane(s_seg_hi[sg]);
     for (int c = lo; c < hi; c += 16 * MB)
-      fold_rows<NB, MB, FULL_R>(bf, p.K, p.N, p.R, scale, nullptr, tile_row + c, s_tok + c,
+      fold_rows<NB, MB, FULL_R>(bf, p.K, p.R, p.K, p.N, scale, nullptr, tile_row + c, s_tok + c,
                                 min(16 * MB, hi - c), n_lo, n_hi, s_part);
   }
 }
@@ -2102,6 +2166,105 @@ void dispatch_grouped(const GroupedArgs& a, int grid, hipStream_t s, int mb) {
   else launch_grouped<8, 1>(a, grid, s);
 }
 
+// The one-kernel launch of a bf16 gather call: its arguments, grid and
+// kernel choice. x has x_rows rows of x_ld elements (row r / top_k, or row r
+// itself with x_by_row), base_out n_slots rows of out_ld elements, the map
+// map_len entries. Validates what the kernels assume; MLORA_OK or an error.
+struct GatherPlan {
+  GatherArgs a;
+  int grid;
+  int small, resident;
+  bool use_resident;
+};
+
+int32_t plan_gather(const char* who, const mlora_expert_route* route, const void* x,
+                    int64_t x_rows, int64_t x_ld, int32_t x_by_row, void* base_out,
+                    int64_t out_ld, const int32_t* indices, const int32_t* row_adapter,
+                    int64_t map_len, int64_t n_slots, int32_t top_k, GatherPlan* plan) {
+  if (!aligned16(x) || !aligned16(base_out))
+    return fail(MLORA_ERR_INVALID, "%s: x and base_out must be 16-byte aligned", who);
+  const int E = route->n_experts, K = route->k_in, N = route->n_out, R = route->max_rank;
+  if (x_ld < K || x_ld % 8 || out_ld < N || out_ld % 8)
+    return fail(MLORA_ERR_INVALID,
+                "%s: row strides x_ld=%lld / out_ld=%lld must be multiples of 8 and at least "
+                "k_in=%d / n_out=%d", who, (long long)x_ld, (long long)out_ld, K, N);
+  const int64_t x_bytes = ((x_rows > 0 ? x_rows - 1 : 0) * x_ld + K) * 2;
+  const int64_t out_bytes = ((n_slots - 1) * out_ld + N) * 2;
+  if (x_bytes > (int64_t)kMaxBufBytes || out_bytes > (int64_t)kMaxBufBytes)
+    return fail(MLORA_ERR_INVALID, "%s: x or base_out exceeds 4 GiB; split the call", who);
+  const int ns_max = (N + kColStep - 1) / kColStep;
+
+  // Launch shape. Row slices first (each slice scans at most kScanMax rows),
+  // then more row slices while slices keep enough rows, then column slices
+  // while the repeated shrink stays cheaper than the expand it splits.
+  const int64_t rows_per_e = (n_slots + E - 1) / E;
+  int rs = (int)((n_slots + kScanMax - 1) / kScanMax);
+  int ns = 1;
+  const int64_t target = 256;  // one workgroup per CU; measured better than two
+  while ((int64_t)E * rs * ns < target && rows_per_e / (rs * 2) >= 32) rs *= 2;
+  // A call with very few experts (a one-entry route over a decode batch)
+  // goes on to slices of as few as 4 rows rather than run on a handful of
+  // workgroups: the router's fold over 80 decode tokens (k_in 2048) measured
+  // 11.3 us at 2 slices, 7.6-8.0 us at 8-16.
+  while ((int64_t)E * rs * ns < target / 4 && rows_per_e / (rs * 2) >= 4) rs *= 2;
+  const double shrink_b = 2.0 * R * K + 2.0 * (double)rows_per_e / rs * K;
+  const double expand_b = 2.0 * N * R + 4.0 * (double)rows_per_e / rs * N;
+  while ((int64_t)E * rs * ns < target && ns * 2 <= ns_max &&
+         (ns * 2) * shrink_b <= 2.0 * (shrink_b + expand_b))
+    ns *= 2;
+  rs = ov(overrides().gather_rs, rs);
+  ns = ov(overrides().gather_ns, ns);
+  if (ns < 1) ns = 1;
+  if (ns > ns_max) ns = ns_max;
+  if (rs < 1) rs = 1;
+  int scan = (int)((n_slots + rs - 1) / rs);
+  if (scan > kScanMax) {
+    rs = (int)((n_slots + kScanMax - 1) / kScanMax);
+    scan = (int)((n_slots + rs - 1) / rs);
+  }
+
+  GatherArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.out = static_cast<uint16_t*>(base_out);
+  a.indices = indices;
+  a.row_adapter = row_adapter;
+  a.a_table = route->a_table;
+  a.b_table = route->b_table;
+  a.scale_table = route->scale_table;
+  a.x_bytes = (uint32_t)x_bytes;
+  a.out_bytes = (uint32_t)out_bytes;
+  a.n_experts = E;
+  a.K = K;
+  a.N = N;
+  a.R = R;
+  a.n_slots = (int32_t)n_slots;
+  a.top_k = top_k;
+  a.n_tokens = (int32_t)map_len;
+  a.x_ld = (int32_t)x_ld;
+  a.out_ld = (int32_t)out_ld;
+  a.x_by_row = x_by_row ? 1 : 0;
+  a.top_k_magic = magic_for(top_k);
+  a.rs_count = rs;
+  a.ns_count = ns;
+  a.scan_len = scan;
+  a.ns_cols = ns_cols_for(N, ns);
+  const int64_t units = (int64_t)E * rs * ns;
+  if (units > 0x7fffffffll / 2)
+    return fail(MLORA_ERR_INVALID, "%s: launch too large", who);
+  a.units = (int32_t)units;
+  a.per_xcd = (int32_t)((units + kXcds - 1) / kXcds);
+  plan->a = a;
+  plan->grid = a.per_xcd * kXcds;
+  // one 16-row block per chunk when a slice is expected to hold few rows
+  const int64_t rows_per_slice = (n_slots + (int64_t)E * rs - 1) / ((int64_t)E * rs);
+  plan->small = ov(overrides().gather_small, rows_per_slice <= 16 ? 1 : 0);
+  // weights held in registers when a slice is expected to hold at most two
+  // 16-row blocks (and the wave's share fits)
+  plan->resident = ov(overrides().gather_resident, rows_per_slice <= 32 ? 1 : 0);
+  plan->use_resident = plan->resident != 0 && gather_resident_fits(a);
+  return MLORA_OK;
+}
+
 }  // namespace
 }  // namespace mlora
 
@@ -2158,73 +2321,17 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
     return launched(who);
   }
 
-  if (!aligned16(x) || !aligned16(base_out))
-    return fail(MLORA_ERR_INVALID, "%s: x and base_out must be 16-byte aligned", who);
-  const int E = route->n_experts, K = route->k_in, N = route->n_out, R = route->max_rank;
-  const int64_t x_bytes = n_tokens * K * 2, out_bytes = n_slots * N * 2;
-  if (x_bytes > (int64_t)kMaxBufBytes || out_bytes > (int64_t)kMaxBufBytes)
-    return fail(MLORA_ERR_INVALID, "%s: x or base_out exceeds 4 GiB; split the call", who);
+  GatherPlan plan;
+  if (int32_t rc = plan_gather(who, route, x, n_tokens, route->k_in, 0, base_out, route->n_out,
+                               indices, row_adapter, n_tokens, n_slots, top_k, &plan))
+    return rc;
+  const GatherArgs& a = plan.a;
+  const int grid = plan.grid;
+  const int small = plan.small;
+  const int resident = plan.resident;
+  const bool use_resident = plan.use_resident;
+  const int E = a.n_experts, K = a.K, N = a.N, R = a.R;
   const int ns_max = (N + kColStep - 1) / kColStep;
-
-  // Launch shape. Row slices first (each slice scans at most kScanMax rows),
-  // then more row slices while slices keep enough rows, then column slices
-  // while the repeated shrink stays cheaper than the expand it splits.
-  const int64_t rows_per_e = (n_slots + E - 1) / E;
-  int rs = (int)((n_slots + kScanMax - 1) / kScanMax);
-  int ns = 1;
-  const int64_t target = 256;  // one workgroup per CU; measured better than two
-  while ((int64_t)E * rs * ns < target && rows_per_e / (rs * 2) >= 32) rs *= 2;
-  const double shrink_b = 2.0 * R * K + 2.0 * (double)rows_per_e / rs * K;
-  const double expand_b = 2.0 * N * R + 4.0 * (double)rows_per_e / rs * N;
-  while ((int64_t)E * rs * ns < target && ns * 2 <= ns_max &&
-         (ns * 2) * shrink_b <= 2.0 * (shrink_b + expand_b))
-    ns *= 2;
-  rs = ov(overrides().gather_rs, rs);
-  ns = ov(overrides().gather_ns, ns);
-  if (ns < 1) ns = 1;
-  if (ns > ns_max) ns = ns_max;
-  if (rs < 1) rs = 1;
-  int scan = (int)((n_slots + rs - 1) / rs);
-  if (scan > kScanMax) {
-    rs = (int)((n_slots + kScanMax - 1) / kScanMax);
-    scan = (int)((n_slots + rs - 1) / rs);
-  }
-
-  GatherArgs a{};
-  a.x = static_cast<const uint16_t*>(x);
-  a.out = static_cast<uint16_t*>(base_out);
-  a.indices = indices;
-  a.row_adapter = row_adapter;
-  a.a_table = route->a_table;
-  a.b_table = route->b_table;
-  a.scale_table = route->scale_table;
-  a.x_bytes = (uint32_t)x_bytes;
-  a.out_bytes = (uint32_t)out_bytes;
-  a.n_experts = E;
-  a.K = K;
-  a.N = N;
-  a.R = R;
-  a.n_slots = (int32_t)n_slots;
-  a.top_k = top_k;
-  a.n_tokens = (int32_t)n_tokens;
-  a.top_k_magic = magic_for(top_k);
-  a.rs_count = rs;
-  a.ns_count = ns;
-  a.scan_len = scan;
-  a.ns_cols = ns_cols_for(N, ns);
-  const int64_t units = (int64_t)E * rs * ns;
-  if (units > 0x7fffffffll / 2)
-    return fail(MLORA_ERR_INVALID, "%s: launch too large", who);
-  a.units = (int32_t)units;
-  a.per_xcd = (int32_t)((units + kXcds - 1) / kXcds);
-  const int grid = a.per_xcd * kXcds;
-  // one 16-row block per chunk when a slice is expected to hold few rows
-  const int64_t rows_per_slice = (n_slots + (int64_t)E * rs - 1) / ((int64_t)E * rs);
-  const int small = ov(overrides().gather_small, rows_per_slice <= 16 ? 1 : 0);
-  // weights held in registers when a slice is expected to hold at most two
-  // 16-row blocks (and the wave's share fits)
-  const int resident = ov(overrides().gather_resident, rows_per_slice <= 32 ? 1 : 0);
-  const bool use_resident = resident != 0 && gather_resident_fits(a);
   // The two-kernel form holds at most kWaves * kTwoSteps k steps per range.
   // It pays where an expert's A_e outweighs its rows' x (few rows per expert,
   // k_in split over several ranges); an expert with many rows streams x once
@@ -2282,6 +2389,119 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
     return launched(who);
   }
   dispatch_gather(a, grid, s, small != 0, resident != 0);
+  return launched(who);
+}
+
+namespace mlora {
+namespace {
+
+template <int NB, int MB, bool FULL_R>
+void launch_fold_set(const GatherSet& gs, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gather_fold_set_kernel<NB, MB, FULL_R>), dim3(grid), dim3(kThreads), 0, s,
+                     gs);
+}
+
+template <bool FULL_R>
+void dispatch_set(const GatherSet& gs, int grid, hipStream_t s, int nb, bool small) {
+  if (nb <= 1) {
+    if (small) return launch_fold_set<1, 1, FULL_R>(gs, grid, s);
+    return launch_fold_set<1, 4, FULL_R>(gs, grid, s);
+  }
+  if (nb <= 2) {
+    if (small) return launch_fold_set<2, 1, FULL_R>(gs, grid, s);
+    return launch_fold_set<2, 4, FULL_R>(gs, grid, s);
+  }
+  if (nb <= 4) {
+    if (small) return launch_fold_set<4, 1, FULL_R>(gs, grid, s);
+    return launch_fold_set<4, 2, FULL_R>(gs, grid, s);
+  }
+  launch_fold_set<8, 1, FULL_R>(gs, grid, s);
+}
+
+}  // namespace
+}  // namespace mlora
+
+extern "C" int32_t mlora_gather_bgmv_set(const mlora_projection* projs, int32_t n_proj,
+                                         void* stream) {
+  const char* who = "mlora_gather_bgmv_set";
+  if (n_proj < 1 || n_proj > kMaxProj)
+    return fail(MLORA_ERR_INVALID, "%s: n_proj=%d outside 1..%d", who, n_proj, kMaxProj);
+  if (!projs) return fail(MLORA_ERR_INVALID, "%s: NULL projections", who);
+  GatherSet gs{};
+  GatherPlan plans[kMaxProj];
+  int nb = 0, members = 0, only = -1;
+  bool full = true, small = true;
+  int64_t total = 0;
+  gs.first[0] = 0;
+  for (int32_t i = 0; i < n_proj; ++i) {
+    const mlora_projection& pj = projs[i];
+    if (int32_t rc = check_route(pj.route, who)) return rc;
+    const mlora_expert_route* r = pj.route;
+    if (r->dtype != MLORA_BF16)
+      return fail(MLORA_ERR_INVALID, "%s: projection %d is not bf16", who, i);
+    if (pj.top_k <= 0)
+      return fail(MLORA_ERR_INVALID, "%s: projection %d: top_k=%d must be positive", who, i,
+                  pj.top_k);
+    if (pj.n_slots < 0 || pj.n_slots > (int64_t)0x7fffffff - kScanMax)
+      return fail(MLORA_ERR_INVALID, "%s: projection %d: n_slots out of range", who, i);
+    const int64_t need_tok = (pj.n_slots + pj.top_k - 1) / pj.top_k;
+    const int64_t need_x = pj.x_by_row ? pj.n_slots : need_tok;
+    if (pj.map_len < need_tok || pj.map_len > 0x3fffffffll || pj.x_rows < need_x ||
+        pj.x_rows > 0x3fffffffll)
+      return fail(MLORA_ERR_INVALID,
+                  "%s: projection %d: %lld map entries and %lld x rows, need >= %lld and %lld",
+                  who, i, (long long)pj.map_len, (long long)pj.x_rows, (long long)need_tok,
+                  (long long)need_x);
+    if (nb == 0) nb = kernel_nb(r->max_rank);
+    if (kernel_nb(r->max_rank) != nb)
+      return fail(MLORA_ERR_INVALID,
+                  "%s: projection %d: max_rank %d and the first one's need different rank "
+                  "blocks (ceil(max_rank / 16) rounded to 1, 2, 4, 8 must agree)",
+                  who, i, r->max_rank);
+    if (pj.n_slots == 0 || r->n_experts == 0) {
+      gs.first[i + 1] = (int32_t)total;
+      gs.a[i] = GatherArgs{};
+      continue;
+    }
+    if (!pj.x || !pj.base_out || !pj.indices || !pj.row_adapter)
+      return fail(MLORA_ERR_INVALID, "%s: projection %d: NULL device pointer", who, i);
+    GatherPlan plan;
+    if (int32_t rc = plan_gather(who, r, pj.x, pj.x_rows, pj.x_ld, pj.x_by_row, pj.base_out,
+                                 pj.out_ld, pj.indices, pj.row_adapter, pj.map_len, pj.n_slots,
+                                 pj.top_k, &plan))
+      return rc;
+    gs.a[i] = plan.a;
+    plans[i] = plan;
+    ++members;
+    only = i;
+    full = full && r->max_rank == 16 * nb;
+    small = small && plan.small != 0;
+    total += plan.a.units;
+    if (total > 0x3fffffffll) return fail(MLORA_ERR_INVALID, "%s: launch too large", who);
+    gs.first[i + 1] = (int32_t)total;
+  }
+  for (int32_t i = n_proj; i < kMaxProj; ++i) gs.first[i + 1] = (int32_t)total;
+  gs.n = n_proj;
+  gs.total = (int32_t)total;
+  if (total == 0) {
+    clear_error();
+    return MLORA_OK;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (members == 1) {
+    // one call with rows: the single-call kernels (the decode-resident one
+    // where it fits), which take their leading arguments preloaded
+    const GatherPlan& pl = plans[only];
+    dispatch_gather(pl.a, pl.grid, s, pl.small != 0, pl.resident != 0);
+    return launched(who);
+  }
+  gs.per_xcd = (int32_t)((total + kXcds - 1) / kXcds);
+  const int grid = gs.per_xcd * kXcds;
+  if (full)
+    dispatch_set<true>(gs, grid, s, nb, small);
+  else
+    dispatch_set<false>(gs, grid, s, nb, small);
   return launched(who);
 }
 

@@ -28,7 +28,7 @@ def test_more_than_one_gpu_is_refused():
 
 @pytest.mark.parametrize("workload,also,want", [
     (None, None, ("decode_down_gather", ["prefill_grouped_down", "gateup_gather",
-                                          "router_gather", "mixed_grouped"])),
+                                          "router_gather", "mixed_grouped", "decode_layer"])),
     ("router_gather", None, ("router_gather", [])),
     ("prefill_grouped_down", None, ("prefill_grouped_down", [])),
     (None, "none", ("decode_down_gather", [])),
@@ -65,6 +65,9 @@ def test_algorithmic_bytes_gather_hand_count():
     got = bench.algorithmic_traffic(case, tables, ra)
     want = 2 * PER_TOKEN + 2 * PER_EXPERT + 3 * PER_ROW + 4 * 6 + 4 * 3 + 20 * 3
     assert got == (want, 2 * 3 * R * (K + N), 6, 3, 1)
+    # slot-major x: each of the 3 folded rows reads its own x row
+    got = bench.algorithmic_traffic(case, tables, ra, x_by_row=True)
+    assert got[0] == want + PER_TOKEN
 
 
 def test_algorithmic_bytes_grouped_hand_count():

@@ -1,0 +1,166 @@
+"""GPU parity of the per-layer projection set (mlora_gather_bgmv_set, one
+launch for several gather calls), through the C ABI.
+
+A decode layer's folds as a set: a one-entry router route over the tokens,
+gate and up over the (token, slot) rows writing the two halves of one fused
+[rows, 2 * n_out] output (row stride 2 * n_out), and down reading slot-major
+x (one x row per flat row). Every projection of a set must come out exactly
+as the same call alone (bit for bit), meet the oracle bound, and leave every
+element outside its rows and columns untouched.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from tests.common import REL_L2_TOL, OracleView, parity_figures, to_f64
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def layer_cases(seed=100):
+    """A decode layer's router, gate, up and slot-major down folds at small
+    sizes (24 sequences x top-4 over 40 experts, hidden 512, inter 384)."""
+    return workloads.decode_layer_cases(seed=seed, n_seq=24, padded_n=32, top_k=4, n_route=40,
+                                        n_adapted=34, skip_seqs=3, hidden=512, inter=384)
+
+
+def oracle_fold(case, base):
+    import oracle
+    view = OracleView(case)
+    x_rows = case.notes.get("x_rows", "token")
+    ref = oracle.fold_gather(view.x, view.a_table, view.b_table, view.scale_table, view.mats,
+                             to_f64(base, case.dtype), case.indices, view.row_adapter,
+                             case.top_k, x_rows=x_rows)
+    return view, ref
+
+
+def test_layer_set_equals_calls_alone_and_the_oracle():
+    import moe_expert_lora_amd as ml
+    from staging import DeviceCase, from_torch, to_torch
+    _need_gpu()
+    router, gate, up, down = layer_cases()
+    devs = {c.name: DeviceCase(c, DEV) for c in (router, gate, up, down)}
+    inter = gate.n_out
+    # fused gate/up output with a 16-column guard band after each half's row
+    guard = 16
+    fused0 = np.full((gate.n_rows, 2 * inter + guard), 0x7F81, dtype=np.uint16)
+    fused0[:, :inter] = gate.base
+    fused0[:, inter:2 * inter] = up.base
+    fused = to_torch(fused0, "bf16", DEV)
+    outs = {"router": devs["router"].base0.clone(), "down": devs["down"].base0.clone()}
+    projs = [
+        ml.make_projection(devs["router"].route, devs["router"].x, outs["router"],
+                           devs["router"].indices, devs["router"].row_adapter, 1),
+        ml.make_projection(devs["gate"].route, devs["gate"].x, fused[:, :inter],
+                           devs["gate"].indices, devs["gate"].row_adapter, gate.top_k),
+        ml.make_projection(devs["up"].route, devs["up"].x, fused[:, inter:2 * inter],
+                           devs["up"].indices, devs["up"].row_adapter, up.top_k),
+        ml.make_projection(devs["down"].route, devs["down"].x, outs["down"],
+                           devs["down"].indices, devs["down"].row_adapter, down.top_k,
+                           x_by_row=True),
+    ]
+    ml.mlora_gather_bgmv_set(projs)
+    torch.cuda.synchronize()
+    got_f = from_torch(fused)
+    got = {"router": from_torch(outs["router"]), "gate": got_f[:, :inter],
+           "up": got_f[:, inter:2 * inter], "down": from_torch(outs["down"])}
+    # the guard band after the two halves is untouched
+    assert np.all(got_f[:, 2 * inter:] == 0x7F81)
+    for c in (router, gate, up):
+        alone = devs[c.name].run(two_kernel=False)
+        assert np.array_equal(got[c.name].view(np.uint16), alone.view(np.uint16)), c.name
+    # one projection alone through the set entry equals the plain call
+    solo = devs["gate"].base0.clone()
+    ml.mlora_gather_bgmv_set([ml.make_projection(devs["gate"].route, devs["gate"].x, solo,
+                                                 devs["gate"].indices,
+                                                 devs["gate"].row_adapter, gate.top_k)])
+    torch.cuda.synchronize()
+    assert np.array_equal(from_torch(solo), got["gate"])
+    for c in (router, gate, up, down):
+        view, ref = oracle_fold(c, c.base)
+        rel, mx, ex = parity_figures(view, to_f64(got[c.name], "bf16"), ref, f"set {c.name}")
+        print(f"set {c.name}: rel_l2={rel:.3e} max_abs={mx:.3e} max_abs/limit={ex:.3f}",
+              flush=True)
+        assert rel <= REL_L2_TOL and ex <= 1.0, c.name
+        live = view.live_rows()
+        assert np.array_equal(got[c.name][~live], c.base[~live]), c.name
+
+
+def test_slot_major_down_rows_and_untouched_rows():
+    """Slot-major x: every row folds its own x row; rows the fold skips keep
+    a signalling-NaN sentinel bit for bit; and x rows that repeat each
+    token's row top_k times fold exactly as the token-major call."""
+    import moe_expert_lora_amd as ml
+    from staging import DeviceCase, from_torch, to_torch
+    _need_gpu()
+    _, gate, _, down = layer_cases(seed=120)
+    dev = DeviceCase(down, DEV)
+    view, _ = oracle_fold(down, down.base)
+    live = view.live_rows()
+    base = down.base.copy()
+    base.view(np.uint16)[~live] = 0x7F81
+    out = to_torch(base, "bf16", DEV)
+    ml.mlora_gather_bgmv_set([ml.make_projection(dev.route, dev.x, out, dev.indices,
+                                                 dev.row_adapter, down.top_k, x_by_row=True)])
+    torch.cuda.synchronize()
+    got = from_torch(out)
+    assert np.array_equal(got[~live], base[~live])
+    # repeated token rows == token-major
+    g = DeviceCase(gate, DEV)
+    want = g.run(two_kernel=False)
+    x_rep = g.x.repeat_interleave(gate.top_k, dim=0)[: gate.n_rows].contiguous()
+    out2 = g.base0.clone()
+    ml.mlora_gather_bgmv_set([ml.make_projection(g.route, x_rep, out2, g.indices,
+                                                 g.row_adapter, gate.top_k, x_by_row=True)])
+    torch.cuda.synchronize()
+    assert np.array_equal(from_torch(out2), want)
+
+
+@pytest.mark.parametrize("shape", ["resident", "streaming_r32", "mixed_empty"])
+def test_set_shapes(shape):
+    """Sets that run the resident decode kernel (k_in <= 1024, rank 16), the
+    streaming one (ranks 32, 24 and 20: two rank blocks each), and a set with
+    an empty projection (no rows): each member equals its call alone."""
+    import moe_expert_lora_amd as ml
+    from staging import DeviceCase, from_torch
+    _need_gpu()
+    if shape == "resident":
+        cases = [workloads.decode_down_gather(),
+                 workloads.make_gather_case(130, n_seq=40, padded_n=48, top_k=8, n_route=64,
+                                            k_in=640, n_out=1024, max_rank=16, n_adapted=50,
+                                            skip_seqs=4)]
+    elif shape == "streaming_r32":
+        cases = [workloads.make_gather_case(131 + i, n_seq=100, padded_n=100, top_k=4,
+                                            n_route=32, k_in=1536 + 256 * i, n_out=264,
+                                            max_rank=(32, 24, 20)[i], n_adapted=30)
+                 for i in range(3)]
+    else:
+        cases = [workloads.make_gather_case(140, n_seq=30, padded_n=30, top_k=2, n_route=12,
+                                            k_in=256, n_out=200, max_rank=16, n_adapted=10),
+                 workloads.make_gather_case(141, n_seq=0, padded_n=0, top_k=2, n_route=12,
+                                            k_in=256, n_out=200, max_rank=16, n_adapted=10,
+                                            n_slots=0),
+                 workloads.make_gather_case(142, n_seq=10, padded_n=10, top_k=2, n_route=12,
+                                            k_in=256, n_out=200, max_rank=16, n_adapted=10)]
+    devs = [DeviceCase(c, DEV) for c in cases]
+    outs = [d.base0.clone() for d in devs]
+    projs = [ml.make_projection(d.route, d.x, o, d.indices, d.row_adapter, c.top_k)
+             for c, d, o in zip(cases, devs, outs)]
+    ml.mlora_gather_bgmv_set(projs)
+    torch.cuda.synchronize()
+    for c, d, o in zip(cases, devs, outs):
+        if c.n_rows == 0:
+            continue
+        alone = d.run(two_kernel=False)
+        assert np.array_equal(from_torch(o).view(np.uint16), alone.view(np.uint16)), c.name

@@ -423,6 +423,42 @@ def test_host_loop_rejects_bad_host_spans(lib):
         assert "span" in lib.mlora_last_error().decode()
 
 
+def _proj(route, **kw):
+    f = dict(x=FAKE, x_rows=64, x_ld=64, x_by_row=0, base_out=FAKE, out_ld=32, indices=FAKE,
+             row_adapter=FAKE, map_len=64, n_slots=64, top_k=1)
+    f.update(kw)
+    return ml.Projection(ctypes.pointer(route), f["x"], f["x_rows"], f["x_ld"], f["x_by_row"],
+                         f["base_out"], f["out_ld"], f["indices"], f["row_adapter"],
+                         f["map_len"], f["n_slots"], f["top_k"])
+
+
+def test_gather_set_rejects_bad_sets(lib):
+    """Every projection is checked before anything is launched (no HIP call
+    is made here)."""
+    r16, r32, r64 = _route(max_rank=16), _route(max_rank=32), _route(max_rank=64)
+    f32 = _route(max_rank=16, dtype=ml.MLORA_F32)
+
+    def call(*projs):
+        arr = (ml.Projection * len(projs))(*projs)
+        return lib.mlora_gather_bgmv_set(arr, len(projs), None)
+
+    assert lib.mlora_gather_bgmv_set(None, 0, None) == ml.MLORA_ERR_INVALID
+    assert call(*[_proj(r16)] * 5) == ml.MLORA_ERR_INVALID            # more than 4
+    assert call(_proj(r16), _proj(r64)) == ml.MLORA_ERR_INVALID       # rank blocks differ
+    assert "rank blocks" in lib.mlora_last_error().decode()
+    assert call(_proj(f32)) == ml.MLORA_ERR_INVALID                   # bf16 only
+    assert call(_proj(r16, x_ld=60)) == ml.MLORA_ERR_INVALID          # x_ld < k_in
+    assert call(_proj(r16, out_ld=36)) == ml.MLORA_ERR_INVALID        # not a multiple of 8
+    assert call(_proj(r16, x_by_row=1, x_rows=63)) == ml.MLORA_ERR_INVALID  # < n_slots
+    assert call(_proj(r16, top_k=4, map_len=15)) == ml.MLORA_ERR_INVALID    # < ceil(64 / 4)
+    assert call(_proj(r16, base_out=FAKE + 8)) == ml.MLORA_ERR_INVALID      # misaligned
+    assert call(_proj(r16), _proj(r16, x=0)) == ml.MLORA_ERR_INVALID        # NULL
+    # ranks 17..32 share two rank blocks: a valid mix, rejected here only for
+    # its NULL x
+    assert call(_proj(r32), _proj(_route(max_rank=24), x=0)) == ml.MLORA_ERR_INVALID
+    assert "projection 1" in lib.mlora_last_error().decode()
+
+
 def test_gather_workspace_bytes(lib):
     f = lib.mlora_gather_bgmv_workspace_bytes
     # KC k ranges (16 k steps each, at most 4) x n_slots x 64 x NB bytes,

@@ -379,6 +379,46 @@ def mixed_grouped() -> FoldCase:
                              name="mixed_grouped")
 
 
+def _with_routing_of(case: FoldCase, like: FoldCase) -> FoldCase:
+    """`case` with the routing (expert ids, adapter slots) of `like`."""
+    case.indices = like.indices.copy()
+    case.adapter_slots = like.adapter_slots.copy()
+    case.padded_n = like.padded_n
+    return case
+
+
+def decode_layer_cases(seed: int = 60, n_seq: int = 64, padded_n: int = 80, top_k: int = 8,
+                       n_route: int = 128, n_adapted: int = 96, skip_seqs: int = 6,
+                       hidden: int = 2048, inter: int = 768, rank: int = 16):
+    """The four folds of one Qwen3-MoE-like decode layer over one batch, as
+    gather problems: the router's one-entry route over the token rows
+    (top_k 1, n_out = n_route expert logits), gate and up over the flat
+    (token, slot) rows (hidden -> inter, one routing, their own adapted sets
+    and weights), and down reading slot-major x (one inter-wide row per flat
+    row, notes["x_rows"] = "row") back to hidden, on the same routing.
+    Draws: gate's case, then up's, down's, down's slot-major x, the router's."""
+    gate = make_gather_case(seed, n_seq=n_seq, padded_n=padded_n, top_k=top_k, n_route=n_route,
+                            k_in=hidden, n_out=inter, max_rank=rank, n_adapted=n_adapted,
+                            skip_seqs=skip_seqs, name="gate")
+    up = _with_routing_of(make_gather_case(
+        seed + 1, n_seq=n_seq, padded_n=padded_n, top_k=top_k, n_route=n_route, k_in=hidden,
+        n_out=inter, max_rank=rank, n_adapted=n_adapted, skip_seqs=skip_seqs, name="up"), gate)
+    down = _with_routing_of(make_gather_case(
+        seed + 2, n_seq=n_seq, padded_n=padded_n, top_k=top_k, n_route=n_route, k_in=inter,
+        n_out=hidden, max_rank=rank, n_adapted=n_adapted, skip_seqs=skip_seqs, name="down"),
+        gate)
+    rng = np.random.default_rng([seed, 3])
+    down.x = _values(rng, (down.n_rows, inter), 1.0, "bf16")
+    down.n_tokens = down.n_rows
+    down.notes["x_rows"] = "row"
+    router = make_gather_case(seed + 4, n_seq=n_seq, padded_n=padded_n, top_k=1, n_route=1,
+                              k_in=hidden, n_out=n_route, max_rank=rank, adapted=np.array([0]),
+                              index_mode="zero", name="router")
+    # the router's token rows skip as the batch's sequences do (Skip, padding)
+    router.adapter_slots = gate.adapter_slots.copy()
+    return router, gate, up, down
+
+
 WORKLOADS = {
     "tiny_gather_f32": tiny_gather_f32,
     "decode_down_gather": decode_down_gather,
