@@ -35,6 +35,12 @@ from .host import (  # noqa: F401
     gather_row_token,
     MAX_EXPERT_ID,
 )
+from .multi import (  # noqa: F401
+    resolve_moe_lora_route_multi,
+    build_moe_row_adapter_decode_multi,
+    pack_expert_tables_multi,
+    fold_gather_multi,
+)
 from .fold import (  # noqa: F401
     bf16_to_f64,
     fold_gather_scalar,
