@@ -56,7 +56,7 @@ DEFAULT_WORKLOAD = "decode_down_gather"
 # the workloads a default run measures: the decode line and, beside it, every
 # other full-size workload (the tiny fp32 one is a parity case only)
 MEASURED = ["decode_down_gather", "prefill_grouped_down", "gateup_gather", "router_gather",
-            "mixed_grouped", "decode_layer"]
+            "mixed_grouped", "decode_layer", "decode_multi_gather"]
 KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_lora_amd", "csrc", "mlora_fold.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -72,6 +72,9 @@ WORKLOAD_TEXT = {
              "rank 16, bf16",
     "mixed_grouped": "mixed prefill grouped fold: 16384 sorted rows, 256 experts (77 unadapted, "
              "duplicate ids), k_in 1536, n_out 4096, rank 16, bf16, windows of 8192",
+    "decode_multi_gather": "decode down-proj gather (64 seqs x top-8, 640 rows, 128 experts, "
+             "k_in 768, n_out 2048, rank 16) with 4 installed adapters, each adapting 96 "
+             "experts; 6 Skip and 5 not-installed sequences; bf16",
     "decode_layer": "Qwen3-MoE-like decode layer, 64 seqs x top-8 (640 rows, 80 tokens), 128 "
              "experts (96 adapted): router one-entry route (k_in 2048, n_out 128), gate and up "
              "(k_in 2048, n_out 768, fused output) in one set, down on slot-major x (k_in 768, "
@@ -890,6 +893,94 @@ def measure_layer(args, cpu_seconds):
     }
 
 
+def measure_multi(args, cpu_seconds):
+    """The multi-adapter gather fold on the decode batch with four installed
+    adapters (workloads.decode_multi_gather), timed as the other workloads
+    are (graph replays over rotating copies of every input)."""
+    import torch
+    import moe_expert_lora_amd as ml
+    import workloads
+    from staging import DeviceMultiCase
+
+    case = workloads.decode_multi_gather()
+    copies = args.copies or max(2, min(64, math.ceil(640e6 / copy_bytes(case))))
+    devs = [DeviceMultiCase(case) for _ in range(copies)]
+    bases = [d.base0.clone() for d in devs]
+    torch.cuda.synchronize()
+
+    def step(k):
+        d = devs[k]
+        ml.mlora_gather_bgmv_multi(d.route, d.x, bases[k], d.indices, d.row_adapter,
+                                   case.top_k)
+
+    steps = args.steps
+    rot = Rotation(step, copies, steps)
+    rot.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    rot.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us = e0.elapsed_time(e1) * 1e3 / steps
+    # algorithmic bytes: cells and tokens of the folded rows, as for one adapter
+    at, bt, st, na, ne = devs[0].tables_host
+    ra = devs[0].row_adapter_host
+    rows = np.arange(case.n_rows)
+    tok = rows // case.top_k
+    slot = ra[tok].astype(np.int64)
+    e = case.indices.astype(np.int64)
+    ok = (slot >= 0) & (slot < na) & (e >= 0) & (e < ne)
+    cell = np.where(ok, slot * ne + e, 0)
+    live = ok & (at[cell] != 0) & (bt[cell] != 0)
+    K, N, R = case.k_in, case.n_out, case.max_rank
+    nbytes = int(np.unique(tok[live]).size * K * 2 + np.unique(cell[live]).size *
+                 (R * K + N * R) * 2 + live.sum() * N * 4 + 4 * case.n_rows + 4 * len(ra) +
+                 20 * na * ne)
+    del rot, devs, bases
+    torch.cuda.empty_cache()
+    cpu = None
+    if cpu_seconds > 0:
+        from oracle.case import OracleMultiView, to_f64
+        from threadpoolctl import threadpool_limits
+        import oracle
+        v = OracleMultiView(case)
+        b64 = to_f64(case.base, case.dtype)
+        threads = cpu_threads()
+        with threadpool_limits(limits=threads):
+            v.fold(case.base)
+            t1 = time.perf_counter()
+            it = 0
+            while True:
+                oracle.fold_gather_multi(v.x, v.a_table, v.b_table, v.scale_table,
+                                         v.n_adapters, v.n_experts, v.mats, b64, case.indices,
+                                         v.row_adapter, case.top_k)
+                it += 1
+                el = time.perf_counter() - t1
+                if (el >= cpu_seconds and it >= 3) or el >= 3 * cpu_seconds:
+                    break
+        cpu = {"value": case.n_rows * it / el, "unit": "rows/s", "cores": threads,
+               "kind": "oracle", "sample": f"the full call, {it}x in {el:.1f} s (fp64, one "
+                                           "row at a time)",
+               "gbs": nbytes * it / el / 1e9, "affinity_cpus": len(os.sched_getaffinity(0)),
+               "cpu_model": cpu_model()}
+    achieved = nbytes / (step_us * 1e-6) / 1e9
+    return {"value": case.n_rows * steps / wall, "unit": "rows/s",
+            "ms_per_step": wall / steps * 1e3, "steps": steps, "dtype": "bf16",
+            "config": {"workload": f"decode_multi_gather: {WORKLOAD_TEXT['decode_multi_gather']}",
+                       "path": "gather (multi-adapter)", "rows_per_step": case.n_rows,
+                       "folded_rows_per_step": int(live.sum()), "kernel_dispatches_per_step": 1,
+                       "rotating_copies": copies},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "unit_of_work": "one mlora_gather_bgmv_multi call",
+                         "algorithmic_bytes": nbytes, "step_us_mean": step_us},
+            "cpu_baseline": cpu}
+
+
 def resolve_workloads(workload, also):
     """(main workload, workloads reported under 'also') from the command line:
     no --workload means the decode default with every other measured workload
@@ -975,9 +1066,9 @@ def main():
     if args.counters:
         args.no_cpu = True
     main_cpu = 0.0 if args.no_cpu else args.cpu_seconds
-    if args.workload == "decode_layer":
-        print("bench.py: decode_layer is reported under 'also' of another workload "
-              "(e.g. --workload decode_down_gather --also decode_layer)", file=sys.stderr)
+    if args.workload in ("decode_layer", "decode_multi_gather"):
+        print(f"bench.py: {args.workload} is reported under 'also' of another workload "
+              f"(e.g. --workload decode_down_gather --also {args.workload})", file=sys.stderr)
         sys.exit(2)
     out = measure(args.workload, args, main_cpu)
     if not args.counters:
@@ -987,9 +1078,9 @@ def main():
     if args.also:
         out["also"] = {}
         for w in args.also:
-            if w == "decode_layer":
-                out["also"][w] = measure_layer(args, 0.0 if args.no_cpu else
-                                               0.6 * args.cpu_seconds)
+            if w in ("decode_layer", "decode_multi_gather"):
+                fn = measure_layer if w == "decode_layer" else measure_multi
+                out["also"][w] = fn(args, 0.0 if args.no_cpu else 0.6 * args.cpu_seconds)
                 continue
             r = measure(w, args, 0.0 if args.no_cpu else 0.6 * args.cpu_seconds)
             out["also"][w] = {k: r[k] for k in ("value", "unit", "ms_per_step", "steps",

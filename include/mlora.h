@@ -245,6 +245,74 @@ typedef struct mlora_projection {
  */
 int32_t mlora_gather_bgmv_set(const mlora_projection* projs, int32_t n_proj, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Several adapters at once (past the pages' single-active phase).           */
+/* ------------------------------------------------------------------------ */
+/*
+ * A reading of [P1 resolve_moe_lora_route, ensure_decode_route_servable],
+ * whose phase-1 design installs one adapter and refuses a decode batch that
+ * asks for another, extended to several installed adapters: every adapter
+ * slot s in [0, n_adapters) has its own expert tables [P2 ExpertTables], and
+ * a row folds with the tables of its own token's slot.
+ */
+
+/* Route of one request: MLORA_ROUTE_SKIP for a negative slot, MLORA_ROUTE_FOLD
+ * for a slot below n_adapters (its tables are installed), MLORA_ROUTE_REFUSE
+ * otherwise (pass it to mlora_ensure_decode_route_servable to refuse). */
+int32_t mlora_resolve_moe_lora_route_multi(int32_t adapter_slot, int32_t n_adapters);
+
+/* Decode map: out[i] (i < padded_n) is sequence i's own slot when its route
+ * is Fold, else -1 (Skip, Refuse, padding). MLORA_ERR_INVALID for a negative
+ * size or a NULL pointer that is needed. */
+int32_t mlora_build_moe_row_adapter_decode_multi(const int32_t* adapter_slots, int64_t n_slots,
+                                                 int64_t padded_n, int32_t n_adapters,
+                                                 int32_t* out);
+
+/* [P2 pack_expert_tables] per slot: entries (adapter_slots[i], expert_ids[i],
+ * a_addrs[i], b_addrs[i], scales[i]) into host tables of n_adapters x
+ * n_experts cells, cell (s, e) at s * n_experts + e; n_adapters = max slot +
+ * 1, n_experts = max id + 1; unnamed cells 0 / 0.0; the last entry wins for a
+ * repeated (slot, id). Slots must lie in [0, 2^16), ids in [0, 2^24).
+ * MLORA_NONE for no entries; MLORA_ERR_CAPACITY (only the two counts
+ * written) when table_cap < n_adapters * n_experts (tables may then be
+ * NULL); MLORA_ERR_INVALID for a bad slot or id. */
+int32_t mlora_pack_expert_tables_multi(const int32_t* adapter_slots, const int32_t* expert_ids,
+                                       const uint64_t* a_addrs, const uint64_t* b_addrs,
+                                       const float* scales, int64_t n_entries,
+                                       uint64_t* a_table, uint64_t* b_table, float* scale_table,
+                                       int64_t table_cap, int32_t* n_adapters,
+                                       int32_t* n_experts);
+
+/* Device tables of several adapters' expert pairs: n_adapters * n_experts
+ * cells, cell (s, e) at s * n_experts + e (as packed above); other fields as
+ * in mlora_expert_route. */
+typedef struct mlora_multi_route {
+  const uint64_t* a_table;
+  const uint64_t* b_table;
+  const float* scale_table;
+  int32_t n_adapters;
+  int32_t n_experts;
+  int32_t k_in;
+  int32_t n_out;
+  int32_t max_rank;
+  int32_t dtype;     /* MLORA_BF16 only */
+} mlora_multi_route;
+
+/*
+ * [P2 moe_lora_gather_bgmv] with several adapters: flat row r (token
+ * t = r / top_k) folds with cell (row_adapter[t], indices[r]), and is skipped
+ * when row_adapter[t] < 0 or >= n_adapters, when indices[r] is negative or
+ * >= n_experts, or when the cell's a or b address is 0. Arithmetic, layouts
+ * and the other rules as mlora_gather_bgmv without a workspace (one kernel;
+ * with n_adapters == 1 and a map of 0 / -1, the same bits as
+ * mlora_gather_bgmv on that slot's tables). Returns MLORA_OK,
+ * MLORA_ERR_INVALID (nothing enqueued) or MLORA_ERR_HIP.
+ */
+int32_t mlora_gather_bgmv_multi(const mlora_multi_route* route, const void* x, int64_t n_tokens,
+                                void* base_out, const int32_t* indices,
+                                const int32_t* row_adapter, int64_t n_slots, int32_t top_k,
+                                void* stream);
+
 /* Bytes of workspace mlora_gather_bgmv may use: KC * n_slots * 64 * NB, KC =
  * clamp(ceil(ceil(k_in / 32) / 16), 1, 4) k ranges, NB = ceil(max_rank / 16)
  * rounded up to 1, 2, 4 or 8, rounded up to 256. 0 for n_slots <= 0 or invalid

@@ -53,6 +53,10 @@ EXPORTS = (
     "mlora_grouped_down_all_noalloc",
     "mlora_apply_expert_lora_sorted",
     "mlora_gather_bgmv_set",
+    "mlora_resolve_moe_lora_route_multi",
+    "mlora_build_moe_row_adapter_decode_multi",
+    "mlora_pack_expert_tables_multi",
+    "mlora_gather_bgmv_multi",
 )
 
 
@@ -71,6 +75,22 @@ class ExpertRoute(ctypes.Structure):
         ("a_table", ctypes.c_void_p),
         ("b_table", ctypes.c_void_p),
         ("scale_table", ctypes.c_void_p),
+        ("n_experts", ctypes.c_int32),
+        ("k_in", ctypes.c_int32),
+        ("n_out", ctypes.c_int32),
+        ("max_rank", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class MultiRoute(ctypes.Structure):
+    """``mlora_multi_route``: device tables of n_adapters x n_experts cells."""
+
+    _fields_ = [
+        ("a_table", ctypes.c_void_p),
+        ("b_table", ctypes.c_void_p),
+        ("scale_table", ctypes.c_void_p),
+        ("n_adapters", ctypes.c_int32),
         ("n_experts", ctypes.c_int32),
         ("k_in", ctypes.c_int32),
         ("n_out", ctypes.c_int32),
@@ -147,6 +167,12 @@ def load() -> ctypes.CDLL:
         "mlora_grouped_down_all_noalloc": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64,
                                                  vp, i32, vp, vp, i32, i64, vp]),
         "mlora_gather_bgmv_set": (i32, [ctypes.POINTER(Projection), i32, vp]),
+        "mlora_resolve_moe_lora_route_multi": (i32, [i32, i32]),
+        "mlora_build_moe_row_adapter_decode_multi": (i32, [_i32p, i64, i64, i32, _i32p]),
+        "mlora_pack_expert_tables_multi": (i32, [_i32p, _i32p, _u64p, _u64p, _f32p, i64, _u64p,
+                                                 _u64p, _f32p, i64, _i32p, _i32p]),
+        "mlora_gather_bgmv_multi": (i32, [ctypes.POINTER(MultiRoute), vp, i64, vp, vp, vp, i64,
+                                          i32, vp]),
         "mlora_apply_expert_lora_sorted": (i32, [ctypes.POINTER(ExpertRoute), vp, i64, vp, i64,
                                                  vp, _i32p, i32, _u64p, _u64p, vp, vp, i32, vp,
                                                  ctypes.c_uint64, vp]),
@@ -557,6 +583,94 @@ def mlora_gather_bgmv_set(projections, stream=None) -> None:
     """Gather folds of 1 to 4 projections (make_projection) in one launch."""
     arr = (Projection * len(projections))(*projections)
     rc = load().mlora_gather_bgmv_set(arr, len(projections), _stream_handle(stream))
+    if rc != MLORA_OK:
+        raise _err(rc)
+
+
+def mlora_resolve_moe_lora_route_multi(adapter_slot: int, n_adapters: int) -> int:
+    return int(load().mlora_resolve_moe_lora_route_multi(int(adapter_slot), int(n_adapters)))
+
+
+def mlora_build_moe_row_adapter_decode_multi(adapter_slots, padded_n: int,
+                                             n_adapters: int) -> np.ndarray:
+    sl = _arr(adapter_slots, np.int32)
+    out = np.zeros(int(padded_n), dtype=np.int32)
+    rc = load().mlora_build_moe_row_adapter_decode_multi(_ptr(sl, ctypes.c_int32), sl.shape[0],
+                                                         int(padded_n), int(n_adapters),
+                                                         _ptr(out, ctypes.c_int32))
+    if rc != MLORA_OK:
+        raise _err(rc)
+    return out
+
+
+def mlora_pack_expert_tables_multi(adapter_slots, expert_ids, a_addrs, b_addrs, scales):
+    """None for no entries, else (a_table, b_table, scale_table, n_adapters,
+    n_experts) with flat tables of n_adapters * n_experts cells."""
+    sl = _arr(adapter_slots, np.int32)
+    ids = _arr(expert_ids, np.int32)
+    a = _arr(a_addrs, np.uint64)
+    b = _arr(b_addrs, np.uint64)
+    s = _arr(scales, np.float32)
+    n = ids.shape[0]
+    if not (sl.shape[0] == a.shape[0] == b.shape[0] == s.shape[0] == n):
+        raise ValueError("entry arrays differ in length")
+    lib = load()
+    na, ne = ctypes.c_int32(0), ctypes.c_int32(0)
+    args = (_ptr(sl, ctypes.c_int32), _ptr(ids, ctypes.c_int32), _ptr(a, ctypes.c_uint64),
+            _ptr(b, ctypes.c_uint64), _ptr(s, ctypes.c_float), n)
+    rc = lib.mlora_pack_expert_tables_multi(*args, None, None, None, 0, ctypes.byref(na),
+                                            ctypes.byref(ne))
+    if rc == MLORA_NONE:
+        return None
+    if rc != MLORA_ERR_CAPACITY:
+        raise _err(rc)
+    cells = na.value * ne.value
+    at = np.zeros(cells, dtype=np.uint64)
+    bt = np.zeros(cells, dtype=np.uint64)
+    st = np.zeros(cells, dtype=np.float32)
+    rc = lib.mlora_pack_expert_tables_multi(*args, _ptr(at, ctypes.c_uint64),
+                                            _ptr(bt, ctypes.c_uint64), _ptr(st, ctypes.c_float),
+                                            cells, ctypes.byref(na), ctypes.byref(ne))
+    if rc != MLORA_OK:
+        raise _err(rc)
+    return at, bt, st, int(na.value), int(ne.value)
+
+
+def make_multi_route(a_table, b_table, scale_table, n_adapters: int, n_experts: int, k_in: int,
+                     n_out: int, max_rank: int) -> MultiRoute:
+    """Multi-adapter route over device tables of n_adapters * n_experts cells
+    (bf16 weights). The caller keeps the tensors alive."""
+    import torch
+    for t in (a_table, b_table, scale_table):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("route tables must be contiguous device tensors")
+    if scale_table.dtype != torch.float32:
+        raise TypeError("scale_table must be float32")
+    return MultiRoute(a_table.data_ptr(), b_table.data_ptr(), scale_table.data_ptr(),
+                      int(n_adapters), int(n_experts), int(k_in), int(n_out), int(max_rank),
+                      MLORA_BF16)
+
+
+def mlora_gather_bgmv_multi(route: MultiRoute, x, base_out, indices, row_adapter, top_k: int,
+                            stream=None) -> None:
+    """Multi-adapter gather fold of every flat row of ``base_out``, in place:
+    row r folds with the cell (row_adapter[r // top_k], indices[r])."""
+    import torch
+    if x.dtype != torch.bfloat16 or base_out.dtype != torch.bfloat16:
+        raise TypeError("the multi-adapter fold is bf16")
+    if x.dim() != 2 or base_out.dim() != 2:
+        raise ValueError("x and base_out must be 2-D")
+    if x.shape[1] != route.k_in or base_out.shape[1] != route.n_out:
+        raise ValueError("x / base_out widths differ from the route's k_in / n_out")
+    n_slots = base_out.shape[0]
+    if indices.numel() != n_slots:
+        raise ValueError("indices must have one entry per base_out row")
+    if row_adapter.numel() < x.shape[0]:
+        raise ValueError("row_adapter must cover every x row")
+    rc = load().mlora_gather_bgmv_multi(
+        ctypes.byref(route), _dev(x, "x"), x.shape[0], _dev(base_out, "base_out"),
+        _dev(indices, "indices", torch.int32), _dev(row_adapter, "row_adapter", torch.int32),
+        n_slots, int(top_k), _stream_handle(stream))
     if rc != MLORA_OK:
         raise _err(rc)
 

@@ -625,7 +625,7 @@ struct GatherArgs {
 // The one-kernel gather fold of work unit u (an expert's row slice and column
 // slice) of the call `p`; all threads of the workgroup call it with the same
 // unit.
-template <int NB, int MB, bool FULL_R>
+template <int NB, int MB, bool FULL_R, bool MULTI = false>
 __device__ __forceinline__ void gather_fold_unit(const uint64_t* __restrict__ a_table,
                                                  const uint64_t* __restrict__ b_table,
                                                  const float* __restrict__ scale_table, int u,
@@ -635,12 +635,16 @@ __device__ __forceinline__ void gather_fold_unit(const uint64_t* __restrict__ a_
   __shared__ int s_toks[kScanMax];
   __shared__ int s_cnt;
 
-  const int e = u / per_e;
-  const int within = u - e * per_e;
+  // table cell of the unit: the expert, or with MULTI (tables of
+  // n_adapters x n_experts cells) adapter slot * n_experts + expert
+  const int cell = u / per_e;
+  const int within = u - cell * per_e;
+  const int ad = MULTI ? cell / p.n_experts : 0;  // adapter slot
+  const int e = cell - ad * p.n_experts;
   const int rs = within / inner, ns = within - rs * inner;
 
-  const uint64_t a_addr = uniform_u64(a_table[e]), b_addr = uniform_u64(b_table[e]);
-  const float scale = uniform_f32(scale_table[e]);
+  const uint64_t a_addr = uniform_u64(a_table[cell]), b_addr = uniform_u64(b_table[cell]);
+  const float scale = uniform_f32(scale_table[cell]);
 
   // This slice's routing, requested together with the table cells.
   const rsrc_t r_idx = make_buf(p.indices, (uint32_t)p.n_slots * 4u);
@@ -678,7 +682,7 @@ __device__ __forceinline__ void gather_fold_unit(const uint64_t* __restrict__ a_
   for (int i = 0; i < kPer; ++i) {
     if (i >= rounds) break;
     const int row = start + i * kThreads + (int)threadIdx.x;
-    const bool hit = row < end && iv[i] == e && mv[i] >= 0;
+    const bool hit = row < end && iv[i] == e && (MULTI ? mv[i] == ad : mv[i] >= 0);
     const int tok = (int)udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
     wave_append(hit, row, p.x_by_row ? row : tok, &s_cnt, s_rows, s_toks, kScanMax);
   }
@@ -695,7 +699,7 @@ __device__ __forceinline__ void gather_fold_unit(const uint64_t* __restrict__ a_
                               min(16 * MB, n - c), n_lo, n_hi, s_part);
 }
 
-template <int NB, int MB, bool FULL_R>
+template <int NB, int MB, bool FULL_R, bool MULTI = false>
 __global__ __launch_bounds__(kThreads) void gather_fold_kernel(
     const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
     const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
@@ -704,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int u = xcd * per_xcd + slot;
   if (u >= units) return;
-  gather_fold_unit<NB, MB, FULL_R>(a_table, b_table, scale_table, u, per_e, inner, p);
+  gather_fold_unit<NB, MB, FULL_R, MULTI>(a_table, b_table, scale_table, u, per_e, inner, p);
 }
 
 
@@ -2502,6 +2506,80 @@ extern "C" int32_t mlora_gather_bgmv_set(const mlora_projection* projs, int32_t 
     dispatch_set<true>(gs, grid, s, nb, small);
   else
     dispatch_set<false>(gs, grid, s, nb, small);
+  return launched(who);
+}
+
+namespace mlora {
+namespace {
+
+template <int NB, int MB>
+void launch_gather_multi(const GatherArgs& a, int grid, hipStream_t s) {
+  if (a.R == 16 * NB)
+    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, true, true>), dim3(grid), dim3(kThreads), 0,
+                       s, LEAD_ARGS(a, a.ns_count));
+  else
+    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, false, true>), dim3(grid), dim3(kThreads), 0,
+                       s, LEAD_ARGS(a, a.ns_count));
+}
+
+// The streaming one-kernel gather with multi-adapter cells (the decode
+// resident kernel keeps one adapter).
+void dispatch_gather_multi(const GatherArgs& a, int grid, hipStream_t s, bool small) {
+  const int nb = kernel_nb(a.R);
+  if (nb <= 1) {
+    if (small) return launch_gather_multi<1, 1>(a, grid, s);
+    return launch_gather_multi<1, 4>(a, grid, s);
+  }
+  if (nb <= 2) {
+    if (small) return launch_gather_multi<2, 1>(a, grid, s);
+    return launch_gather_multi<2, 4>(a, grid, s);
+  }
+  if (nb <= 4) {
+    if (small) return launch_gather_multi<4, 1>(a, grid, s);
+    return launch_gather_multi<4, 2>(a, grid, s);
+  }
+  launch_gather_multi<8, 1>(a, grid, s);
+}
+
+}  // namespace
+}  // namespace mlora
+
+extern "C" int32_t mlora_gather_bgmv_multi(const mlora_multi_route* route, const void* x,
+                                           int64_t n_tokens, void* base_out,
+                                           const int32_t* indices, const int32_t* row_adapter,
+                                           int64_t n_slots, int32_t top_k, void* stream) {
+  const char* who = "mlora_gather_bgmv_multi";
+  if (!route) return fail(MLORA_ERR_INVALID, "%s: NULL route", who);
+  if (route->n_adapters < 0 || route->n_experts < 0)
+    return fail(MLORA_ERR_INVALID, "%s: negative table size", who);
+  const int64_t cells = (int64_t)route->n_adapters * route->n_experts;
+  if (cells > 0x7fffffffll) return fail(MLORA_ERR_INVALID, "%s: too many table cells", who);
+  if (route->dtype != MLORA_BF16) return fail(MLORA_ERR_INVALID, "%s: bf16 only", who);
+  // the cell tables as one route over n_adapters * n_experts "experts"
+  mlora_expert_route flat{route->a_table, route->b_table, route->scale_table, (int32_t)cells,
+                          route->k_in, route->n_out, route->max_rank, route->dtype};
+  if (int32_t rc = check_route(&flat, who)) return rc;
+  if (top_k <= 0) return fail(MLORA_ERR_INVALID, "%s: top_k=%d must be positive", who, top_k);
+  if (n_slots < 0 || n_slots > (int64_t)0x7fffffff - kScanMax)
+    return fail(MLORA_ERR_INVALID, "%s: n_slots=%lld out of range", who, (long long)n_slots);
+  const int64_t need_tok = (n_slots + top_k - 1) / top_k;
+  if (n_tokens < need_tok || n_tokens > 0x3fffffffll)
+    return fail(MLORA_ERR_INVALID, "%s: n_tokens=%lld (need >= ceil(n_slots/top_k)=%lld)", who,
+                (long long)n_tokens, (long long)need_tok);
+  if (n_slots == 0 || cells == 0) {
+    clear_error();
+    return MLORA_OK;
+  }
+  if (!x || !base_out || !indices || !row_adapter)
+    return fail(MLORA_ERR_INVALID, "%s: NULL device pointer", who);
+  GatherPlan plan;
+  if (int32_t rc = plan_gather(who, &flat, x, n_tokens, route->k_in, 0, base_out, route->n_out,
+                               indices, row_adapter, n_tokens, n_slots, top_k, &plan))
+    return rc;
+  plan.a.n_experts = route->n_experts;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  dispatch_gather_multi(plan.a, plan.grid, s, plan.small != 0);
   return launched(who);
 }
 

@@ -16,6 +16,7 @@ namespace mlora {
 namespace {
 thread_local char g_err[512] = "";
 constexpr int32_t kMaxExpertId = (1 << 24) - 1;
+constexpr int32_t kMaxAdapterSlot = (1 << 16) - 1;
 }  // namespace
 
 int32_t fail(int32_t code, const char* fmt, ...) {
@@ -100,6 +101,78 @@ int32_t mlora_pack_expert_tables(const int32_t* expert_ids, const uint64_t* a_ad
     scale_table[e] = scales[i];
   }
   *n_experts = (int32_t)n;
+  mlora::clear_error();
+  return MLORA_OK;
+}
+
+int32_t mlora_resolve_moe_lora_route_multi(int32_t adapter_slot, int32_t n_adapters) {
+  if (adapter_slot < 0) return MLORA_ROUTE_SKIP;
+  return adapter_slot < n_adapters ? MLORA_ROUTE_FOLD : MLORA_ROUTE_REFUSE;
+}
+
+int32_t mlora_build_moe_row_adapter_decode_multi(const int32_t* adapter_slots, int64_t n_slots,
+                                                 int64_t padded_n, int32_t n_adapters,
+                                                 int32_t* out) {
+  if (n_slots < 0 || padded_n < 0 || n_adapters < 0)
+    return fail(MLORA_ERR_INVALID, "build_moe_row_adapter_decode_multi: negative size");
+  if ((n_slots > 0 && padded_n > 0 && !adapter_slots) || (padded_n > 0 && !out))
+    return fail(MLORA_ERR_INVALID, "build_moe_row_adapter_decode_multi: NULL pointer");
+  for (int64_t i = 0; i < padded_n; ++i) {
+    const int32_t s = i < n_slots ? adapter_slots[i] : -1;
+    out[i] = mlora_resolve_moe_lora_route_multi(s, n_adapters) == MLORA_ROUTE_FOLD ? s : -1;
+  }
+  mlora::clear_error();
+  return MLORA_OK;
+}
+
+int32_t mlora_pack_expert_tables_multi(const int32_t* adapter_slots, const int32_t* expert_ids,
+                                       const uint64_t* a_addrs, const uint64_t* b_addrs,
+                                       const float* scales, int64_t n_entries,
+                                       uint64_t* a_table, uint64_t* b_table, float* scale_table,
+                                       int64_t table_cap, int32_t* n_adapters,
+                                       int32_t* n_experts) {
+  const char* who = "pack_expert_tables_multi";
+  if (n_entries < 0) return fail(MLORA_ERR_INVALID, "%s: n_entries < 0", who);
+  if (n_entries == 0) {
+    mlora::clear_error();
+    return MLORA_NONE;
+  }
+  if (!adapter_slots || !expert_ids || !a_addrs || !b_addrs || !scales || !n_adapters ||
+      !n_experts)
+    return fail(MLORA_ERR_INVALID, "%s: NULL input", who);
+  int32_t max_slot = -1, max_id = -1;
+  for (int64_t i = 0; i < n_entries; ++i) {
+    const int32_t sl = adapter_slots[i], e = expert_ids[i];
+    if (sl < 0 || sl > mlora::kMaxAdapterSlot || e < 0 || e > mlora::kMaxExpertId)
+      return fail(MLORA_ERR_INVALID, "%s: entry %lld has slot %d / expert id %d outside "
+                  "[0, 2^16) / [0, 2^24)", who, (long long)i, sl, e);
+    if (sl > max_slot) max_slot = sl;
+    if (e > max_id) max_id = e;
+  }
+  const int64_t na = (int64_t)max_slot + 1, ne = (int64_t)max_id + 1, cells = na * ne;
+  if (cells > 0x7fffffffll)
+    return fail(MLORA_ERR_INVALID, "%s: %lld x %lld cells", who, (long long)na, (long long)ne);
+  if (table_cap < cells) {
+    *n_adapters = (int32_t)na;
+    *n_experts = (int32_t)ne;
+    return fail(MLORA_ERR_CAPACITY, "%s: %lld cells needed, capacity %lld", who,
+                (long long)cells, (long long)table_cap);
+  }
+  if (!a_table || !b_table || !scale_table) return fail(MLORA_ERR_INVALID, "%s: NULL table", who);
+  for (int64_t c = 0; c < cells; ++c) {
+    a_table[c] = 0;
+    b_table[c] = 0;
+    scale_table[c] = 0.0f;
+  }
+  // Entries in input order: a later entry for the same (slot, id) overwrites.
+  for (int64_t i = 0; i < n_entries; ++i) {
+    const int64_t c = (int64_t)adapter_slots[i] * ne + expert_ids[i];
+    a_table[c] = a_addrs[i];
+    b_table[c] = b_addrs[i];
+    scale_table[c] = scales[i];
+  }
+  *n_adapters = (int32_t)na;
+  *n_experts = (int32_t)ne;
   mlora::clear_error();
   return MLORA_OK;
 }

@@ -116,3 +116,53 @@ class OracleView:
                     continue
                 live[r] = self.row_adapter[rid // c.top_k] >= 0
         return live
+
+
+class OracleMultiView:
+    """fp64 view of a multi-adapter FoldCase (workloads.make_multi_gather_case):
+    tables packed and the map built by the oracle's multi-adapter functions."""
+
+    def __init__(self, case: FoldCase):
+        from . import multi as _multi
+        self.case = case
+        self.x = to_f64(case.x, case.dtype)
+        self.entries = [(sl, e, oracle_addr("a", a), oracle_addr("b", b), s)
+                        for (sl, e, a, b, s) in case.notes["multi_entries"]]
+        (self.a_table, self.b_table, self.scale_table, self.n_adapters,
+         self.n_experts) = _multi.pack_expert_tables_multi(self.entries)
+        self.mats = {}
+        for (_, _, a, b, _) in case.notes["multi_entries"]:
+            self.mats[oracle_addr("a", a)] = to_f64(case.a_pool[a], case.dtype)
+            self.mats[oracle_addr("b", b)] = to_f64(case.b_pool[b], case.dtype)
+        self.row_adapter = np.asarray(_multi.build_moe_row_adapter_decode_multi(
+            case.adapter_slots, case.padded_n, case.notes["n_adapters"]), dtype=np.int32)
+
+    def fold(self, base=None) -> np.ndarray:
+        from . import multi as _multi
+        c = self.case
+        base64 = to_f64(c.base if base is None else base, c.dtype)
+        return _multi.fold_gather_multi(self.x, self.a_table, self.b_table, self.scale_table,
+                                        self.n_adapters, self.n_experts, self.mats, base64,
+                                        c.indices, self.row_adapter, c.top_k)
+
+    def magnitude(self) -> np.ndarray:
+        from . import multi as _multi
+        c = self.case
+        mats = {k: np.abs(m) for k, m in self.mats.items()}
+        return _multi.fold_gather_multi(np.abs(self.x), self.a_table, self.b_table,
+                                        [abs(float(v)) for v in self.scale_table],
+                                        self.n_adapters, self.n_experts, mats,
+                                        np.zeros(c.base.shape), c.indices, self.row_adapter,
+                                        c.top_k)
+
+    def live_rows(self) -> np.ndarray:
+        c = self.case
+        live = np.zeros(c.n_rows, dtype=bool)
+        for row in range(c.n_rows):
+            sl = int(self.row_adapter[row // c.top_k])
+            e = int(c.indices[row])
+            if 0 <= sl < self.n_adapters and 0 <= e < self.n_experts:
+                cell = sl * self.n_experts + e
+                live[row] = self.a_table[cell] != 0 and self.b_table[cell] != 0
+        return live
+

@@ -147,3 +147,46 @@ class DeviceCase:
         self.fold(base, windows=windows, two_kernel=two_kernel, pipelined=pipelined)
         torch.cuda.synchronize()
         return from_torch(base)
+
+
+class DeviceMultiCase:
+    """A multi-adapter gather case (workloads.make_multi_gather_case) on the
+    GPU: the weights in pools, the tables packed and the decode map built by
+    the library's multi-adapter host functions."""
+
+    def __init__(self, case: FoldCase, device="cuda"):
+        self.case = case
+        self.device = device
+        c = case
+        self.x = to_torch(c.x, c.dtype, device)
+        self.a_pool = to_torch(c.a_pool, c.dtype, device)
+        self.b_pool = to_torch(c.b_pool, c.dtype, device)
+        self.base0 = to_torch(c.base, c.dtype, device)
+        a_stride = c.max_rank * c.k_in * 2
+        b_stride = c.n_out * c.max_rank * 2
+        ent = c.notes["multi_entries"]
+        slots = np.array([e[0] for e in ent], dtype=np.int32)
+        ids = np.array([e[1] for e in ent], dtype=np.int32)
+        a_addrs = np.array([self.a_pool.data_ptr() + e[2] * a_stride for e in ent], np.uint64)
+        b_addrs = np.array([self.b_pool.data_ptr() + e[3] * b_stride for e in ent], np.uint64)
+        scales = np.array([e[4] for e in ent], dtype=np.float32)
+        at, bt, st, na, ne = ml.mlora_pack_expert_tables_multi(slots, ids, a_addrs, b_addrs,
+                                                               scales)
+        self.tables_host = (at, bt, st, na, ne)
+        self.a_table = u64_to_device(np.concatenate([at, [0]]), device)
+        self.b_table = u64_to_device(np.concatenate([bt, [0]]), device)
+        self.scale_table = torch.from_numpy(np.concatenate([st, [0]]).astype(np.float32)).to(device)
+        self.route = ml.make_multi_route(self.a_table, self.b_table, self.scale_table, na, ne,
+                                         c.k_in, c.n_out, c.max_rank)
+        self.row_adapter_host = ml.mlora_build_moe_row_adapter_decode_multi(
+            c.adapter_slots, c.padded_n, c.notes["n_adapters"])
+        self.row_adapter = torch.from_numpy(self.row_adapter_host).to(device)
+        self.indices = torch.from_numpy(np.ascontiguousarray(c.indices, np.int32)).to(device)
+
+    def run(self, base_host: np.ndarray = None) -> np.ndarray:
+        base = self.base0.clone() if base_host is None else to_torch(base_host, self.case.dtype,
+                                                                     self.device)
+        ml.mlora_gather_bgmv_multi(self.route, self.x, base, self.indices, self.row_adapter,
+                                   self.case.top_k)
+        torch.cuda.synchronize()
+        return from_torch(base)

@@ -28,7 +28,8 @@ def test_more_than_one_gpu_is_refused():
 
 @pytest.mark.parametrize("workload,also,want", [
     (None, None, ("decode_down_gather", ["prefill_grouped_down", "gateup_gather",
-                                          "router_gather", "mixed_grouped", "decode_layer"])),
+                                          "router_gather", "mixed_grouped", "decode_layer",
+                                          "decode_multi_gather"])),
     ("router_gather", None, ("router_gather", [])),
     ("prefill_grouped_down", None, ("prefill_grouped_down", [])),
     (None, "none", ("decode_down_gather", [])),

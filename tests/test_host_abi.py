@@ -498,3 +498,84 @@ def test_single_hip_runtime_in_process():
                          cwd=ROOT, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+# ---------------------------------------------------------------------------
+# multi-adapter host functions against the oracle
+# ---------------------------------------------------------------------------
+
+def test_multi_host_golden_through_the_library():
+    import json
+    import oracle
+    from tests.common import golden_lines
+    route_name = {ml.MLORA_ROUTE_FOLD: "Fold", ml.MLORA_ROUTE_SKIP: "Skip",
+                  ml.MLORA_ROUTE_REFUSE: "Refuse"}
+    for line in golden_lines("multi_host.txt"):
+        kind, rest = line.split(" ", 1)
+        if kind == "route":
+            slot, n, want = rest.split()
+            assert route_name[ml.mlora_resolve_moe_lora_route_multi(int(slot), int(n))] == want
+        elif kind == "decode":
+            c = json.loads(rest)
+            got = ml.mlora_build_moe_row_adapter_decode_multi(c["slots"], c["padded_n"],
+                                                              c["n_adapters"])
+            assert got.tolist() == c["expect"], line
+        else:
+            c = json.loads(rest)
+            ent = c["entries"]
+            got = ml.mlora_pack_expert_tables_multi([e[0] for e in ent], [e[1] for e in ent],
+                                                    [e[2] for e in ent], [e[3] for e in ent],
+                                                    [e[4] for e in ent])
+            if c["expect"] is None:
+                assert got is None
+                continue
+            at, bt, st, na, ne = got
+            e = c["expect"]
+            assert (at.tolist(), bt.tolist(), st.tolist(), na, ne) == \
+                (e["a"], e["b"], e["s"], e["n_adapters"], e["n_experts"]), line
+            assert oracle.pack_expert_tables_multi([tuple(x) for x in ent]) == \
+                (e["a"], e["b"], e["s"], e["n_adapters"], e["n_experts"])
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 5), st.integers(0, 30), st.integers(0, 2**64 - 1),
+                          st.integers(0, 2**64 - 1), st.floats(-4, 4, width=32)),
+                min_size=1, max_size=25),
+       st.lists(st.integers(-3, 7), max_size=12), st.integers(0, 14), st.integers(0, 6))
+def test_multi_host_fuzz(entries, slots, padded_n, n_adapters):
+    import oracle
+    got = ml.mlora_pack_expert_tables_multi([e[0] for e in entries], [e[1] for e in entries],
+                                            [e[2] for e in entries], [e[3] for e in entries],
+                                            [e[4] for e in entries])
+    want = oracle.pack_expert_tables_multi(entries)
+    at, bt, st_, na, ne = got
+    assert (at.tolist(), bt.tolist(), na, ne) == (want[0], want[1], want[3], want[4])
+    assert st_.tolist() == [float(np.float32(v)) for v in want[2]]
+    m = ml.mlora_build_moe_row_adapter_decode_multi(slots, padded_n, n_adapters)
+    assert m.tolist() == oracle.build_moe_row_adapter_decode_multi(slots, padded_n, n_adapters)
+    for s_ in slots:
+        r = ml.mlora_resolve_moe_lora_route_multi(s_, n_adapters)
+        assert {0: "Fold", 1: "Skip", 2: "Refuse"}[r] == \
+            oracle.resolve_moe_lora_route_multi(s_, n_adapters)
+
+
+def test_multi_fold_rejects_bad_calls(lib):
+    u64 = FAKE
+    r = ml.MultiRoute(u64, u64, u64, 2, 4, 64, 32, 16, ml.MLORA_BF16)
+
+    def call(route, n_tokens=4, n_slots=8, top_k=2, x=FAKE):
+        return lib.mlora_gather_bgmv_multi(ctypes.byref(route), x, n_tokens, FAKE, FAKE, FAKE,
+                                           n_slots, top_k, None)
+
+    assert call(r, top_k=0) == ml.MLORA_ERR_INVALID
+    assert call(r, n_tokens=3) == ml.MLORA_ERR_INVALID          # < ceil(8 / 2)
+    assert call(r, x=0) == ml.MLORA_ERR_INVALID
+    assert call(ml.MultiRoute(u64, u64, u64, 2, 4, 64, 32, 16, ml.MLORA_F32)) == \
+        ml.MLORA_ERR_INVALID                                    # bf16 only
+    assert call(ml.MultiRoute(u64, u64, u64, 2, 4, 60, 32, 16, ml.MLORA_BF16)) == \
+        ml.MLORA_ERR_INVALID                                    # k_in not a multiple of 8
+    assert call(ml.MultiRoute(u64, u64, u64, -1, 4, 64, 32, 16, ml.MLORA_BF16)) == \
+        ml.MLORA_ERR_INVALID
+    # no cells or no rows: nothing to do, no device access
+    assert call(ml.MultiRoute(u64, u64, u64, 0, 4, 64, 32, 16, ml.MLORA_BF16)) == ml.MLORA_OK
+    assert call(r, n_slots=0, n_tokens=0) == ml.MLORA_OK

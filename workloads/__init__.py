@@ -379,6 +379,54 @@ def mixed_grouped() -> FoldCase:
                              name="mixed_grouped")
 
 
+def make_multi_gather_case(seed: int, *, n_seq: int, padded_n: int, top_k: int, n_route: int,
+                           k_in: int, n_out: int, max_rank: int, n_adapters: int,
+                           adapted_frac: float = 0.75, skip_seqs: int = 0,
+                           uninstalled_seqs: int = 0, dup_frac: float = 0.0,
+                           scale=(0.5, 2.0), dtype: str = "bf16",
+                           name: str = "multi_gather") -> FoldCase:
+    """Decode-shaped gather problem over several installed adapters.
+
+    Each adapter slot adapts its own seeded subset (adapted_frac) of the
+    n_route experts with its own weights; the packing entries are
+    (slot, expert, a_handle, b_handle, scale) in notes["multi_entries"]
+    (a dup_frac share listed twice, a decoy first). Each sequence asks for a
+    slot drawn uniformly from the installed ones; skip_seqs ask for none (-1)
+    and uninstalled_seqs for the slot past the installed ones.
+    Draw order: routing, slots, adapted sets, scales, x, A, B, base."""
+    rng = np.random.default_rng(seed)
+    n_slots = padded_n * top_k
+    idx = topk_uniform(rng, padded_n, n_route, top_k).reshape(-1).astype(np.int32)
+    slots = rng.integers(0, n_adapters, size=n_seq).astype(np.int32)
+    pick = rng.permutation(n_seq)
+    slots[pick[:skip_seqs]] = -1
+    slots[pick[skip_seqs:skip_seqs + uninstalled_seqs]] = n_adapters
+    entries: List[Tuple[int, int, int, int, float]] = []
+    n_handles = 0
+    for s_ in range(n_adapters):
+        na = max(1, int(round(adapted_frac * n_route)))
+        adapted = np.sort(rng.choice(n_route, size=na, replace=False))
+        scales = rng.uniform(scale[0], scale[1], size=na).astype(np.float32)
+        dups = rng.random(na) < dup_frac
+        for j, e in enumerate(adapted.tolist()):
+            if dups[j]:
+                entries.append((s_, int(e), n_handles, n_handles,
+                                float(rng.uniform(scale[0], scale[1]))))
+                n_handles += 1
+            entries.append((s_, int(e), n_handles, n_handles, float(scales[j])))
+            n_handles += 1
+    x = _values(rng, (padded_n, k_in), 1.0, dtype)
+    a_pool, b_pool = _weights(rng, max(n_handles, 1), max_rank, k_in, n_out, dtype)
+    base = _values(rng, (n_slots, n_out), 1.0, dtype)
+    c = FoldCase(name=name, path="gather", dtype=dtype, seed=seed, top_k=top_k, k_in=k_in,
+                 n_out=n_out, max_rank=max_rank, n_tokens=padded_n, x=x, a_pool=a_pool,
+                 b_pool=b_pool, entries=[], base=base, map_kind="decode_multi",
+                 adapter_slots=slots, padded_n=padded_n, indices=idx)
+    c.notes["multi_entries"] = entries
+    c.notes["n_adapters"] = n_adapters
+    return c
+
+
 def _with_routing_of(case: FoldCase, like: FoldCase) -> FoldCase:
     """`case` with the routing (expert ids, adapter slots) of `like`."""
     case.indices = like.indices.copy()
@@ -417,6 +465,17 @@ def decode_layer_cases(seed: int = 60, n_seq: int = 64, padded_n: int = 80, top_
     # the router's token rows skip as the batch's sequences do (Skip, padding)
     router.adapter_slots = gate.adapter_slots.copy()
     return router, gate, up, down
+
+
+def decode_multi_gather() -> FoldCase:
+    """The decode down-proj gather batch (64 sequences x top-8 over 128
+    experts, padded to 80 tokens, k_in 768, n_out 2048, rank 16) with four
+    installed adapters, each adapting 75% of the experts with its own
+    weights; 6 sequences ask for no adapter and 5 for one not installed."""
+    return make_multi_gather_case(61, n_seq=64, padded_n=80, top_k=8, n_route=128, k_in=768,
+                                  n_out=2048, max_rank=16, n_adapters=4, adapted_frac=0.75,
+                                  skip_seqs=6, uninstalled_seqs=5, dup_frac=0.1,
+                                  name="decode_multi_gather")
 
 
 WORKLOADS = {
