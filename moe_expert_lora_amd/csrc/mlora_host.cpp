@@ -55,9 +55,9 @@ int32_t mlora_ensure_decode_route_servable(int32_t route) {
   }
   if (route == MLORA_ROUTE_REFUSE)
     return fail(MLORA_ERR_REFUSE,
-                "MoE LoRA decode: a sequence routes to a non-active adapter while only "
-                "the active adapter is installed; refusing instead of folding the wrong "
-                "adapter (one adapter per batch)");
+                "MoE LoRA decode refused: a request names an adapter whose expert tables are "
+                "not installed (only the active adapter's are); folding it would apply the "
+                "wrong weights, so it must be served in a batch of its own");
   return fail(MLORA_ERR_INVALID, "ensure_decode_route_servable: %d is not a route", route);
 }
 
@@ -190,12 +190,12 @@ int32_t mlora_build_moe_row_adapter_host(const int32_t* cu_seqlens, int64_t n_cu
                 (long long)n_slots, (long long)batch);
   if (cu_seqlens[0] != 0)
     return fail(MLORA_NONE, "build_moe_row_adapter_host: first boundary is not 0");
-  // Every boundary is checked before the map is sized from the last one.
+  // The boundaries must be a non-decreasing prefix sum; the map's length is
+  // the last one, so none is trusted before all are checked.
   for (int64_t b = 0; b < batch; ++b) {
-    const int32_t start = cu_seqlens[b], end = cu_seqlens[b + 1];
-    if (start < 0 || end < start)
-      return fail(MLORA_NONE, "build_moe_row_adapter_host: boundary %lld is negative or "
-                  "decreasing", (long long)b);
+    if (cu_seqlens[b + 1] < cu_seqlens[b])
+      return fail(MLORA_NONE, "build_moe_row_adapter_host: boundary %lld decreases",
+                  (long long)(b + 1));
   }
   const int64_t n = cu_seqlens[batch];
   if (out_cap < n) {

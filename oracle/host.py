@@ -13,6 +13,8 @@ from __future__ import annotations
 
 from typing import List, Optional, Sequence, Tuple
 
+import numpy as np
+
 FOLD = "Fold"
 SKIP = "Skip"
 REFUSE = "Refuse"
@@ -45,8 +47,8 @@ def ensure_decode_route_servable(route: str, path: str = "decode") -> None:
     ``ensure_decode_route_servable``): a batch mixing adapters cannot be served
     by the single-active fold and must be rejected before it runs."""
     if route == REFUSE:
-        raise RefuseError(f"MoE LoRA {path}: request routes to a non-active adapter; "
-                          "one adapter per batch")
+        raise RefuseError(f"MoE LoRA {path} refused: a request names an adapter whose "
+                          "tables are not installed; serve it in a batch of its own")
 
 
 def build_moe_row_adapter_host(cu_seqlens: Sequence[int],
@@ -54,31 +56,21 @@ def build_moe_row_adapter_host(cu_seqlens: Sequence[int],
     """Per-token adapter map of a packed prefill batch ("moe_row_adapter.rs",
     ``build_moe_row_adapter_host``).
 
-    ``cu_seqlens`` is the prefix sum of stream lengths (``batch + 1`` entries).
-    Stream ``b``'s slot is copied as is onto tokens ``cu[b] .. cu[b+1]``.
-    Returns None, writing nothing, when ``cu`` has fewer than two entries, the
-    slot count differs from ``batch``, ``cu[0]`` is not 0, or any boundary is
-    negative or smaller than the one before it. All boundaries are checked
-    before the map is sized, so a malformed list such as ``[0, 4, 2]`` cannot
-    size the map from its last entry.
+    ``cu_seqlens`` are the stream boundaries, a prefix sum starting at 0
+    (``batch + 1`` entries), and stream ``b`` owns tokens ``cu[b] .. cu[b+1]``;
+    its slot is copied as is onto them. The input is valid when there are at
+    least two boundaries, one slot per stream, the first boundary is 0 and no
+    boundary is below the one before it (so none is negative); otherwise the
+    result is None and nothing is built (so ``[0, 4, 2]`` is rejected rather
+    than sized from its last entry).
     """
-    cu = [int(v) for v in cu_seqlens]
-    slots = [int(v) for v in adapter_slots]
-    if len(cu) < 2:
+    cu = np.asarray(cu_seqlens, dtype=np.int64).reshape(-1)
+    slots = np.asarray(adapter_slots, dtype=np.int64).reshape(-1)
+    valid = (cu.size >= 2 and slots.size == cu.size - 1 and cu[0] == 0
+             and bool(np.all(np.diff(cu) >= 0)))
+    if not valid:
         return None
-    batch = len(cu) - 1
-    if len(slots) != batch:
-        return None
-    if cu[0] != 0:
-        return None
-    for b in range(batch):
-        if cu[b] < 0 or cu[b + 1] < cu[b]:
-            return None
-    out = [-1] * cu[batch]
-    for b in range(batch):
-        for t in range(cu[b], cu[b + 1]):
-            out[t] = slots[b]
-    return out
+    return np.repeat(slots, np.diff(cu)).astype(int).tolist()
 
 
 def build_moe_row_adapter_decode(adapter_slots: Sequence[int], padded_n: int, active: int,

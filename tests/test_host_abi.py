@@ -69,7 +69,7 @@ def test_ensure_decode_route_servable():
     with pytest.raises(ml.MloraError) as ei:
         ml.mlora_ensure_decode_route_servable(ml.MLORA_ROUTE_REFUSE)
     assert ei.value.code == ml.MLORA_ERR_REFUSE
-    assert "one adapter per batch" in str(ei.value)
+    assert "batch of its own" in str(ei.value)
     with pytest.raises(ml.MloraError) as ei:
         ml.mlora_ensure_decode_route_servable(7)
     assert ei.value.code == ml.MLORA_ERR_INVALID

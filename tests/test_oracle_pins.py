@@ -38,7 +38,7 @@ def test_route_truth_table():
 def test_ensure_decode_route_servable():
     oracle.ensure_decode_route_servable(oracle.FOLD)
     oracle.ensure_decode_route_servable(oracle.SKIP)
-    with pytest.raises(oracle.RefuseError, match="one adapter per batch"):
+    with pytest.raises(oracle.RefuseError, match="batch of its own"):
         oracle.ensure_decode_route_servable(oracle.REFUSE)
 
 
