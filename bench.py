@@ -383,6 +383,21 @@ def _tables_and_map(case):
     return tables, full
 
 
+def recorded_traffic(workload):
+    """Counter-measured HBM bytes per step of `workload` from profiles/
+    traffic.json, or None when there is no record or the kernel source has
+    changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if rec and rec.get("kernel_sha256_16") == kernel_hash():
+        return rec.get("hbm_bytes_per_step")
+    return None
+
+
 def traffic_from(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     """Per-step HBM bytes of the fold from FETCH_SIZE / WRITE_SIZE runs (KiB per
     dispatch) of `bench.py --counters`, each scaled by what the counter reads
@@ -706,14 +721,7 @@ def measure(workload, args, cpu_seconds):
     torch.cuda.empty_cache()
 
     achieved = alg_bytes / (step_us * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            rec = json.load(open(TRAFFIC_FILE)).get(workload)
-            if rec and rec.get("kernel_sha256_16") == kernel_hash():
-                traffic = rec.get("hbm_bytes_per_step")
-        except Exception:
-            traffic = None
+    traffic = recorded_traffic(workload)
 
     cpu = cpu_baseline(case, cpu_seconds) if cpu_seconds > 0 else None
     unit = ("one mlora_gather_bgmv call" if case.path == "gather" else
@@ -829,9 +837,12 @@ def measure_layer(args, cpu_seconds):
             ml.mlora_gather_bgmv_set([P[n][k]])
 
     layer_us, layer_ms = timed(layer_step)
-    calls_us, _ = timed(calls_step)
-    alone = {n: timed(lambda k, n=n: ml.mlora_gather_bgmv_set([P[n][k]]))[0]
-             for n in ("router", "gate", "up", "down")}
+    if args.counters:
+        calls_us, alone = None, {}
+    else:
+        calls_us, _ = timed(calls_step)
+        alone = {n: timed(lambda k, n=n: ml.mlora_gather_bgmv_set([P[n][k]]))[0]
+                 for n in ("router", "gate", "up", "down")}
     nbytes = {}
     rows = 0
     for c in cases:
@@ -880,15 +891,16 @@ def measure_layer(args, cpu_seconds):
                    "timing": "HIP graphs of whole rotations over the copies plus the remainder, "
                              "replayed; HIP events on the replay stream"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic("decode_layer"),
                      "unit_of_work": "one decode layer: router fold, gate/up set, down fold",
                      "algorithmic_bytes": total, "algorithmic_bytes_per_fold": nbytes,
                      "step_us_mean": layer_us},
-        "per_call": {"four_calls_us": calls_us,
-                     "four_calls_frac": total / (calls_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                     "alone_us": alone,
-                     "alone_frac": {n: nbytes[n] / (alone[n] * 1e-6) / 1e9 / HBM_PEAK_GBS
-                                    for n in alone}},
+        "per_call": None if calls_us is None else {
+            "four_calls_us": calls_us,
+            "four_calls_frac": total / (calls_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "alone_us": alone,
+            "alone_frac": {n: nbytes[n] / (alone[n] * 1e-6) / 1e9 / HBM_PEAK_GBS
+                           for n in alone}},
         "cpu_baseline": cpu,
     }
 
@@ -975,7 +987,8 @@ def measure_multi(args, cpu_seconds):
                        "folded_rows_per_step": int(live.sum()), "kernel_dispatches_per_step": 1,
                        "rotating_copies": copies},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("decode_multi_gather"),
                          "unit_of_work": "one mlora_gather_bgmv_multi call",
                          "algorithmic_bytes": nbytes, "step_us_mean": step_us},
             "cpu_baseline": cpu}
@@ -1067,6 +1080,11 @@ def main():
         args.no_cpu = True
     main_cpu = 0.0 if args.no_cpu else args.cpu_seconds
     if args.workload in ("decode_layer", "decode_multi_gather"):
+        if args.counters:
+            # counter runs of these two: their own launches only
+            fn = measure_layer if args.workload == "decode_layer" else measure_multi
+            print(json.dumps({args.workload: fn(args, 0.0)}), flush=True)
+            return
         print(f"bench.py: {args.workload} is reported under 'also' of another workload "
               f"(e.g. --workload decode_down_gather --also {args.workload})", file=sys.stderr)
         sys.exit(2)
