@@ -319,6 +319,46 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes": CALIB_BYTES}), flush=True)
 
 
+PROBE_LIB = os.path.join(ROOT, "moe_expert_lora_amd", "libmlora_probe.so")
+
+
+def probes():
+    """The floors that bound one launch of the fold (libmlora_probe.so, built
+    with the fold library): an empty launch, eager and in a HIP graph; and
+    the read rate of 8192 rows of 4096 bytes (a k_in = 2048 bf16 operand) in
+    the folds' MFMA-operand pattern (16 rows x 64 bytes per wave
+    instruction) and row-contiguously (1 KB of one row per instruction), at
+    row strides of 4096 bytes (dense rows), 4160 and 8192."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"bench.py: {PROBE_LIB} is missing; build with "
+                         "python -m moe_expert_lora_amd.build")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.mlora_probe_empty.restype = ctypes.c_int32
+    lib.mlora_probe_empty.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_float),
+                                      ctypes.POINTER(ctypes.c_float)]
+    lib.mlora_probe_read.restype = ctypes.c_int32
+    lib.mlora_probe_read.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.POINTER(ctypes.c_float)]
+    eager, graph = ctypes.c_float(), ctypes.c_float()
+    rc = lib.mlora_probe_empty(1000, ctypes.byref(eager), ctypes.byref(graph))
+    if rc:
+        raise SystemExit(f"bench.py: mlora_probe_empty failed (HIP error {rc})")
+    out = {"empty_launch_us": {"eager": eager.value, "graph": graph.value}, "read": []}
+    useful = 8192 * 4096
+    for name, pattern in (("operand", 0), ("rows", 1)):
+        for stride in (4096, 4160, 8192):
+            us = ctypes.c_float()
+            rc = lib.mlora_probe_read(pattern, stride, 12, 240, ctypes.byref(us))
+            if rc:
+                raise SystemExit(f"bench.py: mlora_probe_read failed (HIP error {rc})")
+            out["read"].append({"pattern": name, "row_stride": stride, "us": us.value,
+                                "gbs": useful / (us.value * 1e-6) / 1e9})
+            print(json.dumps(out["read"][-1]), file=sys.stderr, flush=True)
+    out["read_bytes"] = useful
+    return out
+
+
 def copy_bandwidth(n_bytes=1 << 30, reps=10):
     """Read + write GB/s of a plain device copy of n_bytes (torch's copy kernel),
     timed with HIP events on the current stream: a practical HBM figure beside
@@ -1037,6 +1077,8 @@ def main():
                     help="only time the plain-copy floor of the workload's algorithmic bytes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain copy used to scale HBM counters")
+    ap.add_argument("--probes", action="store_true",
+                    help="only run the launch and read-pattern probes (libmlora_probe.so)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="rocprofv3 --pmc output dirs -> profiles/traffic.json (no GPU)")
     args = ap.parse_args()
@@ -1063,6 +1105,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.probes:
+        print(json.dumps({"probes": probes()}), flush=True)
         return
     if args.floor_copy:
         import workloads

@@ -14,6 +14,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmlora.so")
 SOURCES = [os.path.join(CSRC, "mlora_host.cpp"), os.path.join(CSRC, "mlora_fold.hip")]
+# measurement probes for bench.py (launch and read-pattern floors), a library of their own
+PROBE_LIB = os.path.join(PKG, "libmlora_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "mlora_probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -32,10 +35,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into moe_expert_lora_amd/libmlora.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def _compile(sources, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,7 +47,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile moe_expert_lora_amd/libmlora.so (the fold) and libmlora_probe.so
+    (bench.py's measurement probes); returns the fold library's path."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 

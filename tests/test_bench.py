@@ -186,3 +186,22 @@ def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.kernel_hash() == h1
     src.write_text("int a;\nint c;\n")
     assert bench.kernel_hash() != h1
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """libmlora_probe.so (bench.py --probes) exports both probes, and each
+    rejects invalid arguments before any device call (so this runs on CPU)."""
+    import ctypes
+    lib = ctypes.CDLL(bench.PROBE_LIB)
+    lib.mlora_probe_empty.restype = ctypes.c_int32
+    lib.mlora_probe_empty.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mlora_probe_read.restype = ctypes.c_int32
+    lib.mlora_probe_read.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_void_p]
+    us = ctypes.c_float()
+    assert lib.mlora_probe_empty(0, ctypes.byref(us), ctypes.byref(us)) != 0
+    assert lib.mlora_probe_empty(10, None, None) != 0
+    for args in ((2, 4096, 12, 10), (0, 4095, 12, 10), (0, 8208, 12, 10), (0, 4100, 12, 10),
+                 (1, 4096, 0, 10), (1, 4096, 33, 10), (1, 4096, 12, 0)):
+        assert lib.mlora_probe_read(*args, ctypes.byref(us)) != 0, args
+    assert lib.mlora_probe_read(0, 4096, 12, 10, None) != 0
