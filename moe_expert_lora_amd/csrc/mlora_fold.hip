@@ -713,6 +713,141 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(
 
 
 // ---------------------------------------------------------------------------
+// gather over dense slices: one-entry routes
+// ---------------------------------------------------------------------------
+
+// A route with a single expert (the router's fold) folds nearly every row of
+// every slice, so its slices are short (at most 16*MB rows) and taken in
+// place, without the routing scan's compaction. The x rows of a slice follow
+// from its row numbers alone: every x fragment of the wave's k steps is
+// requested at once, together with the rows' routing and before the table
+// cell is back, and a row's routing (its expert id and map entry) only gates
+// its base_out read and store. A row that folds nothing costs its x loads and
+// MFMA columns; its output is neither read nor written. The k steps, their
+// order and the reduction are those of fold_rows, so every row comes out bit
+// for bit as from the compacting kernel.
+constexpr int kDenseSteps = 16;  // k steps per wave: k_in up to 4 * 16 * 32 = 2048
+
+template <int NB, int MB, bool FULL_R>
+__global__ __launch_bounds__(kThreads) void gather_dense_kernel(
+    const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
+    const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
+    GatherArgs p) {
+  __shared__ float s_part[kWaves * MB * 64 * 4 * NB];
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * per_xcd + slot;
+  if (u >= units) return;
+  const int e = u / per_e;
+  const int within = u - e * per_e;
+  const int rs = within / inner, ns = within - rs * inner;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int start = rs * p.scan_len;
+  const int nrows = min(p.scan_len, p.n_slots - start);  // <= 16 * MB (the plan)
+  const int nrb = (nrows + 15) >> 4;
+  const rsrc_t r_idx = make_buf(p.indices, (uint32_t)p.n_slots * 4u);
+  const rsrc_t r_map = make_buf(p.row_adapter, (uint32_t)p.n_tokens * 4u);
+  const rsrc_t r_x = make_buf(p.x, p.x_bytes);
+  // the rows' routing, then their x fragments
+  Rows<MB> rw;
+  int iv[MB], mv[MB];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    const int m = rb * 16 + li;
+    const bool in = m < nrows;
+    const int row = start + (in ? m : 0);
+    const uint32_t tok = udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
+    const uint32_t xr = p.x_by_row ? (uint32_t)row : tok;
+    iv[rb] = (int)bld4(r_idx, in ? (uint32_t)row * 4u : kOOB);
+    mv[rb] = (int)bld4(r_map, in ? tok * 4u : kOOB);
+    rw.valid[rb] = in;
+    rw.xoff[rb] = xr * (uint32_t)p.x_ld * 2u;
+    rw.ooff[rb] = (uint32_t)row * (uint32_t)p.out_ld * 2u;
+  }
+  // the routing ahead of the x rows: waiting for it later waits for it alone
+  __builtin_amdgcn_sched_barrier(0);
+  const int K = p.K, R = p.R;
+  const int nks = (K + 31) >> 5;
+  u32x4 xv[kDenseSteps][MB];
+#pragma unroll
+  for (int t = 0; t < kDenseSteps; ++t) {
+    const int s = wave_step(wave, t);
+    const int k0 = s * 32 + g * 8;
+    const bool kin = s < nks && k0 < K;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+      xv[t][rb] = bld16(r_x, (kin && rw.valid[rb]) ? rw.xoff[rb] + 2u * k0 : kOOB);
+  }
+  // The table cell is requested only now: scalar loads return out of order,
+  // so any argument fetched after it would wait for it, and the x loads above
+  // must not. No early return for an unadapted cell either (the branch would
+  // be hoisted above the loads): it gets empty weight buffers and no row
+  // that folds.
+  __builtin_amdgcn_sched_barrier(0);
+  const uint64_t a_addr = uniform_u64(a_table[e]), b_addr = uniform_u64(b_table[e]);
+  const float scale = uniform_f32(scale_table[e]);
+  const bool cell = a_addr != 0 && b_addr != 0;
+
+  Bufs bf;
+  bf.x = r_x;
+  bf.a = make_buf(reinterpret_cast<const void*>(a_addr), cell ? (uint32_t)(R * K) * 2u : 0u);
+  bf.b = make_buf(reinterpret_cast<const void*>(b_addr), cell ? (uint32_t)(p.N * R) * 2u : 0u);
+  bf.out = make_buf(p.out, p.out_bytes);
+  u32x4 av[kDenseSteps][NB];
+#pragma unroll
+  for (int t = 0; t < kDenseSteps; ++t) {
+    const int s = wave_step(wave, t);
+    const int k0 = s * 32 + g * 8;
+    const bool kin = s < nks && k0 < K;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
+      av[t][b] = bld16(bf.a, (kin && rank < R) ? (uint32_t)(rank * K + k0) * 2u : kOOB);
+    }
+  }
+  // every A_e fragment in flight before the first MFMA waits for one
+  __builtin_amdgcn_sched_barrier(0);
+  // rows that fold (in the slice, routed to this expert, mapped): their
+  // base_out and the slice's B_e are requested before the shrink is done
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb)
+    rw.valid[rb] = cell && rw.valid[rb] && iv[rb] == e && mv[rb] >= 0;
+  constexpr int UE = Batch<NB, MB>::UE;
+  const int n_lo = ns * p.ns_cols;
+  const int n_hi = min(n_lo + p.ns_cols, p.N);
+  const int ncs = (n_hi - n_lo + kColStep - 1) / kColStep;
+  ExpandBatch<NB, MB, UE> e0;
+  load_expand<NB, MB, UE, FULL_R>(e0, bf, R, rw, wave, 0, ncs, n_lo, n_hi, li, g);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 hacc[MB][NB];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) hacc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Every MFMA is issued and its result kept only for k steps and row blocks
+  // in range (a select, not a branch: a branch would draw the loads it
+  // consumes into it), so the sums are fold_rows' sums term for term.
+#pragma unroll
+  for (int t = 0; t < kDenseSteps; ++t) {
+    const bool tin = wave_step(wave, t) < nks;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      const bool use = tin && rb < nrb;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const f32x4 r = mfma16x16x32(as_bf(av[t][b]), as_bf(xv[t][rb]), hacc[rb][b]);
+        hacc[rb][b] = use ? r : hacc[rb][b];
+      }
+    }
+  }
+  HOp<NB> hop[MB];
+  reduce_split<NB, MB>(hacc, s_part, scale, nrb, wave, lane, hop);
+  expand_rows<NB, MB, FULL_R>(bf, R, rw, hop, nrb, n_lo, n_hi, wave, li, g, e0);
+}
+
+// ---------------------------------------------------------------------------
 // gather, two-kernel form: k-split shrink into a workspace, then expand
 // ---------------------------------------------------------------------------
 
@@ -1950,6 +2085,7 @@ __global__ __launch_bounds__(kThreads) void rowwise_f32_kernel(RowwiseArgs p) {
 // beyond the rounding differences of the two-kernel gather.
 struct Overrides {
   int gather_rs, gather_ns, gather_small, gather_resident, gather_two, gather_two_ns;
+  int gather_dense;
   int grouped_mb, grouped_ns, shrink_mb, expand_mb, expand_cw, all_min_rows;
 };
 constexpr int kUnset = -0x7fffffff;
@@ -1968,6 +2104,7 @@ Overrides read_overrides() {
   o.gather_resident = read_env("MLORA_GATHER_RESIDENT");
   o.gather_two = read_env("MLORA_GATHER_TWO");
   o.gather_two_ns = read_env("MLORA_GATHER_TWO_NS");
+  o.gather_dense = read_env("MLORA_GATHER_DENSE");
   o.grouped_mb = read_env("MLORA_GROUPED_MB");
   o.grouped_ns = read_env("MLORA_GROUPED_NS");
   o.shrink_mb = read_env("MLORA_SHRINK_MB");
@@ -2131,8 +2268,25 @@ void launch_resident(const GatherArgs& a, int grid, hipStream_t s) {
                      LEAD_ARGS(a, a.ns_count));
 }
 
-void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small, bool resident) {
+template <int NB, int MB>
+void launch_dense(const GatherArgs& a, int grid, hipStream_t s) {
+  if (a.R == 16 * NB)
+    hipLaunchKernelGGL((gather_dense_kernel<NB, MB, true>), dim3(grid), dim3(kThreads), 0, s,
+                       LEAD_ARGS(a, a.ns_count));
+  else
+    hipLaunchKernelGGL((gather_dense_kernel<NB, MB, false>), dim3(grid), dim3(kThreads), 0, s,
+                       LEAD_ARGS(a, a.ns_count));
+}
+
+void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small, bool resident,
+                     int dense_mb) {
   const int nb = (a.R + 15) / 16;
+  if (dense_mb > 0) {
+    // the plan's shapes: 32-row slices for one rank block, 16 for two
+    if (nb <= 1) launch_dense<1, 2>(a, grid, s);
+    else launch_dense<2, 1>(a, grid, s);
+    return;
+  }
   if (resident && gather_resident_fits(a)) {
     if (nb <= 1) {
       if (a.R == 16) launch_resident<1, true>(a, grid, s);
@@ -2192,6 +2346,7 @@ struct GatherPlan {
   int grid;
   int small, resident;
   bool use_resident;
+  int dense_mb;  // > 0: one-entry route in slices of at most 16 * dense_mb rows taken in place
 };
 
 int32_t plan_gather(const char* who, const mlora_expert_route* route, const void* x,
@@ -2224,6 +2379,16 @@ int32_t plan_gather(const char* who, const mlora_expert_route* route, const void
   // workgroups: the router's fold over 80 decode tokens (k_in 2048) measured
   // 11.3 us at 2 slices, 7.6-8.0 us at 8-16.
   while ((int64_t)E * rs * ns < target / 4 && rows_per_e / (rs * 2) >= 4) rs *= 2;
+  // A one-entry route (a router's fold) goes to the dense-slice kernel when
+  // its operands fit the kernel's registers: slices of at most 32 rows (16 for
+  // ranks above 16), every k step of a wave's x in registers.
+  const int dense_mb = kernel_nb(R) == 1 ? 2 : 1;
+  bool dense = E == 1 && kernel_nb(R) <= 2 && (K + 31) / 32 <= kWaves * kDenseSteps &&
+               ov(overrides().gather_dense, 1) != 0;
+  if (dense) {
+    const int64_t need = (n_slots + 16 * dense_mb - 1) / (16 * dense_mb);
+    if (rs < need) rs = (int)need;
+  }
   const double shrink_b = 2.0 * R * K + 2.0 * (double)rows_per_e / rs * K;
   const double expand_b = 2.0 * N * R + 4.0 * (double)rows_per_e / rs * N;
   while ((int64_t)E * rs * ns < target && ns * 2 <= ns_max &&
@@ -2239,6 +2404,8 @@ int32_t plan_gather(const char* who, const mlora_expert_route* route, const void
     rs = (int)((n_slots + kScanMax - 1) / kScanMax);
     scan = (int)((n_slots + rs - 1) / rs);
   }
+  // (an override of the row slices can leave them longer than the dense kernel takes)
+  if (scan > 16 * dense_mb) dense = false;
 
   GatherArgs a{};
   a.x = static_cast<const uint16_t*>(x);
@@ -2279,6 +2446,7 @@ int32_t plan_gather(const char* who, const mlora_expert_route* route, const void
   // 16-row blocks (and the wave's share fits)
   plan->resident = ov(overrides().gather_resident, rows_per_slice <= 32 ? 1 : 0);
   plan->use_resident = plan->resident != 0 && gather_resident_fits(a);
+  plan->dense_mb = dense ? dense_mb : 0;
   return MLORA_OK;
 }
 
@@ -2362,7 +2530,7 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
   const bool two_fits = (K + 31) / 32 <= kMaxKc * kWaves * kTwoSteps;
   const int64_t rows_e_all = (n_slots + E - 1) / E;
   const int two_default = (gather_kc(K) > 1 && rows_e_all > 6 && rows_e_all <= 64) ? 1 : 0;
-  if (workspace && !use_resident && two_fits &&
+  if (workspace && !use_resident && plan.dense_mb == 0 && two_fits &&
       ov(overrides().gather_two, two_default) != 0) {
     if (ws_need > (int64_t)kMaxBufBytes)
       return fail(MLORA_ERR_INVALID, "%s: workspace above 4 GiB; split the call", who);
@@ -2405,7 +2573,7 @@ extern "C" int32_t mlora_gather_bgmv(const mlora_expert_route* route, const void
     dispatch_gather_two(g1, g2, s, mb);
     return launched(who);
   }
-  dispatch_gather(a, grid, s, small != 0, resident != 0);
+  dispatch_gather(a, grid, s, small != 0, resident != 0, plan.dense_mb);
   return launched(who);
 }
 
@@ -2510,7 +2678,7 @@ extern "C" int32_t mlora_gather_bgmv_set(const mlora_projection* projs, int32_t 
     // one call with rows: the single-call kernels (the decode-resident one
     // where it fits), which take their leading arguments preloaded
     const GatherPlan& pl = plans[only];
-    dispatch_gather(pl.a, pl.grid, s, pl.small != 0, pl.resident != 0);
+    dispatch_gather(pl.a, pl.grid, s, pl.small != 0, pl.resident != 0, pl.dense_mb);
     return launched(who);
   }
   gs.per_xcd = (int32_t)((total + kXcds - 1) / kXcds);

@@ -740,3 +740,35 @@ def test_graph_replay_workspace_forms(form, overrides):
     view.b_table[live_e] = 0
     check(view, from_torch(base), c.base, f"{form} graph replay, new map and table")
 
+
+
+@pytest.mark.parametrize("label", ["router_gather", "router_skips_wild", "router_r32_k768",
+                                   "router_rows_not_multiple", "router_null_cell"])
+def test_dense_slices_equal_compacting_kernel(label, overrides):
+    """A one-entry route runs as dense slices (rows taken in place, no routing
+    compaction); the compacting kernel folds every row in the same order, so
+    the outputs are equal bit for bit, skipped and wild rows untouched, and the
+    dense form passes the oracle bar on its own."""
+    _need_gpu()
+    from staging import DeviceCase
+    if label == "router_gather":
+        case, view, dev = staged(label)
+    else:
+        kw = dict(n_seq=6, padded_n=300, top_k=1, n_route=1, k_in=2048, n_out=160, max_rank=16,
+                  adapted=np.array([0]), index_mode="zero", name=label)
+        if label == "router_skips_wild":
+            kw.update(n_seq=40, padded_n=333, skip_seqs=5, wild_index_frac=0.1, n_slots=333)
+        elif label == "router_r32_k768":
+            kw.update(k_in=768, max_rank=32, n_out=96, padded_n=250)
+        elif label == "router_rows_not_multiple":
+            kw.update(padded_n=37, k_in=1000, max_rank=12, n_out=72)
+        case = workloads.make_gather_case(314, **kw)
+        if label == "router_null_cell":
+            # the one cell is packed without matrices: nothing folds
+            case.entries = [(0, workloads.NULL_HANDLE, workloads.NULL_HANDLE, 0.0)]
+        view, dev = OracleView(case), DeviceCase(case, DEV)
+    dense = dev.run()
+    check(view, dense, case.base, f"{label} dense")
+    overrides.set("MLORA_GATHER_DENSE", "0")
+    compact = dev.run()
+    assert np.array_equal(dense.view(np.uint8), compact.view(np.uint8))
