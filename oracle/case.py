@@ -66,8 +66,10 @@ class OracleView:
     def _fold_with(self, x, mats, scales, base64, windows):
         c = self.case
         if c.path == "gather":
+            # slot-major cases (notes["x_rows"] == "row") read x at the flat row
             return _fold.fold_gather(x, self.a_table, self.b_table, scales, mats, base64,
-                                     c.indices, self.row_adapter, c.top_k)
+                                     c.indices, self.row_adapter, c.top_k,
+                                     x_rows=c.notes.get("x_rows", "token"))
         if windows is None:
             windows = self.windows()
         return _fold.fold_grouped_windows(x, self.a_table, self.b_table, scales, mats, base64,

@@ -164,3 +164,48 @@ def test_set_shapes(shape):
             continue
         alone = d.run(two_kernel=False)
         assert np.array_equal(from_torch(o).view(np.uint16), alone.view(np.uint16)), c.name
+
+
+@pytest.mark.parametrize("x_by_row", [False, True])
+def test_one_entry_route_dense_slices_with_strides(x_by_row, overrides):
+    """A one-entry route (top_k 3, so token and flat row differ) as a
+    one-member set with strided x and base_out: the dense-slice kernel it
+    runs on equals the compacting kernel bit for bit, meets the oracle bound
+    (slot-major x when x_by_row), and leaves the guard columns untouched."""
+    import moe_expert_lora_amd as ml
+    from staging import DeviceCase, from_torch, to_torch
+    _need_gpu()
+    case = workloads.make_gather_case(271, n_seq=30, padded_n=37, top_k=3, n_route=1, k_in=520,
+                                      n_out=200, max_rank=16, adapted=np.array([0]),
+                                      index_mode="zero", skip_seqs=4, name="one_entry_strided")
+    if x_by_row:
+        rng = np.random.default_rng([271, 9])
+        case.x = workloads._values(rng, (case.n_rows, case.k_in), 1.0, "bf16")
+        case.n_tokens = case.n_rows
+        case.notes["x_rows"] = "row"
+    dev = DeviceCase(case, DEV)
+    gx, gout = 24, 40  # extra columns after each x / base_out row
+    x_wide = np.zeros((case.x.shape[0], case.k_in + gx), dtype=np.uint16)
+    x_wide[:, :case.k_in] = case.x
+    x_wide[:, case.k_in:] = 0x7FC1  # NaN columns no fold may read
+    xt = to_torch(x_wide, "bf16", DEV)
+    outs = {}
+    for dense in ("1", "0"):
+        overrides.set("MLORA_GATHER_DENSE", dense)
+        out0 = np.full((case.n_rows, case.n_out + gout), 0x7F81, dtype=np.uint16)
+        out0[:, :case.n_out] = case.base
+        out = to_torch(out0, "bf16", DEV)
+        proj = ml.make_projection(dev.route, xt[:, :case.k_in], out[:, :case.n_out], dev.indices,
+                                  dev.row_adapter, case.top_k, x_by_row=x_by_row)
+        ml.mlora_gather_bgmv_set([proj])
+        torch.cuda.synchronize()
+        outs[dense] = from_torch(out)
+    got = outs["1"]
+    assert np.array_equal(got.view(np.uint8), outs["0"].view(np.uint8))
+    assert np.all(got[:, case.n_out:] == 0x7F81)
+    view, ref = oracle_fold(case, case.base)
+    g = to_f64(got[:, :case.n_out], "bf16")
+    rel, mx, ex = parity_figures(view, g, ref, "one_entry_strided")
+    assert rel <= REL_L2_TOL and ex <= 1.0, (rel, mx, ex)
+    live = view.live_rows()
+    assert np.array_equal(got[~live, :case.n_out], case.base[~live])

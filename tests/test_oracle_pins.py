@@ -22,6 +22,7 @@ from hypothesis import given, settings, strategies as st
 
 import oracle
 from tests.common import OracleView, golden_json, golden_lines
+import workloads
 from workloads import make_gather_case, make_grouped_case
 
 # ---------------------------------------------------------------------------
@@ -762,3 +763,27 @@ def test_eval_margin_covers_fp32_evaluation():
     err = np.abs(out - ref)
     assert np.all(err <= eps)
     assert float(np.max(err / np.maximum(eps, 1e-300))) < 0.2
+
+
+def test_oracle_view_folds_slot_major_cases_by_row():
+    """The fp64 view of a slot-major case (the decode layer's down fold)
+    reads x at the flat row, in its fold and in its magnitude fold (the
+    tolerance's scale), not at the row's token."""
+    import oracle
+    from oracle.case import OracleView, to_f64
+    down = workloads.decode_layer_cases(seed=7, n_seq=6, padded_n=8, top_k=3, n_route=10,
+                                        n_adapted=8, skip_seqs=1, hidden=64, inter=48)[3]
+    assert down.notes["x_rows"] == "row"
+    view = OracleView(down)
+    base = to_f64(down.base, down.dtype)
+    args = (view.x, view.a_table, view.b_table, view.scale_table, view.mats, base,
+            down.indices, view.row_adapter, down.top_k)
+    by_row = oracle.fold_gather(*args, x_rows="row")
+    by_token = oracle.fold_gather(*args, x_rows="token")
+    assert not np.allclose(by_row, by_token)
+    np.testing.assert_array_equal(view.fold(), by_row)
+    mats = {k: np.abs(m) for k, m in view.mats.items()}
+    mag = oracle.fold_gather(np.abs(view.x), view.a_table, view.b_table,
+                             [abs(float(s)) for s in view.scale_table], mats, np.zeros_like(base),
+                             down.indices, view.row_adapter, down.top_k, x_rows="row")
+    np.testing.assert_array_equal(view.magnitude(), mag)
