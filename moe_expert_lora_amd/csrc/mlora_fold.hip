@@ -720,9 +720,9 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(
 // every slice, so its slices are short (at most 16*MB rows) and taken in
 // place, without the routing scan's compaction. The x rows of a slice follow
 // from its row numbers alone: every x fragment of the wave's k steps is
-// requested at once, together with the rows' routing and before the table
-// cell is back, and a row's routing (its expert id and map entry) only gates
-// its base_out read and store. A row that folds nothing costs its x loads and
+// requested at once, right after the rows' routing and before the table cell,
+// and a row's routing (its expert id and map entry) only gates its base_out
+// read and store. A row that folds nothing costs its x loads and
 // MFMA columns; its output is neither read nor written. The k steps, their
 // order and the reduction are those of fold_rows, so every row comes out bit
 // for bit as from the compacting kernel.
