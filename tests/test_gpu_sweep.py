@@ -1,0 +1,122 @@
+"""GPU parity over a seeded sweep of shapes, through every launch form.
+
+Each case draws its sizes from its seed (k_in and n_out multiples of 8 from
+8 up; ranks 1 to 128; top_k 1 to 8; routes of 1 to 40 experts, one-entry
+routes included; skipped, refused and wild-index rows; slot counts that are
+not a multiple of top_k; grouped windows from a few rows up) and is folded by
+the default form and by every form the overrides can force. Every result must
+meet the oracle bound, and every row that folds nothing must keep its bits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from tests.common import OracleView
+from tests.test_gpu_fold import DEV, _need_gpu, check
+
+pytestmark = pytest.mark.gpu
+
+GATHER_SEEDS = list(range(24))
+GROUPED_SEEDS = list(range(12))
+
+# forced gather forms: (label, overrides, run with a workspace)
+GATHER_FORMS = [
+    ("default", {}, True),
+    ("no workspace", {}, False),
+    ("streaming one kernel", {"MLORA_GATHER_RESIDENT": "0", "MLORA_GATHER_TWO": "0",
+                              "MLORA_GATHER_DENSE": "0"}, True),
+    ("two kernels", {"MLORA_GATHER_RESIDENT": "0", "MLORA_GATHER_TWO": "1",
+                     "MLORA_GATHER_DENSE": "0"}, True),
+    ("small chunks", {"MLORA_GATHER_SMALL": "1", "MLORA_GATHER_RESIDENT": "0",
+                      "MLORA_GATHER_DENSE": "0"}, False),
+]
+
+
+def gather_case(seed):
+    rng = np.random.default_rng([4242, seed])
+    one_entry = seed % 6 == 5
+    top_k = 1 if one_entry and seed % 12 == 5 else int(rng.integers(1, 9))
+    n_route = 1 if one_entry else int(rng.integers(max(2, top_k), 41))
+    n_seq = int(rng.integers(1, 65))
+    padded_n = n_seq + int(rng.integers(0, 9))
+    k_in = 8 * int(rng.integers(1, 263))
+    n_out = 8 * int(rng.integers(1, 138))
+    max_rank = int(rng.choice([1, 3, 8, 12, 16, 17, 24, 32, 40, 64, 100, 128]))
+    kw = dict(n_seq=n_seq, padded_n=padded_n, top_k=top_k, n_route=n_route, k_in=k_in,
+              n_out=n_out, max_rank=max_rank, skip_seqs=int(rng.integers(0, max(1, n_seq // 4))),
+              name=f"sweep_gather_{seed}")
+    if one_entry:
+        kw.update(index_mode="zero", adapted=np.array([0]))
+    else:
+        kw.update(n_adapted=int(rng.integers(1, n_route + 1)),
+                  refuse_seqs=int(rng.integers(0, 2)) if n_seq > 4 else 0,
+                  wild_index_frac=float(rng.choice([0.0, 0.1])),
+                  dup_frac=float(rng.choice([0.0, 0.2])))
+        if seed % 4 == 3:  # slots not a multiple of top_k
+            kw["n_slots"] = max(1, padded_n * top_k - int(rng.integers(1, top_k + 1)))
+    return workloads.make_gather_case(7000 + seed, **kw)
+
+
+def grouped_case(seed):
+    rng = np.random.default_rng([4343, seed])
+    n_streams = int(rng.integers(1, 5))
+    lens = [int(v) for v in rng.integers(0, 160, size=n_streams)]
+    if sum(lens) == 0:
+        lens[0] = 1
+    top_k = int(rng.integers(1, 9))
+    n_route = int(rng.integers(top_k, top_k + 30))
+    kw = dict(stream_lens=lens, top_k=top_k, n_route=n_route,
+              k_in=8 * int(rng.integers(1, 200)), n_out=8 * int(rng.integers(1, 140)),
+              max_rank=int(rng.choice([1, 5, 16, 24, 32, 48, 64, 128])),
+              routing=str(rng.choice(["uniform", "zipf"])),
+              n_unadapted=int(rng.integers(0, n_route // 2 + 1)),
+              dup_frac=float(rng.choice([0.0, 0.2])),
+              cap=int(rng.choice([3, 17, 64, 100, 1000])),
+              stream_slot_values=[int(v) for v in rng.choice([1, 1, 1, -1], size=n_streams)],
+              name=f"sweep_grouped_{seed}")
+    return workloads.make_grouped_case(7100 + seed, **kw)
+
+
+def _sentinel_run(view, dev, case, **kw):
+    live = view.live_rows()
+    if live.all():
+        return
+    base = case.base.copy()
+    base.view(np.uint16)[~live] = 0x7F81
+    got = dev.run(base, **kw)
+    assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
+
+
+@pytest.mark.parametrize("seed", GATHER_SEEDS)
+def test_gather_sweep_every_form(seed, overrides):
+    _need_gpu()
+    from staging import DeviceCase
+    case = gather_case(seed)
+    view = OracleView(case)
+    dev = DeviceCase(case, DEV)
+    for label, ov, ws in GATHER_FORMS:
+        for k in ("MLORA_GATHER_RESIDENT", "MLORA_GATHER_TWO", "MLORA_GATHER_DENSE",
+                  "MLORA_GATHER_SMALL"):
+            if k in ov:
+                overrides.set(k, ov[k])
+            else:
+                overrides.delete(k)
+        check(view, dev.run(two_kernel=ws), case.base, f"{case.name} {label}")
+    _sentinel_run(view, dev, case)
+
+
+@pytest.mark.parametrize("seed", GROUPED_SEEDS)
+def test_grouped_sweep_every_form(seed):
+    _need_gpu()
+    from staging import DeviceCase
+    case = grouped_case(seed)
+    view = OracleView(case)
+    dev = DeviceCase(case, DEV)
+    windows = view.windows()
+    for label, kw in (("two kernels", dict(two_kernel=True, pipelined=False)),
+                      ("one kernel", dict(two_kernel=False, pipelined=False)),
+                      ("all windows", dict(two_kernel=True, pipelined=True))):
+        check(view, dev.run(**kw), case.base, f"{case.name} {label}", windows=windows)
+    _sentinel_run(view, dev, case, two_kernel=True, pipelined=True)
