@@ -4,8 +4,10 @@ Each case draws its sizes from its seed (k_in and n_out multiples of 8 from
 8 up; ranks 1 to 128; top_k 1 to 8; routes of 1 to 40 experts, one-entry
 routes included; skipped, refused and wild-index rows; slot counts that are
 not a multiple of top_k; grouped windows from a few rows up) and is folded by
-the default form and by every form the overrides can force. Every result must
-meet the oracle bound, and every row that folds nothing must keep its bits.
+the default form and by every form the overrides can force; multi-adapter
+cases add adapter counts, uninstalled slots and partly adapted slots. Every
+result must meet the oracle bound, and every row that folds nothing must keep
+its bits.
 """
 from __future__ import annotations
 
@@ -120,3 +122,40 @@ def test_grouped_sweep_every_form(seed):
                       ("all windows", dict(two_kernel=True, pipelined=True))):
         check(view, dev.run(**kw), case.base, f"{case.name} {label}", windows=windows)
     _sentinel_run(view, dev, case, two_kernel=True, pipelined=True)
+
+
+MULTI_SEEDS = list(range(8))
+
+
+def multi_case(seed):
+    rng = np.random.default_rng([4444, seed])
+    top_k = int(rng.integers(1, 9))
+    n_seq = int(rng.integers(2, 49))
+    return workloads.make_multi_gather_case(
+        7200 + seed, n_seq=n_seq, padded_n=n_seq + int(rng.integers(0, 6)), top_k=top_k,
+        n_route=int(rng.integers(top_k, 40)), k_in=8 * int(rng.integers(1, 257)),
+        n_out=8 * int(rng.integers(1, 130)),
+        max_rank=int(rng.choice([1, 7, 16, 24, 32, 64, 128])),
+        n_adapters=int(rng.integers(1, 6)), adapted_frac=float(rng.choice([0.3, 0.75, 1.0])),
+        skip_seqs=int(rng.integers(0, max(1, n_seq // 4))),
+        uninstalled_seqs=int(rng.integers(0, 2)), dup_frac=float(rng.choice([0.0, 0.2])),
+        name=f"sweep_multi_{seed}")
+
+
+@pytest.mark.parametrize("seed", MULTI_SEEDS)
+def test_multi_sweep(seed):
+    """The multi-adapter fold over seeded shapes: the oracle bound and rows
+    that fold nothing untouched."""
+    _need_gpu()
+    from oracle.case import OracleMultiView
+    from staging import DeviceMultiCase
+    from tests.test_gpu_multi import _check
+    case = multi_case(seed)
+    view, dev = OracleMultiView(case), DeviceMultiCase(case, DEV)
+    _check(view, dev.run(), case.base, f"{case.name} R")
+    live = view.live_rows()
+    if not live.all():
+        base = case.base.copy()
+        base.view(np.uint16)[~live] = 0x7F81
+        got = dev.run(base)
+        assert np.array_equal(got[~live].view(np.uint8), base[~live].view(np.uint8))
