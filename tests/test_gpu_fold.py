@@ -772,3 +772,50 @@ def test_dense_slices_equal_compacting_kernel(label, overrides):
     overrides.set("MLORA_GATHER_DENSE", "0")
     compact = dev.run()
     assert np.array_equal(dense.view(np.uint8), compact.view(np.uint8))
+
+
+def test_graph_replay_dense_one_entry_route():
+    """The dense-slice kernel (a one-entry route) captured in a HIP graph:
+    replays match the eager fold, and replays after the map, then the table
+    cell, are rewritten in place follow the new contents."""
+    _need_gpu()
+    from staging import DeviceCase, from_torch, to_torch
+    c = workloads.make_gather_case(84, n_seq=1, padded_n=300, top_k=1, n_route=1, k_in=1024,
+                                   n_out=96, max_rank=16, adapted=np.array([0]),
+                                   index_mode="zero", name="graph_dense")
+    dev = DeviceCase(c, DEV)
+    pristine = to_torch(c.base, "bf16", DEV)
+    base = pristine.clone()
+    eager = dev.run()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            dev.fold(base)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        base.copy_(pristine)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_torch(base), eager)
+    # a new map: about a third of the token rows skip
+    rng = np.random.default_rng(85)
+    new_map = np.where(rng.random(dev.row_adapter.numel()) < 0.35, -1, 1).astype(np.int32)
+    dev.row_adapter.copy_(torch.from_numpy(new_map))
+    base.copy_(pristine)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    view = OracleView(c)
+    view.row_adapter = new_map
+    check(view, from_torch(base), c.base, "graph replay dense, new map")
+    # the cell cleared: nothing folds
+    dev.b_table[0] = 0
+    base.copy_(pristine)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(from_torch(base), c.base)
