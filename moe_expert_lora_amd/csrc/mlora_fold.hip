@@ -37,7 +37,8 @@
 //    one span (or, in the shrink kernel, two spans) at a time.
 //  * Workgroup ids are mapped so that consecutive work units (the splits of
 //    one expert, or neighbouring row tiles) run on the same XCD and share its
-//    L2.
+//    L2. The grouped expand is the exception: its units go to the XCDs in
+//    turn (see there).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -1849,8 +1850,8 @@ __global__ __launch_bounds__(kThreads) void grouped_shrink_kernel(GroupedArgs p)
   grouped_shrink_unit<NB, MB>(p, u, sm);
 }
 
-// Expand: one wave per (16*MB rows, CW column steps). It reads the rows' meta,
-// then requests H', the B_e fragments of the first run of rows (rows with one
+// Expand: one wave per (16*MB rows, CW column steps). It requests the rows'
+// meta and H', then the B_e fragments of the first run of rows (rows with one
 // B_e) and the rows' base_out, the last in a row-contiguous layout: LPR lanes
 // cover one row's CW*32 columns, 16 bytes each. The MFMA deltas (fp32, one
 // lane per row) go through the wave's own LDS to that layout; each row is
@@ -1907,32 +1908,21 @@ __device__ __forceinline__ void grouped_expand_unit(const GroupedArgs& p, int u,
   const bool is_live = (mv.x | mv.y) != 0;
   const uint64_t live = __ballot(is_live);
   if (live == 0) return;
-  u32x4 bv[NI];
-  uint32_t boff[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int col = n_lo + 8 * cc;
-    boff[i] = (uint32_t)(r0 + i * RPI + cr) * (uint32_t)p.N * 2u + 2u * col;
-    const bool ok = col < n_hi && ((live >> (i * RPI + cr)) & 1ull) != 0;
-    bv[i] = bld16_nt(r_out, ok ? boff[i] : kOOB);
-  }
   // a run starts at a live row whose previous live row has another B_e
   const uint64_t below = live & ((1ull << lane) - 1ull);
   const int prev = below ? 63 - __clzll((long long)below) : lane;
   const uint32_t plo = (uint32_t)__shfl((int)mv.x, prev), phi = (uint32_t)__shfl((int)mv.y, prev);
   uint64_t starts = __ballot(is_live && (below == 0 || plo != mv.x || phi != mv.y));
 
-  while (starts) {
-    const int s = __ffsll((unsigned long long)starts) - 1;
-    starts &= starts - 1ull;
-    const int e_row = starts ? __ffsll((unsigned long long)starts) - 1 : 64;
+  auto request_b = [&](BFrag<NB> (&bw)[CW], int s) {
     const uint64_t b_addr = lane_u64(mv.x, mv.y, s);
     const rsrc_t r_b =
         make_buf(reinterpret_cast<const void*>(b_addr), (uint32_t)(p.N * p.R) * 2u);
-    BFrag<NB> bw[CW];
 #pragma unroll
     for (int c = 0; c < CW; ++c)
       load_bfrag<NB, FULL_R>(bw[c], r_b, p.R, n_lo + c * kColStep, n_hi, li, g);
+  };
+  auto run = [&](const BFrag<NB> (&bw)[CW], int s, int e_row) {
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
       if (rb * 16 < e_row && rb * 16 + 16 > s) {
@@ -1957,6 +1947,32 @@ __device__ __forceinline__ void grouped_expand_unit(const GroupedArgs& p, int u,
         }
       }
     }
+  };
+  // The first run's B_e is requested ahead of base_out: waits count loads in
+  // issue order, so its MFMAs and LDS writes then run while base_out is still
+  // on its way (measured 3% faster per call on the 32768-row down projection).
+  BFrag<NB> bw0[CW];
+  const int s0 = __ffsll((unsigned long long)starts) - 1;
+  starts &= starts - 1ull;
+  request_b(bw0, s0);
+  u32x4 bv[NI];
+  uint32_t boff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int col = n_lo + 8 * cc;
+    boff[i] = (uint32_t)(r0 + i * RPI + cr) * (uint32_t)p.N * 2u + 2u * col;
+    const bool ok = col < n_hi && ((live >> (i * RPI + cr)) & 1ull) != 0;
+    bv[i] = bld16_nt(r_out, ok ? boff[i] : kOOB);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  run(bw0, s0, starts ? __ffsll((unsigned long long)starts) - 1 : 64);
+  while (starts) {
+    const int s = __ffsll((unsigned long long)starts) - 1;
+    starts &= starts - 1ull;
+    const int e_row = starts ? __ffsll((unsigned long long)starts) - 1 : 64;
+    BFrag<NB> bw[CW];
+    request_b(bw, s);
+    run(bw, s, e_row);
   }
   wave_lds_sync();
 #pragma unroll
@@ -1974,11 +1990,16 @@ __device__ __forceinline__ void grouped_expand_unit(const GroupedArgs& p, int u,
   }
 }
 
+// Expand units are dealt to the XCDs in turn (the hardware's own order), so
+// the column slices of a row block run on different XCDs and every XCD's
+// share of base_out is spread over the whole window rather than one
+// contiguous eighth. The read-modify-write stream measured faster that way
+// (a plain 64 MiB one: 24.1 against 26.5 us); each XCD then reads only its
+// column slices of B_e, and H' (4 * R bytes a row) is read by several XCDs.
 template <int NB, int MB, int CW, bool FULL_R>
 __global__ __launch_bounds__(64) void grouped_expand_kernel(GroupedArgs p) {
   __shared__ float s_d[ExpandSmem<MB, CW>::kFloats];
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int u = xcd * p.per_xcd + slot;
+  const int u = blockIdx.x;
   if (u >= p.units) return;
   grouped_expand_unit<NB, MB, CW, FULL_R>(p, u, s_d);
 }
@@ -2002,11 +2023,10 @@ __global__ __launch_bounds__(kThreads) void grouped_pipe_kernel(GroupedArgs ps, 
     if (u < ps.units) grouped_shrink_unit<NB, SMB, 1>(ps, u, sm.s);
     return;
   }
-  // sblocks is a multiple of kXcds, so b keeps the block's XCD
+  // expand waves in block order, as in the expand kernel
   const int b = (int)blockIdx.x - sblocks;
-  const int xcd = b % kXcds, slot = b / kXcds;
   const int wave = threadIdx.x >> 6;
-  const int u = (xcd * pe.per_xcd + slot) * kWaves + wave;
+  const int u = b * kWaves + wave;
   if (u < pe.units) grouped_expand_unit<NB, EMB, CW, FULL_R>(pe, u, sm.d[wave]);
 }
 
