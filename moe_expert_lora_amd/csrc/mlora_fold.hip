@@ -301,7 +301,7 @@ __device__ __forceinline__ f32x4 mfma_chunk(const uint32_t (&a)[CW], const uint3
 }
 
 // Loads are issued in batches: the k steps of one shrink batch (A_e and x
-// fragments) or the column steps of one expand batch (B_e and base_out
+// fragments) or the column steps of one expand batch (B_e, then base_out
 // fragments) are requested together and consumed after a single wait. Two
 // batch buffers alternate, so the next batch is in flight while the current
 // one is multiplied: a wave always has memory requests outstanding. The batch
@@ -381,8 +381,12 @@ __device__ __forceinline__ void load_expand(ExpandBatch<NB, MB, UE>& eb, const B
 #pragma unroll
   for (int u = 0; u < UE; ++u) {
     const int cs = col_step(wave, t0 + u, ncs);
+    load_bfrag<NB, FULL_R>(eb.b[u], bf.b, R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li, g);
+  }
+#pragma unroll
+  for (int u = 0; u < UE; ++u) {
+    const int cs = col_step(wave, t0 + u, ncs);
     const int c0 = n_lo + cs * kColStep;
-    load_bfrag<NB, FULL_R>(eb.b[u], bf.b, R, c0, cs < ncs ? n_hi : 0, li, g);
     const int col = c0 + 8 * g;
     const bool cok = cs < ncs && col < n_hi;
 #pragma unroll
@@ -1036,8 +1040,8 @@ __global__ __launch_bounds__(kThreads) void gather_shrink_kernel(
 // Expand: one workgroup per (expert, row slice, column slice of at most
 // kWaves * kTwoSteps column steps). After the routing scan: the rows' partial
 // H (summed over the k ranges in order, scaled and split into hi / lo as in
-// the one-kernel form) and base_out fragments, then the slice's B_e
-// fragments (loaded once, used by every block).
+// the one-kernel form), the slice's B_e fragments (loaded once, used by every
+// block), then the base_out fragments, needed only by the stores.
 constexpr int kMaxKc = 4;
 
 template <int NB, int MB, bool FULL_R>
@@ -1102,6 +1106,7 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(
 #pragma unroll
         for (int q = 0; q < NB; ++q) pv[k][rb][q] = bld16(r_ws, ok ? off + 16u * q : kOOB);
       }
+    if (first) request_b();
     u32x4 ov[kTwoSteps][MB];
 #pragma unroll
     for (int t = 0; t < kTwoSteps; ++t) {
@@ -1112,7 +1117,6 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(
       for (int rb = 0; rb < MB; ++rb)
         ov[t][rb] = bld16_nt(r_out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
     }
-    if (first) request_b();
     __builtin_amdgcn_sched_barrier(0);
     HOp<NB> hop[MB];
 #pragma unroll
@@ -1173,9 +1177,9 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(
 
 // When a wave's whole share of A_e (its k steps) and of B_e (its column steps)
 // fits in registers, A_e is requested together with the routing scan, before
-// any row is known, and B_e right after the first chunk's x and base_out
-// rows. One 16-row block per chunk; the weights serve every chunk of the
-// slice.
+// any row is known, and B_e right after the first chunk's x rows, ahead of
+// its base_out rows. One 16-row block per chunk; the weights serve every
+// chunk of the slice.
 constexpr int kResSteps = 8;  // k steps, and column steps, per wave
 
 // The table pointers and the unit arithmetic come first, as plain arguments:
@@ -1238,9 +1242,9 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
   bf.out = make_buf(p.out, p.out_bytes);
 
   // The wave's weights. A_e is requested now, with the routing; B_e only
-  // after the first chunk's x and base_out rows: it is not needed before the
-  // shrink is done, and requesting it here would hold up the scan behind
-  // three times as many loads.
+  // after the first chunk's x rows: it is not needed before the shrink is
+  // done, and requesting it here would hold up the scan behind three times as
+  // many loads.
   u32x4 av[kResSteps][NB];
 #pragma unroll
   for (int u = 0; u < kResSteps; ++u) {
@@ -1289,12 +1293,6 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
       const int k0 = s * 32 + g * 8;
       xv[u] = bld16(bf.x, (valid && s < nks && k0 < K) ? xoff + 2u * k0 : kOOB);
     }
-#pragma unroll
-    for (int u = 0; u < kResSteps; ++u) {
-      const int cs = col_step(wave, u, ncs);
-      const int col = n_lo + cs * kColStep + 8 * g;
-      ov[u] = bld16(bf.out, (valid && cs < ncs && col < n_hi) ? ooff + 2u * col : kOOB);
-    }
     if (first) {
 #pragma unroll
       for (int u = 0; u < kResSteps; ++u) {
@@ -1302,6 +1300,12 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
         load_bfrag<NB, FULL_R>(bw[u], bf.b, R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li,
                                g);
       }
+    }
+#pragma unroll
+    for (int u = 0; u < kResSteps; ++u) {
+      const int cs = col_step(wave, u, ncs);
+      const int col = n_lo + cs * kColStep + 8 * g;
+      ov[u] = bld16(bf.out, (valid && cs < ncs && col < n_hi) ? ooff + 2u * col : kOOB);
     }
     // shrink
     f32x4 hacc[NB];
