@@ -241,6 +241,11 @@ __device__ __forceinline__ int col_of(int cb, int mi) {
   return (mi >> 2) * 8 + cb * 4 + (mi & 3);
 }
 
+// B_e fragments are requested ahead of a block's base_out rows, so that the
+// expand's MFMAs wait only for them (waits count loads in issue order). For
+// a rank that leaves a partial chunk the words are put together from 16-bit
+// loads, and the compiler waits for those right away; there the callers
+// request base_out first.
 template <int NB, bool FULL_R>
 __device__ __forceinline__ void load_bfrag(BFrag<NB>& f, rsrc_t rb, int R, int c0, int n_hi,
                                            int li, int g) {
@@ -378,20 +383,30 @@ template <int NB, int MB, int UE, bool FULL_R>
 __device__ __forceinline__ void load_expand(ExpandBatch<NB, MB, UE>& eb, const Bufs& bf, int R,
                                             const Rows<MB>& rw, int wave, int t0, int ncs,
                                             int n_lo, int n_hi, int li, int g) {
+  auto request_b = [&]() {
 #pragma unroll
-  for (int u = 0; u < UE; ++u) {
-    const int cs = col_step(wave, t0 + u, ncs);
-    load_bfrag<NB, FULL_R>(eb.b[u], bf.b, R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li, g);
-  }
+    for (int u = 0; u < UE; ++u) {
+      const int cs = col_step(wave, t0 + u, ncs);
+      load_bfrag<NB, FULL_R>(eb.b[u], bf.b, R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li, g);
+    }
+  };
+  auto request_out = [&]() {
 #pragma unroll
-  for (int u = 0; u < UE; ++u) {
-    const int cs = col_step(wave, t0 + u, ncs);
-    const int c0 = n_lo + cs * kColStep;
-    const int col = c0 + 8 * g;
-    const bool cok = cs < ncs && col < n_hi;
+    for (int u = 0; u < UE; ++u) {
+      const int cs = col_step(wave, t0 + u, ncs);
+      const int col = n_lo + cs * kColStep + 8 * g;
+      const bool cok = cs < ncs && col < n_hi;
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
-      eb.o[u][rb] = bld16_nt(bf.out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
+      for (int rb = 0; rb < MB; ++rb)
+        eb.o[u][rb] = bld16_nt(bf.out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
+    }
+  };
+  if constexpr (FULL_R) {
+    request_b();
+    request_out();
+  } else {
+    request_out();
+    request_b();
   }
 }
 
@@ -1106,16 +1121,24 @@ __global__ __launch_bounds__(kThreads) void gather_expand_kernel(
 #pragma unroll
         for (int q = 0; q < NB; ++q) pv[k][rb][q] = bld16(r_ws, ok ? off + 16u * q : kOOB);
       }
-    if (first) request_b();
     u32x4 ov[kTwoSteps][MB];
+    auto request_out = [&]() {
 #pragma unroll
-    for (int t = 0; t < kTwoSteps; ++t) {
-      const int cs = col_step(wave, t, ncs);
-      const int col = n_lo + cs * kColStep + 8 * g;
-      const bool cok = cs < ncs && col < n_hi;
+      for (int t = 0; t < kTwoSteps; ++t) {
+        const int cs = col_step(wave, t, ncs);
+        const int col = n_lo + cs * kColStep + 8 * g;
+        const bool cok = cs < ncs && col < n_hi;
 #pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
-        ov[t][rb] = bld16_nt(r_out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
+        for (int rb = 0; rb < MB; ++rb)
+          ov[t][rb] = bld16_nt(r_out, (rw.valid[rb] && cok) ? rw.ooff[rb] + 2u * col : kOOB);
+      }
+    };
+    if constexpr (FULL_R) {
+      if (first) request_b();
+      request_out();
+    } else {
+      request_out();
+      if (first) request_b();
     }
     __builtin_amdgcn_sched_barrier(0);
     HOp<NB> hop[MB];
@@ -1293,19 +1316,28 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
       const int k0 = s * 32 + g * 8;
       xv[u] = bld16(bf.x, (valid && s < nks && k0 < K) ? xoff + 2u * k0 : kOOB);
     }
-    if (first) {
+    auto request_b = [&]() {
 #pragma unroll
       for (int u = 0; u < kResSteps; ++u) {
         const int cs = col_step(wave, u, ncs);
         load_bfrag<NB, FULL_R>(bw[u], bf.b, R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li,
                                g);
       }
-    }
+    };
+    auto request_out = [&]() {
 #pragma unroll
-    for (int u = 0; u < kResSteps; ++u) {
-      const int cs = col_step(wave, u, ncs);
-      const int col = n_lo + cs * kColStep + 8 * g;
-      ov[u] = bld16(bf.out, (valid && cs < ncs && col < n_hi) ? ooff + 2u * col : kOOB);
+      for (int u = 0; u < kResSteps; ++u) {
+        const int cs = col_step(wave, u, ncs);
+        const int col = n_lo + cs * kColStep + 8 * g;
+        ov[u] = bld16(bf.out, (valid && cs < ncs && col < n_hi) ? ooff + 2u * col : kOOB);
+      }
+    };
+    if constexpr (FULL_R) {
+      if (first) request_b();
+      request_out();
+    } else {
+      request_out();
+      if (first) request_b();
     }
     // shrink
     f32x4 hacc[NB];
@@ -1855,11 +1887,11 @@ __global__ __launch_bounds__(kThreads) void grouped_shrink_kernel(GroupedArgs p)
 }
 
 // Expand: one wave per (16*MB rows, CW column steps). It requests the rows'
-// meta and H', then the B_e fragments of the first run of rows (rows with one
-// B_e) and the rows' base_out, the last in a row-contiguous layout: LPR lanes
-// cover one row's CW*32 columns, 16 bytes each. The MFMA deltas (fp32, one
-// lane per row) go through the wave's own LDS to that layout; each row is
-// then rounded once and stored.
+// meta and H', then the B_e fragments of the first two runs of rows (rows
+// with one B_e) and the rows' base_out, the last in a row-contiguous layout:
+// LPR lanes cover one row's CW*32 columns, 16 bytes each. The MFMA deltas
+// (fp32, one lane per row) go through the wave's own LDS to that layout; each
+// row is then rounded once and stored.
 // LDS floats of one expand wave: its fp32 deltas, one padded row per row.
 template <int MB, int CW>
 struct ExpandSmem {
@@ -1952,24 +1984,39 @@ __device__ __forceinline__ void grouped_expand_unit(const GroupedArgs& p, int u,
       }
     }
   };
-  // The first run's B_e is requested ahead of base_out: waits count loads in
-  // issue order, so its MFMAs and LDS writes then run while base_out is still
-  // on its way (measured 3% faster per call on the 32768-row down projection).
-  BFrag<NB> bw0[CW];
+  // The B_e of the first two runs is requested ahead of base_out: waits count
+  // loads in issue order, so their MFMAs and LDS writes then run while
+  // base_out is still on its way (measured 3% and then another 1.5% faster
+  // per call on the 32768-row down projection). Later runs (a wave meeting
+  // more than two experts) request theirs as they come.
+  BFrag<NB> bw0[CW], bw1[CW];
   const int s0 = __ffsll((unsigned long long)starts) - 1;
   starts &= starts - 1ull;
-  request_b(bw0, s0);
+  const int s1 = starts ? __ffsll((unsigned long long)starts) - 1 : 64;
+  if (starts) starts &= starts - 1ull;
   u32x4 bv[NI];
   uint32_t boff[NI];
+  auto request_out = [&]() {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int col = n_lo + 8 * cc;
-    boff[i] = (uint32_t)(r0 + i * RPI + cr) * (uint32_t)p.N * 2u + 2u * col;
-    const bool ok = col < n_hi && ((live >> (i * RPI + cr)) & 1ull) != 0;
-    bv[i] = bld16_nt(r_out, ok ? boff[i] : kOOB);
+    for (int i = 0; i < NI; ++i) {
+      const int col = n_lo + 8 * cc;
+      boff[i] = (uint32_t)(r0 + i * RPI + cr) * (uint32_t)p.N * 2u + 2u * col;
+      const bool ok = col < n_hi && ((live >> (i * RPI + cr)) & 1ull) != 0;
+      bv[i] = bld16_nt(r_out, ok ? boff[i] : kOOB);
+    }
+  };
+  if constexpr (FULL_R) {
+    request_b(bw0, s0);
+    if (s1 < 64) request_b(bw1, s1);
+    request_out();
+  } else {
+    request_out();
+    request_b(bw0, s0);
+    if (s1 < 64) request_b(bw1, s1);
   }
   __builtin_amdgcn_sched_barrier(0);
-  run(bw0, s0, starts ? __ffsll((unsigned long long)starts) - 1 : 64);
+  run(bw0, s0, s1);
+  if (s1 < 64) run(bw1, s1, starts ? __ffsll((unsigned long long)starts) - 1 : 64);
   while (starts) {
     const int s = __ffsll((unsigned long long)starts) - 1;
     starts &= starts - 1ull;
