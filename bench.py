@@ -324,11 +324,14 @@ PROBE_LIB = os.path.join(ROOT, "moe_expert_lora_amd", "libmlora_probe.so")
 
 def probes():
     """The floors that bound one launch of the fold (libmlora_probe.so, built
-    with the fold library): an empty launch, eager and in a HIP graph; and
-    the read rate of 8192 rows of 4096 bytes (a k_in = 2048 bf16 operand) in
+    with the fold library): an empty launch, eager and in a HIP graph; the
+    read rate of 8192 rows of 4096 bytes (a k_in = 2048 bf16 operand) in
     the folds' MFMA-operand pattern (16 rows x 64 bytes per wave
     instruction) and row-contiguously (1 KB of one row per instruction), at
-    row strides of 4096 bytes (dense rows), 4160 and 8192."""
+    row strides of 4096 bytes (dense rows), 4160 and 8192; and the
+    read-modify-write rate of a 64 MiB bf16 buffer in the grouped expand's
+    wave tile, by rows and by contiguous workgroup blocks, with the units in
+    block order or each XCD on a contiguous eighth, plain or non-temporal."""
     import ctypes
     if not os.path.exists(PROBE_LIB):
         raise SystemExit(f"bench.py: {PROBE_LIB} is missing; build with "
@@ -356,6 +359,24 @@ def probes():
                                 "gbs": useful / (us.value * 1e-6) / 1e9})
             print(json.dumps(out["read"][-1]), file=sys.stderr, flush=True)
     out["read_bytes"] = useful
+    # read-modify-write of a 64 MiB bf16 buffer (one prefill launch group's
+    # base_out), 10 buffers rotated past MALL
+    lib.mlora_probe_rmw.restype = ctypes.c_int32
+    lib.mlora_probe_rmw.argtypes = [ctypes.c_int32] * 5 + [ctypes.POINTER(ctypes.c_float)]
+    rmw_bytes = 2 * 16384 * 4096
+    out["rmw"] = []
+    for name, pattern in (("tile", 0), ("row", 1), ("flat", 2)):
+        for xcdc in (0, 1):
+            for nt in (1, 0):
+                us = ctypes.c_float()
+                rc = lib.mlora_probe_rmw(pattern, xcdc, nt, 10, 40, ctypes.byref(us))
+                if rc:
+                    raise SystemExit(f"bench.py: mlora_probe_rmw failed (HIP error {rc})")
+                out["rmw"].append({"pattern": name, "xcd_contiguous": bool(xcdc),
+                                   "non_temporal": bool(nt), "us": us.value,
+                                   "gbs": rmw_bytes / (us.value * 1e-6) / 1e9})
+                print(json.dumps(out["rmw"][-1]), file=sys.stderr, flush=True)
+    out["rmw_bytes"] = rmw_bytes
     return out
 
 

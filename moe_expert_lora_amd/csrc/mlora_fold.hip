@@ -1468,6 +1468,7 @@ struct GroupedArgs {
   int32_t n_experts, K, N, R, n_route, top_k, n_tokens;
   uint32_t top_k_magic;
   int32_t n_tiles, ns_count, ns_cols, units, per_xcd;  // units = tiles * sub-tiles * ns
+  int32_t expand_xcd;  // expand: 1 each XCD takes a contiguous share of units, 0 block order
   // two-kernel form only: the workspace regions
   uint8_t* ws_h;
   uint64_t* ws_meta;
@@ -2041,19 +2042,22 @@ __device__ __forceinline__ void grouped_expand_unit(const GroupedArgs& p, int u,
   }
 }
 
+// The expand block that launch block b runs: in block order (the hardware
+// deals consecutive blocks to the XCDs in turn, so the column slices of a row
+// block run on different XCDs and each XCD reads only its slices of B_e but
+// every row's H'), or with each XCD on a contiguous share (H' and B_e read by
+// one XCD each). The planner picks (expand_xcd).
+__device__ __forceinline__ int expand_block(const GroupedArgs& p, int b) {
+  return p.expand_xcd ? (b % kXcds) * p.per_xcd + b / kXcds : b;
+}
+
 // Four independent expand waves per workgroup (one wave per workgroup
-// measured 3% slower on the mixed batch). Expand units are dealt to the XCDs
-// in turn (the hardware's own order), so the column slices of a row block
-// run on different XCDs and every XCD's share of base_out is spread over the
-// whole window rather than one contiguous eighth. The read-modify-write
-// stream measured faster that way (a plain 64 MiB one: 24.1 against
-// 26.5 us); each XCD then reads only its column slices of B_e, and H'
-// (4 * R bytes a row) is read by several XCDs.
+// measured 3% slower on the mixed batch).
 template <int NB, int MB, int CW, bool FULL_R>
 __global__ __launch_bounds__(kThreads) void grouped_expand_kernel(GroupedArgs p) {
   __shared__ float s_d[kWaves][ExpandSmem<MB, CW>::kFloats];
   const int wave = threadIdx.x >> 6;
-  const int u = (int)blockIdx.x * kWaves + wave;
+  const int u = expand_block(p, (int)blockIdx.x) * kWaves + wave;
   if (u >= p.units) return;
   grouped_expand_unit<NB, MB, CW, FULL_R>(p, u, s_d[wave]);
 }
@@ -2077,10 +2081,10 @@ __global__ __launch_bounds__(kThreads) void grouped_pipe_kernel(GroupedArgs ps, 
     if (u < ps.units) grouped_shrink_unit<NB, SMB, 1>(ps, u, sm.s);
     return;
   }
-  // expand waves in block order, as in the expand kernel
+  // sblocks is a multiple of kXcds, so b keeps the block's XCD
   const int b = (int)blockIdx.x - sblocks;
   const int wave = threadIdx.x >> 6;
-  const int u = b * kWaves + wave;
+  const int u = expand_block(pe, b) * kWaves + wave;
   if (u < pe.units) grouped_expand_unit<NB, EMB, CW, FULL_R>(pe, u, sm.d[wave]);
 }
 
@@ -2160,7 +2164,7 @@ __global__ __launch_bounds__(kThreads) void rowwise_f32_kernel(RowwiseArgs p) {
 struct Overrides {
   int gather_rs, gather_ns, gather_small, gather_resident, gather_two, gather_two_ns;
   int gather_dense;
-  int grouped_mb, grouped_ns, shrink_mb, expand_mb, expand_cw, all_min_rows;
+  int grouped_mb, grouped_ns, shrink_mb, expand_mb, expand_cw, expand_xcd, all_min_rows;
 };
 constexpr int kUnset = -0x7fffffff;
 
@@ -2184,6 +2188,7 @@ Overrides read_overrides() {
   o.shrink_mb = read_env("MLORA_SHRINK_MB");
   o.expand_mb = read_env("MLORA_EXPAND_MB");
   o.expand_cw = read_env("MLORA_EXPAND_CW");
+  o.expand_xcd = read_env("MLORA_EXPAND_XCD");
   o.all_min_rows = read_env("MLORA_ALL_MIN_ROWS");
   return o;
 }
@@ -2891,6 +2896,26 @@ int expand_cw(int R, int requested) {
   return (R == 16 * nb && nb <= 2 && requested >= 4) ? 4 : 2;
 }
 
+// How expand units meet the XCDs. In block order every XCD reads the H'
+// (4 * R bytes) of every row, eight reads where one would do, and its
+// read-modify-write of base_out runs beside the other XCDs' on the same rows;
+// with contiguous shares each row's H' is read once. Block order where the
+// extra H' reads stay under 1/8 of base_out's bytes (8 * 4R <= 2N / 8): it
+// measured 2-3% faster per call on n_out = 4096, rank 16, and contiguous
+// shares 3.5% faster on n_out = 2048, rank 32.
+int expand_xcd(int R, int N) {
+  const int v = ov(overrides().expand_xcd, N < 128 * R ? 1 : 0);
+  return v ? 1 : 0;
+}
+
+// Grid of the expand kernel (four waves a block) over a.units units.
+int64_t expand_grid(GroupedArgs& a) {
+  const int64_t blocks = ((int64_t)a.units + kWaves - 1) / kWaves;
+  a.per_xcd = (int32_t)((blocks + kXcds - 1) / kXcds);
+  a.expand_xcd = expand_xcd(a.R, a.N);
+  return (int64_t)a.per_xcd * kXcds;
+}
+
 template <int NB, int MB>
 void launch_expand(const GroupedArgs& a, int grid, hipStream_t s, int cw) {
   const bool full = a.R == 16 * NB;
@@ -3137,8 +3162,8 @@ extern "C" int32_t mlora_grouped_down(const mlora_expert_route* route, const voi
     if (int32_t rc = launched(who)) return rc;
     a.ns_count = (int32_t)t.eslices;
     a.units = (int32_t)(t.etiles * t.eslices);
-    a.per_xcd = (int32_t)((a.units + kXcds - 1) / kXcds);
-    dispatch_expand(a, (a.units + kWaves - 1) / kWaves, s, t.emb, t.cw);
+    const int64_t eg = expand_grid(a);
+    dispatch_expand(a, (int)eg, s, t.emb, t.cw);
     return launched(who);
   }
 
@@ -3409,15 +3434,13 @@ static int32_t grouped_down_all_impl(const mlora_expert_route* route, const void
     int64_t sb = 0, eb = 0;
     const GroupedArgs ps = window(w, false, &sb);
     GroupedArgs pe = window(w - 1, true, &eb);
-    pe.per_xcd = (int32_t)((eb + kXcds - 1) / kXcds);  // expand blocks per XCD
-    const int64_t grid = sb + (int64_t)pe.per_xcd * kXcds;
+    const int64_t grid = sb + expand_grid(pe);  // eb expand blocks, per_xcd * kXcds >= eb
     dispatch_pipe(ps, pe, (int)grid, s, emb, cw);
     if (int32_t rc = launched(who)) return rc;
   }
   int64_t lb = 0;
   GroupedArgs last = window(n_win - 1, true, &lb);
-  last.per_xcd = (int32_t)((last.units + kXcds - 1) / kXcds);
-  dispatch_expand(last, (last.units + kWaves - 1) / kWaves, s, emb, cw);
+  dispatch_expand(last, (int)expand_grid(last), s, emb, cw);
   return launched(who);
 }
 

@@ -10,6 +10,14 @@
 //                          step pairs completing 128-byte lines) or one row's
 //                          1 KB per wave instruction, buffers rotated past
 //                          L2 and MALL.
+//   mlora_probe_rmw        read-modify-write rate of a 16384 x 2048 bf16
+//                          buffer (64 MiB, the base_out of one prefill launch
+//                          group) in the grouped expand's wave tile (32 rows x
+//                          128 columns, 4 rows x 256 bytes per instruction),
+//                          one row's 1 KB per instruction, or a workgroup's
+//                          contiguous 32 KB; units in the hardware's block
+//                          order or each XCD on a contiguous eighth; plain or
+//                          non-temporal loads and stores.
 //
 // Each entry point allocates and frees its own buffers, synchronizes the
 // device and returns 0, or a HIP error code.
@@ -69,6 +77,57 @@ __global__ __launch_bounds__(kThreads) void read_rows_kernel(const char* x, unsi
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc ^= v[i];
   sink[blockIdx.x * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// Read-modify-write probes: every 16-byte piece of the buffer gets one added
+// to each word. 8192 wave units of 32 rows x 128 columns (tile) or 2 rows
+// (row), four per 256-thread workgroup, or 2048 workgroups of a contiguous
+// 32 KB each (flat): 2048 workgroups in every pattern.
+constexpr int kRmwRows = 16384;
+constexpr int kRmwRowBytes = 4096;
+constexpr uint32_t kRmwBytes = (uint32_t)kRmwRows * kRmwRowBytes;
+constexpr int kRmwUnits = 8192;
+constexpr int kRmwBlocks = kRmwUnits / 4;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t rmw_buf(char* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)kRmwBytes, 0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4 rmw_ld(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ void rmw_st(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, AUX);
+}
+
+// PATTERN 0 tile, 1 row, 2 flat; XCDC: block b's XCD (b % 8) takes units of
+// its own contiguous eighth; AUX 0 plain, 2 non-temporal.
+template <int PATTERN, bool XCDC, int AUX>
+__global__ __launch_bounds__(256) void rmw_kernel(char* buf) {
+  const rsrc_t r = rmw_buf(buf);
+  const int b = blockIdx.x, w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int blk = XCDC ? (b % 8) * (kRmwBlocks / 8) + b / 8 : b;
+  const int u = blk * 4 + w;
+  uint32_t off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (PATTERN == 0) {  // rows 32*(u/16) .., columns 128*(u%16) ..
+      const int row = (u >> 4) * 32 + i * 4 + (l >> 4);
+      off[i] = (uint32_t)row * kRmwRowBytes + (uint32_t)((u & 15) * 128 + 8 * (l & 15)) * 2u;
+    } else if constexpr (PATTERN == 1) {  // rows 2u, 2u+1, 1 KB per instruction
+      off[i] = (uint32_t)(2 * u + (i >> 2)) * kRmwRowBytes + (uint32_t)(i & 3) * 1024u + 16u * l;
+    } else {  // 32 KB from 32 KB * blk, 4 KB per workgroup instruction
+      off[i] = (uint32_t)blk * 32768u + (uint32_t)i * 4096u + (uint32_t)threadIdx.x * 16u;
+    }
+  }
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = rmw_ld<AUX>(r, off[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rmw_st<AUX>(r, off[i], v[i] + u32x4{1u, 1u, 1u, 1u});
 }
 
 // The first failing call's code is kept; later calls are skipped.
@@ -181,5 +240,55 @@ extern "C" int32_t mlora_probe_read(int32_t pattern, int32_t stride, int32_t cop
   for (char* b : bufs)
     if (b) (void)hipFree(b);
   if (sink) (void)hipFree(sink);
+  return (int32_t)st.rc;
+}
+
+// pattern 0 tile / 1 row / 2 flat; xcd_contiguous 0 or 1; nt 0 or 1; us: mean
+// microseconds per launch over `iters` launches rotating over `copies`
+// buffers of 64 MiB (1 .. 16).
+extern "C" int32_t mlora_probe_rmw(int32_t pattern, int32_t xcd_contiguous, int32_t nt,
+                                   int32_t copies, int32_t iters, float* us) {
+  if (pattern < 0 || pattern > 2 || (xcd_contiguous != 0 && xcd_contiguous != 1) ||
+      (nt != 0 && nt != 1) || copies < 1 || copies > 16 || iters < 1 || !us)
+    return (int32_t)hipErrorInvalidValue;
+  std::vector<char*> bufs(copies, nullptr);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  Status st;
+  for (int i = 0; st.ok() && i < copies; ++i) {
+    st(hipMalloc(&bufs[i], kRmwBytes));
+    if (st.ok()) st(hipMemset(bufs[i], 0, kRmwBytes));
+  }
+  if (st.ok()) st(hipEventCreate(&e0));
+  if (st.ok()) st(hipEventCreate(&e1));
+  if (st.ok()) {
+    using K = void (*)(char*);
+    static const K kernels[3][2][2] = {
+        {{rmw_kernel<0, false, 0>, rmw_kernel<0, false, 2>},
+         {rmw_kernel<0, true, 0>, rmw_kernel<0, true, 2>}},
+        {{rmw_kernel<1, false, 0>, rmw_kernel<1, false, 2>},
+         {rmw_kernel<1, true, 0>, rmw_kernel<1, true, 2>}},
+        {{rmw_kernel<2, false, 0>, rmw_kernel<2, false, 2>},
+         {rmw_kernel<2, true, 0>, rmw_kernel<2, true, 2>}}};
+    const K k = kernels[pattern][xcd_contiguous][nt];
+    auto launch = [&](int i) {
+      hipLaunchKernelGGL(k, dim3(kRmwBlocks), dim3(256), 0, 0, bufs[i % copies]);
+    };
+    for (int i = 0; i < 2 * copies; ++i) launch(i);
+    st(hipDeviceSynchronize());
+    float ms = 0.f;
+    if (st.ok()) {
+      st(hipEventRecord(e0, 0));
+      for (int i = 0; i < iters; ++i) launch(i);
+      st(hipEventRecord(e1, 0));
+      st(hipEventSynchronize(e1));
+      st(hipEventElapsedTime(&ms, e0, e1));
+      *us = ms * 1e3f / (float)iters;
+    }
+  }
+  st(hipGetLastError());
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  for (char* b : bufs)
+    if (b) (void)hipFree(b);
   return (int32_t)st.rc;
 }

@@ -189,8 +189,9 @@ def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
-    """libmlora_probe.so (bench.py --probes) exports both probes, and each
-    rejects invalid arguments before any device call (so this runs on CPU)."""
+    """libmlora_probe.so (bench.py --probes) exports its three probes, and
+    each rejects invalid arguments before any device call (so this runs on
+    CPU)."""
     import ctypes
     lib = ctypes.CDLL(bench.PROBE_LIB)
     lib.mlora_probe_empty.restype = ctypes.c_int32
@@ -205,3 +206,9 @@ def test_probe_library_exports_and_rejects_bad_arguments():
                  (1, 4096, 0, 10), (1, 4096, 33, 10), (1, 4096, 12, 0)):
         assert lib.mlora_probe_read(*args, ctypes.byref(us)) != 0, args
     assert lib.mlora_probe_read(0, 4096, 12, 10, None) != 0
+    lib.mlora_probe_rmw.restype = ctypes.c_int32
+    lib.mlora_probe_rmw.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p]
+    for args in ((3, 0, 0, 10, 10), (-1, 0, 0, 10, 10), (0, 2, 0, 10, 10), (0, 0, 2, 10, 10),
+                 (0, 0, 0, 0, 10), (0, 0, 0, 17, 10), (0, 0, 0, 10, 0)):
+        assert lib.mlora_probe_rmw(*args, ctypes.byref(us)) != 0, args
+    assert lib.mlora_probe_rmw(0, 0, 0, 10, 10, None) != 0

@@ -4,7 +4,8 @@ Each case draws its sizes from its seed (k_in and n_out multiples of 8 from
 8 up; ranks 1 to 128; top_k 1 to 8; routes of 1 to 40 experts, one-entry
 routes included; skipped, refused and wild-index rows; slot counts that are
 not a multiple of top_k; grouped windows from a few rows up) and is folded by
-the default form and by every form the overrides can force; multi-adapter
+the default form and by every form the overrides can force (the grouped
+expand's two unit orders must give the same bits); multi-adapter
 cases add adapter counts, uninstalled slots and partly adapted slots. Every
 result must meet the oracle bound, and every row that folds nothing must keep
 its bits.
@@ -110,7 +111,7 @@ def test_gather_sweep_every_form(seed, overrides):
 
 
 @pytest.mark.parametrize("seed", GROUPED_SEEDS)
-def test_grouped_sweep_every_form(seed):
+def test_grouped_sweep_every_form(seed, overrides):
     _need_gpu()
     from staging import DeviceCase
     case = grouped_case(seed)
@@ -121,6 +122,14 @@ def test_grouped_sweep_every_form(seed):
                       ("one kernel", dict(two_kernel=False, pipelined=False)),
                       ("all windows", dict(two_kernel=True, pipelined=True))):
         check(view, dev.run(**kw), case.base, f"{case.name} {label}", windows=windows)
+    # the expand units in block order and in contiguous XCD shares: the same bits
+    forced = []
+    for xcd in (0, 1):
+        overrides.set("MLORA_EXPAND_XCD", xcd)
+        forced.append(dev.run(two_kernel=True, pipelined=True))
+    overrides.delete("MLORA_EXPAND_XCD")
+    check(view, forced[0], case.base, f"{case.name} expand units in block order", windows=windows)
+    assert np.array_equal(forced[0].view(np.uint16), forced[1].view(np.uint16))
     _sentinel_run(view, dev, case, two_kernel=True, pipelined=True)
 
 
