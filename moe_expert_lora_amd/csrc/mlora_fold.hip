@@ -2896,23 +2896,26 @@ int expand_cw(int R, int requested) {
   return (R == 16 * nb && nb <= 2 && requested >= 4) ? 4 : 2;
 }
 
-// How expand units meet the XCDs. In block order every XCD reads the H'
-// (4 * R bytes) of every row, eight reads where one would do, and its
-// read-modify-write of base_out runs beside the other XCDs' on the same rows;
-// with contiguous shares each row's H' is read once. Block order where the
-// extra H' reads stay under 1/8 of base_out's bytes (8 * 4R <= 2N / 8): it
-// measured 2-3% faster per call on n_out = 4096, rank 16, and contiguous
-// shares 3.5% faster on n_out = 2048, rank 32.
-int expand_xcd(int R, int N) {
-  const int v = ov(overrides().expand_xcd, N < 128 * R ? 1 : 0);
+// How expand units meet the XCDs. In block order the column units of a row
+// block go to the XCDs in turn: all XCDs work on the same rows at once, and
+// every XCD reads the H' (4 * R bytes) of every row. With contiguous shares
+// each XCD works through its own eighth of the window and each row's H' is
+// read once. Measured on 32768-row prefill batches (all windows, µs per
+// call), block order won where a row block splits into more than 16 column
+// units (n_out 4096 at ranks 16 and 32, n_out 2048 at rank 64 with its
+// 64-column waves: 2-3%) and contiguous shares won at 16 or fewer (n_out 2048
+// at ranks 16 and 32, n_out 1024: 1-3.5%).
+int expand_xcd(int ns_count) {
+  const int v = ov(overrides().expand_xcd, ns_count <= 16 ? 1 : 0);
   return v ? 1 : 0;
 }
 
-// Grid of the expand kernel (four waves a block) over a.units units.
+// Grid of the expand kernel (four waves a block) over a.units units, with
+// a.ns_count already set.
 int64_t expand_grid(GroupedArgs& a) {
   const int64_t blocks = ((int64_t)a.units + kWaves - 1) / kWaves;
   a.per_xcd = (int32_t)((blocks + kXcds - 1) / kXcds);
-  a.expand_xcd = expand_xcd(a.R, a.N);
+  a.expand_xcd = expand_xcd(a.ns_count);
   return (int64_t)a.per_xcd * kXcds;
 }
 

@@ -682,8 +682,8 @@ def test_graph_replay_reads_routing_on_device():
     check(view, from_torch(base), c.base, "graph replay, new routing")
 
 
-@pytest.mark.parametrize("form", ["grouped_all", "grouped_all_per_window", "grouped_window",
-                                  "gather_two"])
+@pytest.mark.parametrize("form", ["grouped_all", "grouped_all_per_window",
+                                  "grouped_all_block_order", "grouped_window", "gather_two"])
 def test_graph_replay_workspace_forms(form, overrides):
     """The workspace forms captured in a HIP graph: every replay (with eager
     work and syncs between) equals the eager fold bit for bit, and a replay
@@ -705,6 +705,10 @@ def test_graph_replay_workspace_forms(form, overrides):
         if form == "grouped_all_per_window":
             # one window per launch: the pipe kernel runs inside the graph
             overrides.set("MLORA_ALL_MIN_ROWS", "1")
+        if form == "grouped_all_block_order":
+            # expand units in block order (this shape's plan takes XCD shares)
+            overrides.set("MLORA_ALL_MIN_ROWS", "1")
+            overrides.set("MLORA_EXPAND_XCD", "0")
         dev = DeviceCase(c, DEV, pipelined=form.startswith("grouped_all"))
         assert len(dev.windows) > 1
     dev.workspace_for(getattr(dev, "windows", None))   # allocated before capture
