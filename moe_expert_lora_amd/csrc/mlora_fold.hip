@@ -242,10 +242,12 @@ __device__ __forceinline__ int col_of(int cb, int mi) {
 }
 
 // B_e fragments are requested ahead of a block's base_out rows, so that the
-// expand's MFMAs wait only for them (waits count loads in issue order). For
-// a rank that leaves a partial chunk the words are put together from 16-bit
-// loads, and the compiler waits for those right away; there the callers
-// request base_out first.
+// expand's MFMAs wait only for them (waits count loads in issue order).
+// FULL_R: the rank is a multiple of the chunk (whole_chunks), so each lane's
+// chunk of a B_e row lies wholly inside the row (one 8- or 16-byte load, its
+// offset a multiple of the load size) or wholly past the rank (not read, 0).
+// Otherwise the words are put together from 16-bit loads, and the compiler
+// waits for those right away; there the callers request base_out first.
 template <int NB, bool FULL_R>
 __device__ __forceinline__ void load_bfrag(BFrag<NB>& f, rsrc_t rb, int R, int c0, int n_hi,
                                            int li, int g) {
@@ -259,12 +261,13 @@ __device__ __forceinline__ void load_bfrag(BFrag<NB>& f, rsrc_t rb, int R, int c
       const int r0 = g * 4 * NB + q * CR;  // first rank of the chunk
       const uint32_t base = (uint32_t)(col * R + r0) * 2u;
       if constexpr (FULL_R) {
+        const bool in = ok && r0 < R;
         if constexpr (CW == 2) {
-          const u32x2 v = bld8(rb, ok ? base : kOOB);
+          const u32x2 v = bld8(rb, in ? base : kOOB);
           f.w[cb][q][0] = v.x;
           f.w[cb][q][1] = v.y;
         } else {
-          const u32x4 v = bld16(rb, ok ? base : kOOB);
+          const u32x4 v = bld16(rb, in ? base : kOOB);
           f.w[cb][q][0] = v.x;
           f.w[cb][q][1] = v.y;
           f.w[cb][q][2] = v.z;
@@ -2206,6 +2209,11 @@ int ov(int v, int dflt) { return v == kUnset ? dflt : v; }
 
 uint32_t magic_for(int32_t d) { return (uint32_t)(0xFFFFFFFFu / (uint32_t)d); }
 
+// A rank whose B_e rows load as whole lane chunks (the kernels' FULL_R form):
+// a multiple of a lane's chunk of ranks, 4 for ranks up to 16 (one rank
+// block), else 8.
+bool whole_chunks(int R) { return R % (R <= 16 ? 4 : 8) == 0; }
+
 int32_t check_route(const mlora_expert_route* r, const char* who) {
   if (!r) return fail(MLORA_ERR_INVALID, "%s: NULL route", who);
   if (r->n_experts < 0) return fail(MLORA_ERR_INVALID, "%s: n_experts < 0", who);
@@ -2250,7 +2258,7 @@ int ns_cols_for(int N, int ns) {
 
 template <int NB, int MB>
 void launch_gather(const GatherArgs& a, int grid, hipStream_t s) {
-  if (a.R == 16 * NB)
+  if (whole_chunks(a.R))
     hipLaunchKernelGGL((gather_fold_kernel<NB, MB, true>), dim3(grid), dim3(kThreads), 0, s,
                        LEAD_ARGS(a, a.ns_count));
   else
@@ -2313,7 +2321,7 @@ template <int NB, int MB>
 void launch_gather_two(const GatherArgs& g1, const GatherArgs& g2, hipStream_t s) {
   hipLaunchKernelGGL((gather_shrink_kernel<NB, MB>), dim3(g1.per_xcd * kXcds), dim3(kThreads), 0,
                      s, LEAD_ARGS(g1, g1.kc_count));
-  if (g2.R == 16 * NB)
+  if (whole_chunks(g2.R))
     hipLaunchKernelGGL((gather_expand_kernel<NB, MB, true>), dim3(g2.per_xcd * kXcds),
                        dim3(kThreads), 0, s, LEAD_ARGS(g2, g2.ns_count));
   else
@@ -2349,7 +2357,7 @@ void launch_resident(const GatherArgs& a, int grid, hipStream_t s) {
 
 template <int NB, int MB>
 void launch_dense(const GatherArgs& a, int grid, hipStream_t s) {
-  if (a.R == 16 * NB)
+  if (whole_chunks(a.R))
     hipLaunchKernelGGL((gather_dense_kernel<NB, MB, true>), dim3(grid), dim3(kThreads), 0, s,
                        LEAD_ARGS(a, a.ns_count));
   else
@@ -2389,7 +2397,7 @@ void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small, b
 
 template <int NB, int MB>
 void launch_grouped(const GroupedArgs& a, int grid, hipStream_t s) {
-  if (a.R == 16 * NB)
+  if (whole_chunks(a.R))
     hipLaunchKernelGGL((grouped_fold_kernel<NB, MB, true>), dim3(grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((grouped_fold_kernel<NB, MB, false>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -2738,7 +2746,7 @@ extern "C" int32_t mlora_gather_bgmv_set(const mlora_projection* projs, int32_t 
     plans[i] = plan;
     ++members;
     only = i;
-    full = full && r->max_rank == 16 * nb;
+    full = full && whole_chunks(r->max_rank);
     small = small && plan.small != 0;
     total += plan.a.units;
     if (total > 0x3fffffffll) return fail(MLORA_ERR_INVALID, "%s: launch too large", who);
@@ -2774,7 +2782,7 @@ namespace {
 
 template <int NB, int MB>
 void launch_gather_multi(const GatherArgs& a, int grid, hipStream_t s) {
-  if (a.R == 16 * NB)
+  if (whole_chunks(a.R))
     hipLaunchKernelGGL((gather_fold_kernel<NB, MB, true, true>), dim3(grid), dim3(kThreads), 0,
                        s, LEAD_ARGS(a, a.ns_count));
   else
@@ -2889,11 +2897,11 @@ void dispatch_shrink(const GroupedArgs& a, int grid, hipStream_t s, int mb) {
   else launch_shrink<8>(a, grid, s, 1);
 }
 
-// Column steps per expand wave: 4 where the operands leave room (full rank
-// blocks of at most 32 ranks), else 2.
+// Column steps per expand wave: 4 where the operands leave room (ranks of
+// whole lane chunks, at most 32), else 2.
 int expand_cw(int R, int requested) {
   const int nb = (R + 15) / 16;
-  return (R == 16 * nb && nb <= 2 && requested >= 4) ? 4 : 2;
+  return (whole_chunks(R) && nb <= 2 && requested >= 4) ? 4 : 2;
 }
 
 // How expand units meet the XCDs. In block order the column units of a row
@@ -2921,7 +2929,7 @@ int64_t expand_grid(GroupedArgs& a) {
 
 template <int NB, int MB>
 void launch_expand(const GroupedArgs& a, int grid, hipStream_t s, int cw) {
-  const bool full = a.R == 16 * NB;
+  const bool full = whole_chunks(a.R);
   if (!full) {
     hipLaunchKernelGGL((grouped_expand_kernel<NB, MB, 2, false>), dim3(grid), dim3(kThreads), 0, s, a);
   } else if constexpr (NB <= 2) {
@@ -2965,16 +2973,19 @@ struct TwoPlan {
 TwoPlan two_plan(int R, int N, int64_t rows, bool pipe) {
   TwoPlan t;
   // two expand row blocks per wave share each B_e fragment where the rank
-  // blocks are full and at most 32 ranks (measured 4% faster per window)
-  const bool small_full = R == 16 * kernel_nb(R) && kernel_nb(R) <= 2;
-  // 64-row shrink tiles for at most 32 ranks: A_e is read once per 64 rows
-  // (measured 3.5% faster per call than 32-row tiles, 15% than 16-row ones)
-  t.smb = kernel_nb(R) <= 2 ? 4 : 1;
+  // has whole lane chunks and is at most 64 (measured 4% faster per window
+  // at rank 32)
+  const bool small_full = whole_chunks(R) && kernel_nb(R) <= 4;
+  // shrink tiles of 64 rows for at most 32 ranks, 32 rows for at most 64: A_e
+  // is read once per tile (at rank 32, 64-row tiles measured 3.5% faster per
+  // call than 32-row ones and 15% than 16-row ones; at rank 64, 32-row tiles
+  // with 32-row expand waves 23% faster than 16-row ones)
+  t.smb = kernel_nb(R) <= 2 ? 4 : (kernel_nb(R) <= 4 ? 2 : 1);
   t.emb = expand_mb(R, ov(overrides().expand_mb, small_full ? 2 : 1));
   t.cw = expand_cw(R, ov(overrides().expand_cw, 4));
   if (pipe) {
-    // the pipe kernel takes 1 expand row block, or 2 for full rank blocks of
-    // at most 32 ranks, and always its default shrink tile
+    // the pipe kernel takes 1 expand row block, or 2 for ranks of whole lane
+    // chunks up to 64, and always its default shrink tile
     t.emb = (t.emb >= 2 && small_full) ? 2 : 1;
   } else {
     const int w = ov(overrides().shrink_mb, t.smb);
@@ -2996,14 +3007,16 @@ void launch_pipe(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipStre
 template <int NB>
 void dispatch_pipe_nb(const GroupedArgs& ps, const GroupedArgs& pe, int grid, hipStream_t s,
                       int emb, int cw) {
-  constexpr int SMB = NB <= 2 ? 4 : 1;
-  if (ps.R != 16 * NB) return launch_pipe<NB, SMB, 1, 2, false>(ps, pe, grid, s);
+  constexpr int SMB = NB <= 2 ? 4 : (NB <= 4 ? 2 : 1);
+  if (!whole_chunks(ps.R)) return launch_pipe<NB, SMB, 1, 2, false>(ps, pe, grid, s);
   if constexpr (NB <= 2) {
     if (emb >= 2) {
       if (cw >= 4) return launch_pipe<NB, SMB, 2, 4, true>(ps, pe, grid, s);
       return launch_pipe<NB, SMB, 2, 2, true>(ps, pe, grid, s);
     }
     if (cw >= 4) return launch_pipe<NB, SMB, 1, 4, true>(ps, pe, grid, s);
+  } else if constexpr (NB <= 4) {
+    if (emb >= 2) return launch_pipe<NB, SMB, 2, 2, true>(ps, pe, grid, s);
   }
   launch_pipe<NB, SMB, 1, 2, true>(ps, pe, grid, s);
 }
