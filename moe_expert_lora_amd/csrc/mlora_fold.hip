@@ -2376,10 +2376,10 @@ void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small, b
   }
   if (resident && gather_resident_fits(a)) {
     if (nb <= 1) {
-      if (a.R == 16) launch_resident<1, true>(a, grid, s);
+      if (whole_chunks(a.R)) launch_resident<1, true>(a, grid, s);
       else launch_resident<1, false>(a, grid, s);
     } else {
-      if (a.R == 32) launch_resident<2, true>(a, grid, s);
+      if (whole_chunks(a.R)) launch_resident<2, true>(a, grid, s);
       else launch_resident<2, false>(a, grid, s);
     }
     return;
