@@ -262,6 +262,8 @@ SMALL = [
                             k_in=72, n_out=104, max_rank=24, n_adapted=10, dup_frac=0.3)),
     ("gather_r48", dict(kind="gather", n_seq=64, padded_n=70, top_k=4, n_route=6, k_in=200,
                         n_out=136, max_rank=48, skip_seqs=5)),
+    ("gather_r17_decode", dict(kind="gather", n_seq=30, padded_n=32, top_k=8, n_route=24,
+                               k_in=256, n_out=200, max_rank=17, skip_seqs=2, n_adapted=20)),
     ("gather_r100", dict(kind="gather", n_seq=37, padded_n=40, top_k=2, n_route=5, k_in=264,
                          n_out=520, max_rank=100)),
     ("gather_r128", dict(kind="gather", n_seq=33, padded_n=33, top_k=3, n_route=4, k_in=128,
@@ -553,7 +555,7 @@ def test_grouped_workspace_reused_across_windows_and_calls():
 
 
 @pytest.mark.parametrize("label", ["decode_down_gather", "gather_r24_k72", "gather_slots_not_multiple",
-                                   "gather_r16_ns4"])
+                                   "gather_r16_ns4", "gather_ragged_r8", "gather_r17_decode"])
 def test_resident_weights_path_equals_streaming_path(label, overrides):
     """The decode path that holds a wave's weights in registers and the
     streaming path fold in the same order: outputs equal bit for bit, and the

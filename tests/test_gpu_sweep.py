@@ -21,8 +21,8 @@ from tests.test_gpu_fold import DEV, _need_gpu, check
 
 pytestmark = pytest.mark.gpu
 
-GATHER_SEEDS = list(range(24))
-GROUPED_SEEDS = list(range(12))
+GATHER_SEEDS = list(range(32))
+GROUPED_SEEDS = list(range(16))
 
 # forced gather forms: (label, overrides, run with a workspace)
 GATHER_FORMS = [
@@ -46,7 +46,7 @@ def gather_case(seed):
     padded_n = n_seq + int(rng.integers(0, 9))
     k_in = 8 * int(rng.integers(1, 263))
     n_out = 8 * int(rng.integers(1, 138))
-    max_rank = int(rng.choice([1, 3, 8, 12, 16, 17, 24, 32, 40, 64, 100, 128]))
+    max_rank = int(rng.choice([1, 3, 8, 12, 16, 17, 24, 32, 40, 56, 64, 72, 96, 100, 128]))
     kw = dict(n_seq=n_seq, padded_n=padded_n, top_k=top_k, n_route=n_route, k_in=k_in,
               n_out=n_out, max_rank=max_rank, skip_seqs=int(rng.integers(0, max(1, n_seq // 4))),
               name=f"sweep_gather_{seed}")
@@ -72,7 +72,7 @@ def grouped_case(seed):
     n_route = int(rng.integers(top_k, top_k + 30))
     kw = dict(stream_lens=lens, top_k=top_k, n_route=n_route,
               k_in=8 * int(rng.integers(1, 200)), n_out=8 * int(rng.integers(1, 140)),
-              max_rank=int(rng.choice([1, 5, 16, 24, 32, 48, 64, 128])),
+              max_rank=int(rng.choice([1, 5, 8, 16, 24, 32, 40, 48, 56, 64, 96, 128])),
               routing=str(rng.choice(["uniform", "zipf"])),
               n_unadapted=int(rng.integers(0, n_route // 2 + 1)),
               dup_frac=float(rng.choice([0.0, 0.2])),
