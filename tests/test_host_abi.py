@@ -375,7 +375,8 @@ def test_grouped_all_workspace_bytes_covers_every_override(lib, overrides, n_row
                                                            max_rank):
     """The size query reads no environment and covers the call under every
     launch minimum (MLORA_ALL_MIN_ROWS, clamped to 1 .. 16384 by the call):
-    the largest of those needs is exactly the queried size."""
+    the largest of those needs is exactly the queried size; the tile and
+    unit-order overrides change neither."""
     query = lib.mlora_grouped_down_all_workspace_bytes(n_rows, cap, max_rank)
     needs = []
     n_caps = -(-n_rows // cap)
@@ -388,6 +389,16 @@ def test_grouped_all_workspace_bytes_covers_every_override(lib, overrides, n_row
         assert lib.mlora_grouped_down_all_workspace_bytes(n_rows, cap, max_rank) == query
         needs.append(_all_needed(lib, n_rows, cap, max_rank))
     assert max(needs) == query
+    # the tile and unit-order overrides change neither the query nor the need
+    overrides.delete("MLORA_ALL_MIN_ROWS")
+    base_need = _all_needed(lib, n_rows, cap, max_rank)
+    for name, values in (("MLORA_EXPAND_XCD", (0, 1)), ("MLORA_EXPAND_MB", (1, 2, 4)),
+                         ("MLORA_EXPAND_CW", (2, 4)), ("MLORA_SHRINK_MB", (1, 2, 4))):
+        for v in values:
+            overrides.set(name, v)
+            assert lib.mlora_grouped_down_all_workspace_bytes(n_rows, cap, max_rank) == query
+            assert _all_needed(lib, n_rows, cap, max_rank) == base_need
+        overrides.delete(name)
 
 
 def test_noalloc_rejects_calls_beyond_its_scratch(lib):
