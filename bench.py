@@ -331,7 +331,10 @@ def probes():
     row strides of 4096 bytes (dense rows), 4160 and 8192; and the
     read-modify-write rate of a 64 MiB bf16 buffer in the grouped expand's
     wave tile, by rows and by contiguous workgroup blocks, with the units in
-    block order or each XCD on a contiguous eighth, plain or non-temporal."""
+    block order or each XCD on a contiguous eighth, plain or non-temporal;
+    and launches shaped like the decode fold (192 or 256 workgroups, each
+    streaming its own weights and read-modify-writing its own rows, no
+    dependent load), replayed in a HIP graph: the floor of one such launch."""
     import ctypes
     if not os.path.exists(PROBE_LIB):
         raise SystemExit(f"bench.py: {PROBE_LIB} is missing; build with "
@@ -377,6 +380,22 @@ def probes():
                                    "gbs": rmw_bytes / (us.value * 1e-6) / 1e9})
                 print(json.dumps(out["rmw"][-1]), file=sys.stderr, flush=True)
     out["rmw_bytes"] = rmw_bytes
+    # launches shaped like the decode fold with no dependent load: each
+    # workgroup reads its own weight bytes and reads-modifies-writes its own
+    # rows; 64 buffer sets rotated (>= 640 MB), replayed in a HIP graph
+    lib.mlora_probe_stream.restype = ctypes.c_int32
+    lib.mlora_probe_stream.argtypes = [ctypes.c_int32] * 5 + [ctypes.POINTER(ctypes.c_float)]
+    out["stream"] = []
+    for units, w_kb, r_kb in ((192, 44, 8), (256, 32, 8), (192, 0, 0)):
+        us = ctypes.c_float()
+        rc = lib.mlora_probe_stream(units, w_kb, r_kb, 64, 256, ctypes.byref(us))
+        if rc:
+            raise SystemExit(f"bench.py: mlora_probe_stream failed (HIP error {rc})")
+        moved = units * (w_kb + 2 * r_kb) * 1024
+        out["stream"].append({"workgroups": units, "weight_kb": w_kb, "row_kb_rmw": r_kb,
+                              "bytes": moved, "us": us.value,
+                              "gbs": moved / (us.value * 1e-6) / 1e9})
+        print(json.dumps(out["stream"][-1]), file=sys.stderr, flush=True)
     return out
 
 

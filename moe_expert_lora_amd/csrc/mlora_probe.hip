@@ -18,6 +18,13 @@
 //                          contiguous 32 KB; units in the hardware's block
 //                          order or each XCD on a contiguous eighth; plain or
 //                          non-temporal loads and stores.
+//   mlora_probe_stream     a launch shaped like the decode fold with no
+//                          dependent load: `units` workgroups, each reading
+//                          its own region of weight bytes and
+//                          reading-modifying-writing its own region of row
+//                          bytes, requested at kernel start; replayed in a
+//                          HIP graph over rotated buffers. The floor of what
+//                          one launch of those bytes can take.
 //
 // Each entry point allocates and frees its own buffers, synchronizes the
 // device and returns 0, or a HIP error code.
@@ -128,6 +135,38 @@ __global__ __launch_bounds__(256) void rmw_kernel(char* buf) {
   for (int i = 0; i < 8; ++i) v[i] = rmw_ld<AUX>(r, off[i]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) rmw_st<AUX>(r, off[i], v[i] + u32x4{1u, 1u, 1u, 1u});
+}
+
+// Stream probe: workgroup b reads w16 pieces of 16 bytes per thread of
+// weights (its own region, 4 KB per workgroup instruction) and
+// reads-modifies-writes r16 pieces per thread of rows (its own region), all
+// loads issued before any use; pieces past the counts lie past the buffers
+// (the resource's size), so they read 0 and their stores are dropped.
+constexpr int kStreamMax = 16;  // pieces per thread of each kind (64 KB a workgroup)
+constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
+
+__global__ __launch_bounds__(256) void stream_kernel(const char* w, char* rows, unsigned* sink,
+                                                     int w16, int r16, uint32_t wbytes,
+                                                     uint32_t rbytes) {
+  const uint32_t t16 = threadIdx.x * 16u;
+  const rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(w), 0, (int)wbytes,
+                                                      0x00020000);
+  const rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(rows, 0, (int)rbytes, 0x00020000);
+  const uint32_t wb = blockIdx.x * (uint32_t)w16 * 4096u, rb = blockIdx.x * (uint32_t)r16 * 4096u;
+  u32x4 wv[kStreamMax], rv[kStreamMax];
+#pragma unroll
+  for (int i = 0; i < kStreamMax; ++i)
+    wv[i] = rmw_ld<0>(rw, i < w16 ? wb + i * 4096u + t16 : kPastEnd);
+#pragma unroll
+  for (int i = 0; i < kStreamMax; ++i)
+    rv[i] = rmw_ld<2>(rr, i < r16 ? rb + i * 4096u + t16 : kPastEnd);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < kStreamMax; ++i) acc ^= wv[i];
+#pragma unroll
+  for (int i = 0; i < kStreamMax; ++i)
+    rmw_st<2>(rr, i < r16 ? rb + i * 4096u + t16 : kPastEnd, rv[i] + acc);
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) sink[threadIdx.x] = acc.x;
 }
 
 // The first failing call's code is kept; later calls are skipped.
@@ -290,5 +329,71 @@ extern "C" int32_t mlora_probe_rmw(int32_t pattern, int32_t xcd_contiguous, int3
   if (e1) (void)hipEventDestroy(e1);
   for (char* b : bufs)
     if (b) (void)hipFree(b);
+  return (int32_t)st.rc;
+}
+
+// units: workgroups (1 .. 4096); w_kb / r_kb: weight and row kilobytes per
+// workgroup, multiples of 4 up to 64; copies: rotated buffer sets (1 .. 64);
+// us: mean microseconds per launch over `iters` launches (1 .. 4096)
+// replayed in one HIP graph.
+extern "C" int32_t mlora_probe_stream(int32_t units, int32_t w_kb, int32_t r_kb,
+                                      int32_t copies, int32_t iters, float* us) {
+  if (units < 1 || units > 4096 || w_kb < 0 || w_kb > 4 * kStreamMax || w_kb % 4 || r_kb < 0 ||
+      r_kb > 4 * kStreamMax || r_kb % 4 || copies < 1 || copies > 64 || iters < 1 ||
+      iters > 4096 || !us)
+    return (int32_t)hipErrorInvalidValue;
+  const int w16 = w_kb / 4, r16 = r_kb / 4;
+  const size_t wbytes = (size_t)units * w_kb * 1024 + 4096;
+  const size_t rbytes = (size_t)units * r_kb * 1024 + 4096;
+  std::vector<char*> wbuf(copies, nullptr), rbuf(copies, nullptr);
+  unsigned* sink = nullptr;
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  Status st;
+  st(hipMalloc(&sink, 256 * sizeof(unsigned)));
+  for (int i = 0; st.ok() && i < copies; ++i) {
+    st(hipMalloc(&wbuf[i], wbytes));
+    if (st.ok()) st(hipMemset(wbuf[i], i, wbytes));
+    if (st.ok()) st(hipMalloc(&rbuf[i], rbytes));
+    if (st.ok()) st(hipMemset(rbuf[i], 0, rbytes));
+  }
+  if (st.ok()) st(hipStreamCreate(&s));
+  if (st.ok()) st(hipEventCreate(&e0));
+  if (st.ok()) st(hipEventCreate(&e1));
+  if (st.ok()) st(hipDeviceSynchronize());
+  if (st.ok()) {
+    st(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    if (st.ok()) {
+      for (int i = 0; i < iters; ++i)
+        hipLaunchKernelGGL(stream_kernel, dim3(units), dim3(256), 0, s, wbuf[i % copies],
+                           rbuf[i % copies], sink, w16, r16, (uint32_t)wbytes, (uint32_t)rbytes);
+      st(hipStreamEndCapture(s, &graph));
+    }
+  }
+  if (st.ok()) st(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+  if (st.ok()) {
+    float ms = 0.f;
+    st(hipGraphLaunch(exec, s));
+    st(hipStreamSynchronize(s));
+    st(hipEventRecord(e0, s));
+    st(hipGraphLaunch(exec, s));
+    st(hipEventRecord(e1, s));
+    st(hipEventSynchronize(e1));
+    st(hipEventElapsedTime(&ms, e0, e1));
+    *us = ms * 1e3f / (float)iters;
+  }
+  st(hipGetLastError());
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (s) (void)hipStreamDestroy(s);
+  for (char* b : wbuf)
+    if (b) (void)hipFree(b);
+  for (char* b : rbuf)
+    if (b) (void)hipFree(b);
+  if (sink) (void)hipFree(sink);
   return (int32_t)st.rc;
 }

@@ -189,7 +189,7 @@ def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
-    """libmlora_probe.so (bench.py --probes) exports its three probes, and
+    """libmlora_probe.so (bench.py --probes) exports its four probes, and
     each rejects invalid arguments before any device call (so this runs on
     CPU)."""
     import ctypes
@@ -212,3 +212,10 @@ def test_probe_library_exports_and_rejects_bad_arguments():
                  (0, 0, 0, 0, 10), (0, 0, 0, 17, 10), (0, 0, 0, 10, 0)):
         assert lib.mlora_probe_rmw(*args, ctypes.byref(us)) != 0, args
     assert lib.mlora_probe_rmw(0, 0, 0, 10, 10, None) != 0
+    lib.mlora_probe_stream.restype = ctypes.c_int32
+    lib.mlora_probe_stream.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p]
+    for args in ((0, 4, 4, 8, 8), (4097, 4, 4, 8, 8), (8, 2, 4, 8, 8), (8, 68, 4, 8, 8),
+                 (8, 4, -4, 8, 8), (8, 4, 4, 0, 8), (8, 4, 4, 65, 8), (8, 4, 4, 8, 0),
+                 (8, 4, 4, 8, 4097)):
+        assert lib.mlora_probe_stream(*args, ctypes.byref(us)) != 0, args
+    assert lib.mlora_probe_stream(8, 4, 4, 8, 8, None) != 0
