@@ -1212,7 +1212,7 @@ constexpr int kResSteps = 8;  // k steps, and column steps, per wave
 // the library is built with kernel-argument preloading, so they arrive in
 // SGPRs and the table-cell loads issue without waiting for the argument
 // block (measured 0.3 us per call on the decode down projection).
-template <int NB, bool FULL_R>
+template <int NB, bool FULL_R, int PER>
 __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
     const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
     const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
@@ -1237,7 +1237,7 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
   const rsrc_t r_map = make_buf(p.row_adapter, (uint32_t)p.n_tokens * 4u);
   const int start = rs * p.scan_len;
   const int end = min(start + p.scan_len, p.n_slots);
-  constexpr int kPer = kScanMax / kThreads;
+  constexpr int kPer = PER;  // routing rounds: rows of the slice / kThreads, rounded up
   const int rounds = (end - start + kThreads - 1) / kThreads;
   int iv[kPer], mv[kPer];
 #pragma unroll
@@ -2349,10 +2349,22 @@ void dispatch_gather_two(const GatherArgs& g1, const GatherArgs& g2, hipStream_t
   }
 }
 
+template <int NB, bool FULL_R, int PER>
+void launch_resident_per(const GatherArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER>), dim3(grid), dim3(kThreads), 0, s,
+                     LEAD_ARGS(a, a.ns_count));
+}
+
+// The routing rounds the slice needs (scan_len rows, kThreads a round),
+// rounded up to 1, 2, 4 or 8: rounds past the slice would still issue their
+// (out-of-range) loads.
 template <int NB, bool FULL_R>
 void launch_resident(const GatherArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R>), dim3(grid), dim3(kThreads), 0, s,
-                     LEAD_ARGS(a, a.ns_count));
+  const int rounds = (a.scan_len + kThreads - 1) / kThreads;
+  if (rounds <= 1) return launch_resident_per<NB, FULL_R, 1>(a, grid, s);
+  if (rounds <= 2) return launch_resident_per<NB, FULL_R, 2>(a, grid, s);
+  if (rounds <= 4) return launch_resident_per<NB, FULL_R, 4>(a, grid, s);
+  launch_resident_per<NB, FULL_R, kScanMax / kThreads>(a, grid, s);
 }
 
 template <int NB, int MB>
