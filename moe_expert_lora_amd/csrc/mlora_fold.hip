@@ -648,7 +648,7 @@ struct GatherArgs {
 // The one-kernel gather fold of work unit u (an expert's row slice and column
 // slice) of the call `p`; all threads of the workgroup call it with the same
 // unit.
-template <int NB, int MB, bool FULL_R, bool MULTI = false>
+template <int NB, int MB, bool FULL_R, bool MULTI = false, int PER = kScanMax / kThreads>
 __device__ __forceinline__ void gather_fold_unit(const uint64_t* __restrict__ a_table,
                                                  const uint64_t* __restrict__ b_table,
                                                  const float* __restrict__ scale_table, int u,
@@ -674,7 +674,7 @@ __device__ __forceinline__ void gather_fold_unit(const uint64_t* __restrict__ a_
   const rsrc_t r_map = make_buf(p.row_adapter, (uint32_t)p.n_tokens * 4u);
   const int start = rs * p.scan_len;
   const int end = min(start + p.scan_len, p.n_slots);
-  constexpr int kPer = kScanMax / kThreads;
+  constexpr int kPer = PER;  // routing rounds of the slice, rounded up to 4 or 8
   const int rounds = (end - start + kThreads - 1) / kThreads;  // wave-uniform, <= kPer
   int iv[kPer], mv[kPer];
 #pragma unroll
@@ -722,7 +722,7 @@ __device__ __forceinline__ void gather_fold_unit(const uint64_t* __restrict__ a_
                               min(16 * MB, n - c), n_lo, n_hi, s_part);
 }
 
-template <int NB, int MB, bool FULL_R, bool MULTI = false>
+template <int NB, int MB, bool FULL_R, bool MULTI = false, int PER = kScanMax / kThreads>
 __global__ __launch_bounds__(kThreads) void gather_fold_kernel(
     const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
     const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
@@ -731,7 +731,7 @@ __global__ __launch_bounds__(kThreads) void gather_fold_kernel(
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int u = xcd * per_xcd + slot;
   if (u >= units) return;
-  gather_fold_unit<NB, MB, FULL_R, MULTI>(a_table, b_table, scale_table, u, per_e, inner, p);
+  gather_fold_unit<NB, MB, FULL_R, MULTI, PER>(a_table, b_table, scale_table, u, per_e, inner, p);
 }
 
 
@@ -1440,14 +1440,15 @@ __device__ __forceinline__ int set_member(const GatherSet& s, int u) {
     default: { const GatherArgs& g = s.a[3]; BODY(3); break; } \
   }
 
-template <int NB, int MB, bool FULL_R>
+template <int NB, int MB, bool FULL_R, int PER>
 __global__ __launch_bounds__(kThreads) void gather_fold_set_kernel(GatherSet s) {
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int u = xcd * s.per_xcd + slot;
   if (u >= s.total) return;
 #define MLORA_FOLD_BODY(m)                                                              \
-  gather_fold_unit<NB, MB, FULL_R>(g.a_table, g.b_table, g.scale_table, u - s.first[m], \
-                                   g.rs_count * g.ns_count, g.ns_count, g)
+  gather_fold_unit<NB, MB, FULL_R, false, PER>(g.a_table, g.b_table, g.scale_table,  \
+                                               u - s.first[m],                          \
+                                               g.rs_count * g.ns_count, g.ns_count, g)
   MLORA_SET_DISPATCH(MLORA_FOLD_BODY)
 #undef MLORA_FOLD_BODY
 }
@@ -2256,14 +2257,24 @@ int ns_cols_for(int N, int ns) {
   (a).a_table, (a).b_table, (a).scale_table, (a).per_xcd, (a).units,                    \
       (a).rs_count * (inner), (inner), (a)
 
+// Routing rounds a slice of scan_len rows needs, rounded up to 4 or 8: the
+// kernels issue every round's loads, those past the slice out of range.
+constexpr int scan_rounds(int scan_len) { return scan_len <= 4 * kThreads ? 4 : 8; }
+
+template <int NB, int MB, bool MULTI, int PER>
+void launch_gather_per(const GatherArgs& a, int grid, hipStream_t s) {
+  if (whole_chunks(a.R))
+    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, true, MULTI, PER>), dim3(grid), dim3(kThreads),
+                       0, s, LEAD_ARGS(a, a.ns_count));
+  else
+    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, false, MULTI, PER>), dim3(grid),
+                       dim3(kThreads), 0, s, LEAD_ARGS(a, a.ns_count));
+}
+
 template <int NB, int MB>
 void launch_gather(const GatherArgs& a, int grid, hipStream_t s) {
-  if (whole_chunks(a.R))
-    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, true>), dim3(grid), dim3(kThreads), 0, s,
-                       LEAD_ARGS(a, a.ns_count));
-  else
-    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, false>), dim3(grid), dim3(kThreads), 0, s,
-                       LEAD_ARGS(a, a.ns_count));
+  if (scan_rounds(a.scan_len) == 4) return launch_gather_per<NB, MB, false, 4>(a, grid, s);
+  launch_gather_per<NB, MB, false, 8>(a, grid, s);
 }
 
 // Rank blocks of 16 -> (NB, MB) instantiation. `small` picks one 16-row block
@@ -2681,8 +2692,14 @@ namespace {
 
 template <int NB, int MB, bool FULL_R>
 void launch_fold_set(const GatherSet& gs, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gather_fold_set_kernel<NB, MB, FULL_R>), dim3(grid), dim3(kThreads), 0, s,
-                     gs);
+  int scan = 0;
+  for (int i = 0; i < gs.n; ++i) scan = gs.a[i].scan_len > scan ? gs.a[i].scan_len : scan;
+  if (scan_rounds(scan) == 4)
+    hipLaunchKernelGGL((gather_fold_set_kernel<NB, MB, FULL_R, 4>), dim3(grid), dim3(kThreads), 0,
+                       s, gs);
+  else
+    hipLaunchKernelGGL((gather_fold_set_kernel<NB, MB, FULL_R, 8>), dim3(grid), dim3(kThreads), 0,
+                       s, gs);
 }
 
 template <bool FULL_R>
@@ -2794,12 +2811,8 @@ namespace {
 
 template <int NB, int MB>
 void launch_gather_multi(const GatherArgs& a, int grid, hipStream_t s) {
-  if (whole_chunks(a.R))
-    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, true, true>), dim3(grid), dim3(kThreads), 0,
-                       s, LEAD_ARGS(a, a.ns_count));
-  else
-    hipLaunchKernelGGL((gather_fold_kernel<NB, MB, false, true>), dim3(grid), dim3(kThreads), 0,
-                       s, LEAD_ARGS(a, a.ns_count));
+  if (scan_rounds(a.scan_len) == 4) return launch_gather_per<NB, MB, true, 4>(a, grid, s);
+  launch_gather_per<NB, MB, true, 8>(a, grid, s);
 }
 
 // The streaming one-kernel gather with multi-adapter cells (the decode
