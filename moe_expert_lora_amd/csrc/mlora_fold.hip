@@ -1212,7 +1212,7 @@ constexpr int kResSteps = 8;  // k steps, and column steps, per wave
 // the library is built with kernel-argument preloading, so they arrive in
 // SGPRs and the table-cell loads issue without waiting for the argument
 // block (measured 0.3 us per call on the decode down projection).
-template <int NB, bool FULL_R, int PER>
+template <int NB, bool FULL_R, int PER, int KS>
 __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
     const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
     const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
@@ -1271,9 +1271,9 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
   // after the first chunk's x rows: it is not needed before the shrink is
   // done, and requesting it here would hold up the scan behind three times as
   // many loads.
-  u32x4 av[kResSteps][NB];
+  u32x4 av[KS][NB];
 #pragma unroll
-  for (int u = 0; u < kResSteps; ++u) {
+  for (int u = 0; u < KS; ++u) {
     const int s = wave_step(wave, u);
     const int k0 = s * 32 + g * 8;
     const bool kin = s < nks && k0 < K;
@@ -1312,9 +1312,9 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
     const bool valid = t >= 0;
     const uint32_t xoff = (uint32_t)(valid ? t : 0) * (uint32_t)p.x_ld * 2u;
     const uint32_t ooff = (uint32_t)r * (uint32_t)p.out_ld * 2u;
-    u32x4 xv[kResSteps], ov[kResSteps];
+    u32x4 xv[KS], ov[kResSteps];
 #pragma unroll
-    for (int u = 0; u < kResSteps; ++u) {
+    for (int u = 0; u < KS; ++u) {
       const int s = wave_step(wave, u);
       const int k0 = s * 32 + g * 8;
       xv[u] = bld16(bf.x, (valid && s < nks && k0 < K) ? xoff + 2u * k0 : kOOB);
@@ -1347,7 +1347,7 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
 #pragma unroll
     for (int b = 0; b < NB; ++b) hacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < kResSteps; ++u) {
+    for (int u = 0; u < KS; ++u) {
       if (wave_step(wave, u) < nks) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) hacc[b] = mfma16x16x32(as_bf(av[u][b]), as_bf(xv[u]), hacc[b]);
@@ -2362,8 +2362,14 @@ void dispatch_gather_two(const GatherArgs& g1, const GatherArgs& g2, hipStream_t
 
 template <int NB, bool FULL_R, int PER>
 void launch_resident_per(const GatherArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER>), dim3(grid), dim3(kThreads), 0, s,
-                     LEAD_ARGS(a, a.ns_count));
+  // k steps per wave: 6 cover k_in up to 768 (4 waves x 6 steps of 32),
+  // else every step of the register arrays
+  if ((a.K + 31) / 32 <= kWaves * 6)
+    hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER, 6>), dim3(grid), dim3(kThreads), 0,
+                       s, LEAD_ARGS(a, a.ns_count));
+  else
+    hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER, kResSteps>), dim3(grid),
+                       dim3(kThreads), 0, s, LEAD_ARGS(a, a.ns_count));
 }
 
 // The routing rounds the slice needs (scan_len rows, kThreads a round),
