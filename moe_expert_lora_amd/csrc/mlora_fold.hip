@@ -3003,6 +3003,12 @@ struct TwoPlan {
   int64_t sunits, etiles, eslices;
 };
 
+// Row blocks of a standalone shrink launch's tile: `want` (1, 2 or 4) within
+// what the rank's kernels take (4 up to 32 ranks, 2 up to 64, else 1).
+int shrink_tile_mb(int R, int want) {
+  return (want >= 4 && kernel_nb(R) <= 2) ? 4 : (want >= 2 && kernel_nb(R) <= 4 ? 2 : 1);
+}
+
 TwoPlan two_plan(int R, int N, int64_t rows, bool pipe) {
   TwoPlan t;
   // two expand row blocks per wave share each B_e fragment where the rank
@@ -3021,8 +3027,7 @@ TwoPlan two_plan(int R, int N, int64_t rows, bool pipe) {
     // chunks up to 64, and always its default shrink tile
     t.emb = (t.emb >= 2 && small_full) ? 2 : 1;
   } else {
-    const int w = ov(overrides().shrink_mb, t.smb);
-    t.smb = (w >= 4 && kernel_nb(R) <= 2) ? 4 : (w >= 2 && kernel_nb(R) <= 4 ? 2 : 1);
+    t.smb = shrink_tile_mb(R, ov(overrides().shrink_mb, t.smb));
   }
   t.sunits = (rows + 16 * t.smb - 1) / (16 * t.smb);
   t.etiles = (rows + 16 * t.emb - 1) / (16 * t.emb);
@@ -3477,7 +3482,16 @@ static int32_t grouped_down_all_impl(const mlora_expert_route* route, const void
   const int cw = plan.cw, emb = plan.emb;
   int64_t nb = 0;
   GroupedArgs first = window(0, false, &nb);
-  dispatch_shrink(first, (int)nb, s, two_plan(R, N, win_rows, true).smb);
+  {
+    // the first shrink runs alone: its tile may differ from the pipe kernel's
+    const int fmb = shrink_tile_mb(R, ov(overrides().shrink_mb, plan.smb));
+    const int64_t rows0 = first.row_end - first.row_offset;
+    const int64_t units = (rows0 + 16 * fmb - 1) / (16 * fmb);
+    first.units = (int32_t)units;
+    first.per_xcd = (int32_t)((units + kXcds - 1) / kXcds);
+    nb = (int64_t)first.per_xcd * kXcds;
+    dispatch_shrink(first, (int)nb, s, fmb);
+  }
   if (int32_t rc = launched(who)) return rc;
   for (int64_t w = 1; w < n_win; ++w) {
     int64_t sb = 0, eb = 0;

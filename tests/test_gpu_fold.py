@@ -350,7 +350,8 @@ def test_grouped_two_kernel_equals_one_kernel(label):
 def test_grouped_launch_shapes_give_the_same_bits(label, overrides):
     """Shrink tiles of 16, 32 or 64 rows and expand waves of 16 or 32 rows
     (MLORA_SHRINK_MB / MLORA_EXPAND_MB) change which workgroup computes a row,
-    not how: every shape gives the bits of the default per-window call."""
+    not how: every shape gives the bits of the default per-window call, and
+    every first-shrink tile of the all-windows call the bits of its default."""
     _need_gpu()
     from staging import DeviceCase
     if label in workloads.WORKLOADS:
@@ -364,6 +365,15 @@ def test_grouped_launch_shapes_give_the_same_bits(label, overrides):
         overrides.set("MLORA_EXPAND_MB", emb)
         got = dev.run(two_kernel=True, pipelined=False)
         assert np.array_equal(ref.view(np.uint8), got.view(np.uint8)), (smb, emb)
+    # the all-windows call's first shrink runs alone and takes the shrink tile
+    # override too
+    overrides.delete("MLORA_EXPAND_MB")
+    overrides.delete("MLORA_SHRINK_MB")
+    pipe_ref = dev.run(two_kernel=True, pipelined=True)
+    for smb in ("1", "2"):
+        overrides.set("MLORA_SHRINK_MB", smb)
+        got = dev.run(two_kernel=True, pipelined=True)
+        assert np.array_equal(pipe_ref.view(np.uint8), got.view(np.uint8)), ("first shrink", smb)
 
 
 GATHER_SMALL = [s[0] for s in SMALL if s[1]["kind"] == "gather" and s[1].get("dtype") != "f32"]
