@@ -281,6 +281,12 @@ SMALL = [
     ("gather_f32_r24", dict(kind="gather", n_seq=9, padded_n=11, top_k=3, n_route=6, k_in=48,
                             n_out=40, max_rank=24, dtype="f32", skip_seqs=1,
                             wild_index_frac=0.1)),
+    # hidden sizes of large MoE layers: a long k (streaming kernels, k split
+    # over many steps) and a wide n (many column slices)
+    ("gather_k7168", dict(kind="gather", n_seq=24, padded_n=26, top_k=8, n_route=16,
+                          k_in=7168, n_out=2048, max_rank=16, skip_seqs=2)),
+    ("gather_n7168_r64", dict(kind="gather", n_seq=20, padded_n=20, top_k=8, n_route=12,
+                              k_in=2048, n_out=7168, max_rank=64)),
     ("grouped_zipf_r32", dict(kind="grouped", stream_lens=[130, 0, 77, 300], top_k=6,
                               n_route=20, k_in=192, n_out=320, max_rank=32, routing="zipf",
                               n_unadapted=3, cap=100, stream_slot_values=[1, 1, -1, 1])),
@@ -293,6 +299,10 @@ SMALL = [
                               k_in=320, n_out=200, max_rank=100, cap=150)),
     ("grouped_r128", dict(kind="grouped", stream_lens=[100], top_k=2, n_route=3, k_in=128,
                           n_out=256, max_rank=128, cap=64)),
+    ("grouped_k7168", dict(kind="grouped", stream_lens=[200, 90], top_k=8, n_route=20,
+                           k_in=7168, n_out=1024, max_rank=32, cap=1000)),
+    ("grouped_n7168", dict(kind="grouped", stream_lens=[150], top_k=6, n_route=16, k_in=512,
+                           n_out=7168, max_rank=16, cap=400)),
     ("grouped_f32", dict(kind="grouped", stream_lens=[20, 9], top_k=3, n_route=7, k_in=40,
                          n_out=48, max_rank=12, dtype="f32", n_unadapted=2, cap=30)),
 ]

@@ -1,9 +1,10 @@
 """GPU parity over a seeded sweep of shapes, through every launch form.
 
 Each case draws its sizes from its seed (k_in and n_out multiples of 8 from
-8 up; ranks 1 to 128; top_k 1 to 8; routes of 1 to 40 experts, one-entry
-routes included; skipped, refused and wild-index rows; slot counts that are
-not a multiple of top_k; grouped windows from a few rows up) and is folded by
+8 up to about 2000, or 8000 for the later seeds; ranks 1 to 128; top_k 1 to
+8; routes of 1 to 40 experts, one-entry routes included; skipped, refused
+and wild-index rows; slot counts that are not a multiple of top_k; grouped
+windows from a few rows up) and is folded by
 the default form and by every form the overrides can force (the grouped
 expand's two unit orders must give the same bits); multi-adapter
 cases add adapter counts, uninstalled slots and partly adapted slots. Every
@@ -21,8 +22,10 @@ from tests.test_gpu_fold import DEV, _need_gpu, check
 
 pytestmark = pytest.mark.gpu
 
-GATHER_SEEDS = list(range(32))
-GROUPED_SEEDS = list(range(16))
+# seeds past the first 32 gather / 16 grouped ones draw k_in and n_out up to
+# about 8000 (the hidden sizes of large MoE layers)
+GATHER_SEEDS = list(range(44))
+GROUPED_SEEDS = list(range(22))
 
 # forced gather forms: (label, overrides, run with a workspace)
 GATHER_FORMS = [
@@ -44,8 +47,9 @@ def gather_case(seed):
     n_route = 1 if one_entry else int(rng.integers(max(2, top_k), 41))
     n_seq = int(rng.integers(1, 65))
     padded_n = n_seq + int(rng.integers(0, 9))
-    k_in = 8 * int(rng.integers(1, 263))
-    n_out = 8 * int(rng.integers(1, 138))
+    wide = seed >= 32
+    k_in = 8 * int(rng.integers(1, 1001 if wide else 263))
+    n_out = 8 * int(rng.integers(1, 1001 if wide else 138))
     max_rank = int(rng.choice([1, 3, 8, 12, 16, 17, 24, 32, 40, 56, 64, 72, 96, 100, 128]))
     kw = dict(n_seq=n_seq, padded_n=padded_n, top_k=top_k, n_route=n_route, k_in=k_in,
               n_out=n_out, max_rank=max_rank, skip_seqs=int(rng.integers(0, max(1, n_seq // 4))),
@@ -71,7 +75,8 @@ def grouped_case(seed):
     top_k = int(rng.integers(1, 9))
     n_route = int(rng.integers(top_k, top_k + 30))
     kw = dict(stream_lens=lens, top_k=top_k, n_route=n_route,
-              k_in=8 * int(rng.integers(1, 200)), n_out=8 * int(rng.integers(1, 140)),
+              k_in=8 * int(rng.integers(1, 1001 if seed >= 16 else 200)),
+              n_out=8 * int(rng.integers(1, 1001 if seed >= 16 else 140)),
               max_rank=int(rng.choice([1, 5, 8, 16, 24, 32, 40, 48, 56, 64, 96, 128])),
               routing=str(rng.choice(["uniform", "zipf"])),
               n_unadapted=int(rng.integers(0, n_route // 2 + 1)),
