@@ -327,8 +327,9 @@ def probes():
     with the fold library): an empty launch, eager and in a HIP graph; the
     read rate of 8192 rows of 4096 bytes (a k_in = 2048 bf16 operand) in
     the folds' MFMA-operand pattern (16 rows x 64 bytes per wave
-    instruction) and row-contiguously (1 KB of one row per instruction), at
-    row strides of 4096 bytes (dense rows), 4160 and 8192; and the
+    instruction), row-contiguously (1 KB of one row per instruction) and
+    row-contiguously straight into LDS, read back there in the operand
+    pattern, at row strides of 4096 bytes (dense rows), 4160 and 8192; and the
     read-modify-write rate of a 64 MiB bf16 buffer in the grouped expand's
     wave tile, by rows and by contiguous workgroup blocks, with the units in
     block order or each XCD on a contiguous eighth, plain or non-temporal;
@@ -352,7 +353,7 @@ def probes():
         raise SystemExit(f"bench.py: mlora_probe_empty failed (HIP error {rc})")
     out = {"empty_launch_us": {"eager": eager.value, "graph": graph.value}, "read": []}
     useful = 8192 * 4096
-    for name, pattern in (("operand", 0), ("rows", 1)):
+    for name, pattern in (("operand", 0), ("rows", 1), ("rows_via_lds", 2)):
         for stride in (4096, 4160, 8192):
             us = ctypes.c_float()
             rc = lib.mlora_probe_read(pattern, stride, 12, 240, ctypes.byref(us))

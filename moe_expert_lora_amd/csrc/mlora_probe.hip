@@ -7,9 +7,11 @@
 //                          of a k_in = 2048 bf16 operand) at a given row
 //                          stride, in the access pattern of the folds' MFMA
 //                          operands (16 rows x 64 bytes per wave instruction,
-//                          step pairs completing 128-byte lines) or one row's
-//                          1 KB per wave instruction, buffers rotated past
-//                          L2 and MALL.
+//                          step pairs completing 128-byte lines), one row's
+//                          1 KB per wave instruction, or one row's 1 KB per
+//                          instruction straight into LDS and read back there
+//                          in the operand pattern; buffers rotated past L2
+//                          and MALL.
 //   mlora_probe_rmw        read-modify-write rate of a 16384 x 2048 bf16
 //                          buffer (64 MiB, the base_out of one prefill launch
 //                          group) in the grouped expand's wave tile (32 rows x
@@ -83,6 +85,41 @@ __global__ __launch_bounds__(kThreads) void read_rows_kernel(const char* x, unsi
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc ^= v[i];
+  sink[blockIdx.x * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// Same rows and the same per-lane data as read_operand_kernel, but moved in
+// 1 KB row pieces straight into LDS (buffer loads with the LDS flag: lane l
+// of an instruction lands at the instruction's LDS base + 16 l) and read
+// back by every wave in the operand layout. Rows sit 4112 bytes apart in LDS
+// so that the 16 rows of an operand read fall on different banks.
+constexpr int kLdsPitch = kRowBytes + 16;
+constexpr int kLdsBytes = 32 * kLdsPitch;
+
+__global__ __launch_bounds__(kThreads) void read_lds_kernel(const char* x, unsigned* sink,
+                                                           int stride) {
+  __shared__ __attribute__((aligned(16))) char s_x[kLdsBytes];
+  const int b = blockIdx.x, w = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 15, g = l >> 4;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(x) + (size_t)32 * b * stride, 0, 32 * stride, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int idx = i * 8 + w;  // 128 pieces of 1 KB: (row, quarter)
+    const int row = idx >> 2, q = idx & 3;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(s_x + row * kLdsPitch + q * 1024), 16,
+        row * stride + q * 1024 + 16 * l, 0, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int st = 2 * w + (t & 1) + 16 * (t >> 1);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      acc ^= *reinterpret_cast<const u32x4*>(s_x + (16 * rb + li) * kLdsPitch + 64 * st + 16 * g);
+  }
   sink[blockIdx.x * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
@@ -232,12 +269,15 @@ extern "C" int32_t mlora_probe_empty(int32_t launches, float* eager_us, float* g
   return (int32_t)st.rc;
 }
 
-// pattern 0: operand pattern, 1: row-contiguous. stride: bytes from one row
-// to the next (4096 .. 8192, a multiple of 16). us: mean microseconds per
-// launch over `iters` launches rotating over `copies` buffers.
+// pattern 0: operand pattern, 1: row-contiguous, 2: row-contiguous into
+// LDS, read back in the operand pattern (checked against pattern 0's
+// per-lane values first: hipErrorUnknown if they differ). stride: bytes
+// from one row to the next (4096 .. 8192, a multiple of 16). us: mean
+// microseconds per launch over `iters` launches rotating over `copies`
+// buffers.
 extern "C" int32_t mlora_probe_read(int32_t pattern, int32_t stride, int32_t copies,
                                     int32_t iters, float* us) {
-  if ((pattern != 0 && pattern != 1) || stride < kRowBytes || stride > 8192 || stride % 16 ||
+  if (pattern < 0 || pattern > 2 || stride < kRowBytes || stride > 8192 || stride % 16 ||
       copies < 1 || copies > 32 || iters < 1 || !us)
     return (int32_t)hipErrorInvalidValue;
   const size_t bytes = (size_t)kRows * stride;
@@ -257,11 +297,34 @@ extern "C" int32_t mlora_probe_read(int32_t pattern, int32_t stride, int32_t cop
       if (pattern == 0)
         hipLaunchKernelGGL(read_operand_kernel, dim3(256), dim3(kThreads), 0, 0,
                            bufs[i % copies], sink, stride);
-      else
+      else if (pattern == 1)
         hipLaunchKernelGGL(read_rows_kernel, dim3(256), dim3(kThreads), 0, 0, bufs[i % copies],
                            sink, stride);
+      else
+        hipLaunchKernelGGL(read_lds_kernel, dim3(256), dim3(kThreads), 0, 0, bufs[i % copies],
+                           sink, stride);
     };
-    for (int i = 0; i < 2 * copies; ++i) launch(i);
+    if (pattern == 2 && st.ok()) {
+      // the LDS route must hand every lane pattern 0's values: fill a buffer
+      // with distinct words, compare the two kernels' per-lane sinks
+      std::vector<uint32_t> words(bytes / 4);
+      for (size_t j = 0; j < words.size(); ++j) words[j] = (uint32_t)(j * 2654435761u) ^ (uint32_t)j;
+      st(hipMemcpy(bufs[0], words.data(), bytes, hipMemcpyHostToDevice));
+      const size_t n_sink = (size_t)256 * kThreads;
+      std::vector<unsigned> a(n_sink), c(n_sink);
+      if (st.ok()) {
+        hipLaunchKernelGGL(read_operand_kernel, dim3(256), dim3(kThreads), 0, 0, bufs[0], sink,
+                           stride);
+        st(hipMemcpy(a.data(), sink, n_sink * sizeof(unsigned), hipMemcpyDeviceToHost));
+      }
+      if (st.ok()) {
+        hipLaunchKernelGGL(read_lds_kernel, dim3(256), dim3(kThreads), 0, 0, bufs[0], sink,
+                           stride);
+        st(hipMemcpy(c.data(), sink, n_sink * sizeof(unsigned), hipMemcpyDeviceToHost));
+      }
+      if (st.ok() && a != c) st(hipErrorUnknown);
+    }
+    for (int i = 0; st.ok() && i < 2 * copies; ++i) launch(i);
     st(hipDeviceSynchronize());
     float ms = 0.f;
     if (st.ok()) {

@@ -202,7 +202,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     us = ctypes.c_float()
     assert lib.mlora_probe_empty(0, ctypes.byref(us), ctypes.byref(us)) != 0
     assert lib.mlora_probe_empty(10, None, None) != 0
-    for args in ((2, 4096, 12, 10), (0, 4095, 12, 10), (0, 8208, 12, 10), (0, 4100, 12, 10),
+    for args in ((3, 4096, 12, 10), (-1, 4096, 12, 10), (0, 4095, 12, 10), (0, 8208, 12, 10), (0, 4100, 12, 10),
                  (1, 4096, 0, 10), (1, 4096, 33, 10), (1, 4096, 12, 0)):
         assert lib.mlora_probe_read(*args, ctypes.byref(us)) != 0, args
     assert lib.mlora_probe_read(0, 4096, 12, 10, None) != 0
