@@ -1212,7 +1212,7 @@ constexpr int kResSteps = 8;  // k steps, and column steps, per wave
 // the library is built with kernel-argument preloading, so they arrive in
 // SGPRs and the table-cell loads issue without waiting for the argument
 // block (measured 0.3 us per call on the decode down projection).
-template <int NB, bool FULL_R, int PER, int KS>
+template <int NB, bool FULL_R, int PER, int KS, bool MULTI = false>
 __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
     const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
     const float* __restrict__ scale_table, int per_xcd, int units, int per_e, int inner,
@@ -1226,9 +1226,13 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int u0 = xcd * per_xcd + slot;
   if (u0 >= units) return;
+  // table cell of the unit: the expert, or with MULTI (tables of
+  // n_adapters x n_experts cells) adapter slot * n_experts + expert
   const int e = u0 / per_e;
   const int within = u0 - e * per_e;
   const int rs = within / inner, ns = within - rs * inner;
+  const int ad = MULTI ? e / p.n_experts : 0;
+  const int ex = e - ad * p.n_experts;
 
   const uint64_t a_addr = uniform_u64(a_table[e]), b_addr = uniform_u64(b_table[e]);
   const float scale = uniform_f32(scale_table[e]);
@@ -1291,7 +1295,7 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
   for (int i = 0; i < kPer; ++i) {
     if (i >= rounds) break;
     const int row = start + i * kThreads + (int)threadIdx.x;
-    const bool hit = row < end && iv[i] == e && mv[i] >= 0;
+    const bool hit = row < end && iv[i] == ex && (MULTI ? mv[i] == ad : mv[i] >= 0);
     const int tok = (int)udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
     wave_append(hit, row, p.x_by_row ? row : tok, &s_cnt, s_rows, s_toks, kScanMax);
   }
@@ -2360,15 +2364,15 @@ void dispatch_gather_two(const GatherArgs& g1, const GatherArgs& g2, hipStream_t
   }
 }
 
-template <int NB, bool FULL_R, int PER>
+template <int NB, bool FULL_R, int PER, bool MULTI>
 void launch_resident_per(const GatherArgs& a, int grid, hipStream_t s) {
   // k steps per wave: 6 cover k_in up to 768 (4 waves x 6 steps of 32),
   // else every step of the register arrays
   if ((a.K + 31) / 32 <= kWaves * 6)
-    hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER, 6>), dim3(grid), dim3(kThreads), 0,
-                       s, LEAD_ARGS(a, a.ns_count));
+    hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER, 6, MULTI>), dim3(grid),
+                       dim3(kThreads), 0, s, LEAD_ARGS(a, a.ns_count));
   else
-    hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER, kResSteps>), dim3(grid),
+    hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER, kResSteps, MULTI>), dim3(grid),
                        dim3(kThreads), 0, s, LEAD_ARGS(a, a.ns_count));
 }
 
@@ -2376,14 +2380,14 @@ void launch_resident_per(const GatherArgs& a, int grid, hipStream_t s) {
 // rounded up to 1, 2, 3, 4 or 8: rounds past the slice would still issue
 // their (out-of-range) loads, and each such load costs issue time (three
 // rounds instead of four: 1.5% per call on the decode down projection).
-template <int NB, bool FULL_R>
+template <int NB, bool FULL_R, bool MULTI = false>
 void launch_resident(const GatherArgs& a, int grid, hipStream_t s) {
   const int rounds = (a.scan_len + kThreads - 1) / kThreads;
-  if (rounds <= 1) return launch_resident_per<NB, FULL_R, 1>(a, grid, s);
-  if (rounds <= 2) return launch_resident_per<NB, FULL_R, 2>(a, grid, s);
-  if (rounds <= 3) return launch_resident_per<NB, FULL_R, 3>(a, grid, s);
-  if (rounds <= 4) return launch_resident_per<NB, FULL_R, 4>(a, grid, s);
-  launch_resident_per<NB, FULL_R, kScanMax / kThreads>(a, grid, s);
+  if (rounds <= 1) return launch_resident_per<NB, FULL_R, 1, MULTI>(a, grid, s);
+  if (rounds <= 2) return launch_resident_per<NB, FULL_R, 2, MULTI>(a, grid, s);
+  if (rounds <= 3) return launch_resident_per<NB, FULL_R, 3, MULTI>(a, grid, s);
+  if (rounds <= 4) return launch_resident_per<NB, FULL_R, 4, MULTI>(a, grid, s);
+  launch_resident_per<NB, FULL_R, kScanMax / kThreads, MULTI>(a, grid, s);
 }
 
 template <int NB, int MB>
@@ -2823,10 +2827,20 @@ void launch_gather_multi(const GatherArgs& a, int grid, hipStream_t s) {
   launch_gather_per<NB, MB, true, 8>(a, grid, s);
 }
 
-// The streaming one-kernel gather with multi-adapter cells (the decode
-// resident kernel keeps one adapter).
-void dispatch_gather_multi(const GatherArgs& a, int grid, hipStream_t s, bool small) {
+// The multi-adapter cells through the decode kernel (weights in registers)
+// where the plan asks for it and the wave's share fits, else through the
+// streaming one-kernel gather.
+void dispatch_gather_multi(const GatherArgs& a, int grid, hipStream_t s, bool small,
+                           bool resident) {
   const int nb = kernel_nb(a.R);
+  if (resident && gather_resident_fits(a)) {
+    if (nb <= 1) {
+      if (whole_chunks(a.R)) return launch_resident<1, true, true>(a, grid, s);
+      return launch_resident<1, false, true>(a, grid, s);
+    }
+    if (whole_chunks(a.R)) return launch_resident<2, true, true>(a, grid, s);
+    return launch_resident<2, false, true>(a, grid, s);
+  }
   if (nb <= 1) {
     if (small) return launch_gather_multi<1, 1>(a, grid, s);
     return launch_gather_multi<1, 4>(a, grid, s);
@@ -2878,9 +2892,24 @@ extern "C" int32_t mlora_gather_bgmv_multi(const mlora_multi_route* route, const
                                indices, row_adapter, n_tokens, n_slots, top_k, &plan))
     return rc;
   plan.a.n_experts = route->n_experts;
+  GatherArgs& a = plan.a;
+  if (plan.resident && kernel_nb(a.R) <= 2 && (a.K + 31) / 32 <= kWaves * kResSteps &&
+      !gather_resident_fits(a)) {
+    // column slices narrow enough for the decode kernel's registers
+    const int ncs = (a.N + kColStep - 1) / kColStep;
+    const int ns = (ncs + kWaves * kResSteps - 1) / (kWaves * kResSteps);
+    const int64_t units = (int64_t)cells * a.rs_count * ns;
+    if (units <= 0x7fffffffll / 2) {
+      a.ns_count = ns;
+      a.ns_cols = ns_cols_for(a.N, ns);
+      a.units = (int32_t)units;
+      a.per_xcd = (int32_t)((units + kXcds - 1) / kXcds);
+      plan.grid = a.per_xcd * kXcds;
+    }
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  dispatch_gather_multi(plan.a, plan.grid, s, plan.small != 0);
+  dispatch_gather_multi(a, plan.grid, s, plan.small != 0, plan.resident != 0);
   return launched(who);
 }
 

@@ -97,3 +97,21 @@ def test_multi_equals_one_single_call_per_slot(label, kw):
         ml.mlora_gather_bgmv(route, dev.x, out, dev.indices, m, c.top_k)
         torch.cuda.synchronize()
     assert np.array_equal(from_torch(out).view(np.uint16), got.view(np.uint16))
+
+
+@pytest.mark.parametrize("label,kw", CASES, ids=[c[0] for c in CASES])
+def test_multi_decode_kernel_equals_streaming_kernel(label, kw, overrides):
+    """The multi-adapter cells run through the decode kernel (weights in
+    registers) where they fit and through the streaming kernel when that one
+    is forced (MLORA_GATHER_RESIDENT=0): the same bits, and the forced form
+    meets the oracle bound on its own."""
+    from oracle.case import OracleMultiView
+    from staging import DeviceMultiCase
+    _need_gpu()
+    c = workloads.make_multi_gather_case(212, name=label, **kw)
+    view, dev = OracleMultiView(c), DeviceMultiCase(c, DEV)
+    default = dev.run()
+    overrides.set("MLORA_GATHER_RESIDENT", "0")
+    streaming = dev.run()
+    _check(view, streaming, c.base, f"multi {label} streaming")
+    assert np.array_equal(default.view(np.uint16), streaming.view(np.uint16))
