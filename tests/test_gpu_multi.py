@@ -115,3 +115,56 @@ def test_multi_decode_kernel_equals_streaming_kernel(label, kw, overrides):
     streaming = dev.run()
     _check(view, streaming, c.base, f"multi {label} streaming")
     assert np.array_equal(default.view(np.uint16), streaming.view(np.uint16))
+
+
+@pytest.mark.parametrize("label,kw", CASES[:2], ids=[c[0] for c in CASES[:2]])
+def test_multi_graph_replay_reads_routing_on_device(label, kw):
+    """The multi-adapter fold captured in a HIP graph: every replay (with eager
+    work and syncs between) equals the eager fold bit for bit, and a replay
+    after the routing, the map and one table cell are rewritten in place folds
+    by the new contents (the oracle bound on the new case)."""
+    from oracle.case import OracleMultiView
+    from staging import DeviceMultiCase, from_torch, to_torch
+    _need_gpu()
+    c = workloads.make_multi_gather_case(213, name=label, **kw)
+    dev = DeviceMultiCase(c, DEV)
+    eager = dev.run()
+    import moe_expert_lora_amd as ml
+    pristine = to_torch(c.base, "bf16", DEV)
+    base = pristine.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            ml.mlora_gather_bgmv_multi(dev.route, dev.x, base, dev.indices, dev.row_adapter,
+                                       c.top_k)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        base.copy_(pristine)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_torch(base).view(np.uint16), eager.view(np.uint16))
+    # new routing, a new map (Skip, every installed slot, one slot past them)
+    # and one live cell cleared, all written in place
+    na, ne = dev.tables_host[3], dev.tables_host[4]
+    rng = np.random.default_rng(214)
+    new_idx = rng.integers(0, ne, size=c.indices.shape, dtype=np.int64).astype(np.int32)
+    new_map = rng.integers(-1, na + 1, size=dev.row_adapter.numel()).astype(np.int32)
+    dev.indices.copy_(torch.from_numpy(new_idx))
+    dev.row_adapter.copy_(torch.from_numpy(new_map))
+    live_cell = int(np.flatnonzero(dev.tables_host[0])[0])
+    dev.a_table[live_cell] = 0
+    base.copy_(pristine)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    c2 = workloads.FoldCase(**{k: getattr(c, k) for k in c.__dataclass_fields__})
+    c2.indices = new_idx
+    view = OracleMultiView(c2)
+    view.row_adapter = new_map
+    view.a_table = list(view.a_table)
+    view.a_table[live_cell] = 0
+    _check(view, from_torch(base), c.base, f"multi {label} graph replay, new routing")
