@@ -1276,15 +1276,17 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
   // done, and requesting it here would hold up the scan behind three times as
   // many loads.
   u32x4 av[KS][NB];
+  if constexpr (!MULTI) {
 #pragma unroll
-  for (int u = 0; u < KS; ++u) {
-    const int s = wave_step(wave, u);
-    const int k0 = s * 32 + g * 8;
-    const bool kin = s < nks && k0 < K;
+    for (int u = 0; u < KS; ++u) {
+      const int s = wave_step(wave, u);
+      const int k0 = s * 32 + g * 8;
+      const bool kin = s < nks && k0 < K;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
-      av[u][b] = bld16(bf.a, (kin && rank < R) ? (uint32_t)(rank * K + k0) * 2u : kOOB);
+      for (int b = 0; b < NB; ++b) {
+        const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
+        av[u][b] = bld16(bf.a, (kin && rank < R) ? (uint32_t)(rank * K + k0) * 2u : kOOB);
+      }
     }
   }
   BFrag<NB> bw[kResSteps];
@@ -1301,6 +1303,22 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
   }
   lds_barrier();
   const int n = __builtin_amdgcn_readfirstlane(s_cnt);
+  // With several adapters many cells of a batch have no rows: their A_e is
+  // requested only once the scan has found some.
+  if constexpr (MULTI) {
+    if (n == 0) return;
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      const int s = wave_step(wave, u);
+      const int k0 = s * 32 + g * 8;
+      const bool kin = s < nks && k0 < K;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
+        av[u][b] = bld16(bf.a, (kin && rank < R) ? (uint32_t)(rank * K + k0) * 2u : kOOB);
+      }
+    }
+  }
 
   // One 16-row chunk: its x and base_out loads, shrink, k-split reduction,
   // expand and store. The first chunk runs outside the loop: a loop header
