@@ -845,3 +845,30 @@ def test_graph_replay_dense_one_entry_route():
     g.replay()
     torch.cuda.synchronize()
     assert np.array_equal(from_torch(base), c.base)
+
+
+# slice lengths on both sides of each routing-round count of the decode
+# kernel (256 rows a round; 1, 2, 3, 4 or 8 rounds) and of a second row slice
+# (2048 rows a slice)
+ROUND_EDGES = [200, 256, 257, 512, 600, 768, 769, 1024, 1100, 2048, 2056]
+
+
+@pytest.mark.parametrize("n_slots", ROUND_EDGES)
+def test_decode_kernel_routing_rounds(n_slots, overrides):
+    """The decode kernel at every routing-round count and across a second row
+    slice: the oracle bound, and the bits of the streaming kernel."""
+    _need_gpu()
+    from staging import DeviceCase
+    top_k = 8
+    n_seq = -(-n_slots // top_k)
+    case = workloads.make_gather_case(3000 + n_slots, n_seq=n_seq, padded_n=n_seq, top_k=top_k,
+                                      n_route=128, k_in=256, n_out=512, max_rank=16,
+                                      n_adapted=100, skip_seqs=max(1, n_seq // 16),
+                                      n_slots=n_slots, name=f"rounds_{n_slots}")
+    view, dev = OracleView(case), DeviceCase(case, DEV)
+    overrides.set("MLORA_GATHER_RESIDENT", "1")
+    res = dev.run(two_kernel=False)
+    check(view, res, case.base, f"rounds_{n_slots} decode kernel")
+    overrides.set("MLORA_GATHER_RESIDENT", "0")
+    stream = dev.run(two_kernel=False)
+    assert np.array_equal(res.view(np.uint16), stream.view(np.uint16))
