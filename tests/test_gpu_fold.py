@@ -872,3 +872,22 @@ def test_decode_kernel_routing_rounds(n_slots, overrides):
     overrides.set("MLORA_GATHER_RESIDENT", "0")
     stream = dev.run(two_kernel=False)
     assert np.array_equal(res.view(np.uint16), stream.view(np.uint16))
+
+
+@pytest.mark.parametrize("k_in", [8, 760, 768, 776, 1016, 1024])
+def test_decode_kernel_k_steps(k_in, overrides):
+    """The decode kernel on both sides of its k-step counts (6 steps a wave up
+    to k_in 768, 8 up to 1024): the oracle bound, and the bits of the
+    streaming kernel."""
+    _need_gpu()
+    from staging import DeviceCase
+    case = workloads.make_gather_case(3100 + k_in, n_seq=40, padded_n=44, top_k=8, n_route=64,
+                                      k_in=k_in, n_out=1032, max_rank=16, n_adapted=50,
+                                      skip_seqs=3, name=f"ksteps_{k_in}")
+    view, dev = OracleView(case), DeviceCase(case, DEV)
+    overrides.set("MLORA_GATHER_RESIDENT", "1")
+    res = dev.run(two_kernel=False)
+    check(view, res, case.base, f"ksteps_{k_in} decode kernel")
+    overrides.set("MLORA_GATHER_RESIDENT", "0")
+    stream = dev.run(two_kernel=False)
+    assert np.array_equal(res.view(np.uint16), stream.view(np.uint16))
