@@ -22,10 +22,22 @@ from tests.test_gpu_fold import DEV, _need_gpu, check
 
 pytestmark = pytest.mark.gpu
 
+
+def _extra_seeds(name):
+    """Seeds beyond the default lists, from an environment variable holding
+    `first-last` (inclusive) or one seed, for a wider run by hand."""
+    import os
+    v = os.environ.get(name, "").strip()
+    if not v:
+        return []
+    lo, _, hi = v.partition("-")
+    return list(range(int(lo), int(hi or lo) + 1))
+
+
 # seeds past the first 32 gather / 16 grouped ones draw k_in and n_out up to
 # about 8000 (the hidden sizes of large MoE layers)
-GATHER_SEEDS = list(range(44))
-GROUPED_SEEDS = list(range(22))
+GATHER_SEEDS = list(range(44)) + _extra_seeds("MLORA_SWEEP_GATHER_SEEDS")
+GROUPED_SEEDS = list(range(22)) + _extra_seeds("MLORA_SWEEP_GROUPED_SEEDS")
 
 # forced gather forms: (label, overrides, run with a workspace)
 GATHER_FORMS = [
@@ -138,7 +150,7 @@ def test_grouped_sweep_every_form(seed, overrides):
     _sentinel_run(view, dev, case, two_kernel=True, pipelined=True)
 
 
-MULTI_SEEDS = list(range(8))
+MULTI_SEEDS = list(range(8)) + _extra_seeds("MLORA_SWEEP_MULTI_SEEDS")
 
 
 def multi_case(seed):
