@@ -57,7 +57,8 @@ DEFAULT_WORKLOAD = "decode_down_gather"
 # other full-size workload (the tiny fp32 one is a parity case only)
 MEASURED = ["decode_down_gather", "prefill_grouped_down", "gateup_gather", "router_gather",
             "mixed_grouped", "decode_layer", "decode_multi_gather"]
-KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_lora_amd", "csrc", "mlora_fold.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_expert_lora_amd", "csrc", name)
+                  for name in ("mlora_fold.hip", "mlora_resident_body.inc")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOAD_TEXT = {
@@ -83,14 +84,16 @@ WORKLOAD_TEXT = {
 
 
 def kernel_hash() -> str:
-    """Hash of the kernel source's code: line comments and blank lines are
-    dropped first, so an edit of the comments keeps recorded counters valid."""
+    """Hash of the kernel sources' code (mlora_fold.hip, then the decode
+    kernel's body that it includes): line comments and blank lines are dropped
+    first, so an edit of the comments keeps recorded counters valid."""
     code = []
-    with open(KERNEL_SOURCE) as f:
-        for line in f:
-            line = line.split("//", 1)[0].rstrip()
-            if line:
-                code.append(line)
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            for line in f:
+                line = line.split("//", 1)[0].rstrip()
+                if line:
+                    code.append(line)
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 

@@ -1226,203 +1226,7 @@ __global__ __launch_bounds__(kThreads) void gather_resident_kernel(
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int u0 = xcd * per_xcd + slot;
   if (u0 >= units) return;
-  // table cell of the unit: the expert, or with MULTI (tables of
-  // n_adapters x n_experts cells) adapter slot * n_experts + expert
-  const int e = u0 / per_e;
-  const int within = u0 - e * per_e;
-  const int rs = within / inner, ns = within - rs * inner;
-  const int ad = MULTI ? e / p.n_experts : 0;
-  const int ex = e - ad * p.n_experts;
-
-  const uint64_t a_addr = uniform_u64(a_table[e]), b_addr = uniform_u64(b_table[e]);
-  const float scale = uniform_f32(scale_table[e]);
-
-  const rsrc_t r_idx = make_buf(p.indices, (uint32_t)p.n_slots * 4u);
-  const rsrc_t r_map = make_buf(p.row_adapter, (uint32_t)p.n_tokens * 4u);
-  const int start = rs * p.scan_len;
-  const int end = min(start + p.scan_len, p.n_slots);
-  constexpr int kPer = PER;  // routing rounds: rows of the slice / kThreads, rounded up
-  const int rounds = (end - start + kThreads - 1) / kThreads;
-  int iv[kPer], mv[kPer];
-#pragma unroll
-  // Loads for every round, those past the slice at an out-of-range offset:
-  // straight-line code keeps the wait before the scan exact, so it does not
-  // also wait for the weight loads issued after these.
-  for (int i = 0; i < kPer; ++i) {
-    const int row = start + i * kThreads + (int)threadIdx.x;
-    const bool in = i < rounds && row < end;
-    const uint32_t tok = udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
-    iv[i] = (int)bld4(r_idx, in ? (uint32_t)row * 4u : kOOB);
-    mv[i] = (int)bld4(r_map, in ? tok * 4u : kOOB);
-  }
-  if (a_addr == 0 || b_addr == 0) return;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int li = lane & 15, g = lane >> 4;
-  const int K = p.K, N = p.N, R = p.R;
-  const int n_lo = ns * p.ns_cols;
-  const int n_hi = min(n_lo + p.ns_cols, N);
-  const int nks = (K + 31) >> 5;
-  const int ncs = (n_hi - n_lo + kColStep - 1) / kColStep;
-  Bufs bf;
-  bf.x = make_buf(p.x, p.x_bytes);
-  bf.a = make_buf(reinterpret_cast<const void*>(a_addr), (uint32_t)(R * K) * 2u);
-  bf.b = make_buf(reinterpret_cast<const void*>(b_addr), (uint32_t)(N * R) * 2u);
-  bf.out = make_buf(p.out, p.out_bytes);
-
-  // The wave's weights. A_e is requested now, with the routing; B_e only
-  // after the first chunk's x rows: it is not needed before the shrink is
-  // done, and requesting it here would hold up the scan behind three times as
-  // many loads.
-  u32x4 av[KS][NB];
-  if constexpr (!MULTI) {
-#pragma unroll
-    for (int u = 0; u < KS; ++u) {
-      const int s = wave_step(wave, u);
-      const int k0 = s * 32 + g * 8;
-      const bool kin = s < nks && k0 < K;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
-        av[u][b] = bld16(bf.a, (kin && rank < R) ? (uint32_t)(rank * K + k0) * 2u : kOOB);
-      }
-    }
-  }
-  BFrag<NB> bw[kResSteps];
-
-  if (threadIdx.x == 0) s_cnt = 0;
-  lds_barrier();
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (i >= rounds) break;
-    const int row = start + i * kThreads + (int)threadIdx.x;
-    const bool hit = row < end && iv[i] == ex && (MULTI ? mv[i] == ad : mv[i] >= 0);
-    const int tok = (int)udiv((uint32_t)row, (uint32_t)p.top_k, p.top_k_magic);
-    wave_append(hit, row, p.x_by_row ? row : tok, &s_cnt, s_rows, s_toks, kScanMax);
-  }
-  lds_barrier();
-  const int n = __builtin_amdgcn_readfirstlane(s_cnt);
-  // With several adapters many cells of a batch have no rows: their A_e is
-  // requested only once the scan has found some.
-  if constexpr (MULTI) {
-    if (n == 0) return;
-#pragma unroll
-    for (int u = 0; u < KS; ++u) {
-      const int s = wave_step(wave, u);
-      const int k0 = s * 32 + g * 8;
-      const bool kin = s < nks && k0 < K;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int rank = (li >> 2) * 4 * NB + 4 * b + (li & 3);
-        av[u][b] = bld16(bf.a, (kin && rank < R) ? (uint32_t)(rank * K + k0) * 2u : kOOB);
-      }
-    }
-  }
-
-  // One 16-row chunk: its x and base_out loads, shrink, k-split reduction,
-  // expand and store. The first chunk runs outside the loop: a loop header
-  // merges the load counts of the paths that reach it and would make the
-  // chunk's loads wait for the weight loads still in flight.
-  auto chunk = [&](int c, bool first) {
-    const int m = c + li;
-    int t = -1, r = 0;
-    if (m < n) {
-      t = s_toks[m];
-      r = s_rows[m];
-    }
-    const bool valid = t >= 0;
-    const uint32_t xoff = (uint32_t)(valid ? t : 0) * (uint32_t)p.x_ld * 2u;
-    const uint32_t ooff = (uint32_t)r * (uint32_t)p.out_ld * 2u;
-    u32x4 xv[KS], ov[kResSteps];
-#pragma unroll
-    for (int u = 0; u < KS; ++u) {
-      const int s = wave_step(wave, u);
-      const int k0 = s * 32 + g * 8;
-      xv[u] = bld16(bf.x, (valid && s < nks && k0 < K) ? xoff + 2u * k0 : kOOB);
-    }
-    auto request_b = [&]() {
-#pragma unroll
-      for (int u = 0; u < kResSteps; ++u) {
-        const int cs = col_step(wave, u, ncs);
-        load_bfrag<NB, FULL_R>(bw[u], bf.b, R, n_lo + cs * kColStep, cs < ncs ? n_hi : 0, li,
-                               g);
-      }
-    };
-    auto request_out = [&]() {
-#pragma unroll
-      for (int u = 0; u < kResSteps; ++u) {
-        const int cs = col_step(wave, u, ncs);
-        const int col = n_lo + cs * kColStep + 8 * g;
-        ov[u] = bld16(bf.out, (valid && cs < ncs && col < n_hi) ? ooff + 2u * col : kOOB);
-      }
-    };
-    if constexpr (FULL_R) {
-      if (first) request_b();
-      request_out();
-    } else {
-      request_out();
-      if (first) request_b();
-    }
-    // shrink
-    f32x4 hacc[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) hacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < KS; ++u) {
-      if (wave_step(wave, u) < nks) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) hacc[b] = mfma16x16x32(as_bf(av[u][b]), as_bf(xv[u]), hacc[b]);
-      }
-    }
-    float* dst = s_part + ((size_t)wave * 64 + lane) * HW;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(dst + 4 * b) = hacc[b];
-    lds_barrier();
-    HOp<NB> hop;
-#pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      f32x4 h = *reinterpret_cast<const f32x4*>(s_part + (size_t)lane * HW + 4 * s);
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w)
-        h += *reinterpret_cast<const f32x4*>(s_part + ((size_t)w * 64 + lane) * HW + 4 * s);
-      const f32x4 v = scale * h;
-      const uint32_t hi01 = pack_bf16(v.x, v.y), hi23 = pack_bf16(v.z, v.w);
-      const uint32_t lo01 = pack_bf16(v.x - lo_f(hi01), v.y - hi_f(hi01));
-      const uint32_t lo23 = pack_bf16(v.z - lo_f(hi23), v.w - hi_f(hi23));
-      constexpr int CR = Chunk<NB>::kRanks;
-      const int q = (4 * s) / CR, w0 = ((4 * s) % CR) / 2;
-      hop.hi[q][w0] = hi01;
-      hop.hi[q][w0 + 1] = hi23;
-      hop.lo[q][w0] = lo01;
-      hop.lo[q][w0 + 1] = lo23;
-    }
-    // expand
-#pragma unroll
-    for (int u = 0; u < kResSteps; ++u) {
-      const int cs = col_step(wave, u, ncs);
-      if (cs < ncs) {
-        f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < Chunk<NB>::kCount; ++q) {
-          d0 = mfma_chunk(bw[u].w[0][q], hop.hi[q], d0);
-          d1 = mfma_chunk(bw[u].w[1][q], hop.hi[q], d1);
-          d0 = mfma_chunk(bw[u].w[0][q], hop.lo[q], d0);
-          d1 = mfma_chunk(bw[u].w[1][q], hop.lo[q], d1);
-        }
-        const int col = n_lo + cs * kColStep + 8 * g;
-        const u32x4 bq = ov[u];
-        const uint32_t o0 = pack_bf16(lo_f(bq.x) + d0.x, hi_f(bq.x) + d0.y);
-        const uint32_t o1 = pack_bf16(lo_f(bq.y) + d0.z, hi_f(bq.y) + d0.w);
-        const uint32_t o2 = pack_bf16(lo_f(bq.z) + d1.x, hi_f(bq.z) + d1.y);
-        const uint32_t o3 = pack_bf16(lo_f(bq.w) + d1.z, hi_f(bq.w) + d1.w);
-        bst16(bf.out, (valid && col < n_hi) ? ooff + 2u * col : kOOB, u32x4{o0, o1, o2, o3});
-      }
-    }
-    lds_barrier();  // s_part is rewritten by the next chunk
-  };
-  if (n > 0) chunk(0, true);
-  for (int c = 16; c < n; c += 16) chunk(c, false);
+#include "mlora_resident_body.inc"
 }
 
 // ---------------------------------------------------------------------------
@@ -1475,6 +1279,62 @@ __global__ __launch_bounds__(kThreads) void gather_fold_set_kernel(GatherSet s) 
 #undef MLORA_FOLD_BODY
 }
 #undef MLORA_SET_DISPATCH
+
+// The set through the decode kernel's unit (weights in registers), where
+// every member's wave share fits there: the decode kernel's body, included
+// once per member (its single-call kernel keeps its own code unchanged).
+// One rank block may take 16 k steps a wave here (k_in up to 2048).
+template <int NB, bool FULL_R, int PER, int KS>
+__global__ __launch_bounds__(kThreads) void gather_resident_set_kernel(GatherSet s) {
+  constexpr bool MULTI = false;
+  constexpr int HW = 4 * NB;
+  __shared__ float s_part[kWaves * 64 * HW];
+  __shared__ int s_rows[kScanMax];
+  __shared__ int s_toks[kScanMax];
+  __shared__ int s_cnt;
+
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = xcd * s.per_xcd + slot;
+  if (u >= s.total) return;
+  switch (set_member(s, u)) {
+    case 0: {
+      const GatherArgs& p = s.a[0];
+      const uint64_t* __restrict__ a_table = p.a_table;
+      const uint64_t* __restrict__ b_table = p.b_table;
+      const float* __restrict__ scale_table = p.scale_table;
+      const int u0 = u - s.first[0], per_e = p.rs_count * p.ns_count, inner = p.ns_count;
+#include "mlora_resident_body.inc"
+      break;
+    }
+    case 1: {
+      const GatherArgs& p = s.a[1];
+      const uint64_t* __restrict__ a_table = p.a_table;
+      const uint64_t* __restrict__ b_table = p.b_table;
+      const float* __restrict__ scale_table = p.scale_table;
+      const int u0 = u - s.first[1], per_e = p.rs_count * p.ns_count, inner = p.ns_count;
+#include "mlora_resident_body.inc"
+      break;
+    }
+    case 2: {
+      const GatherArgs& p = s.a[2];
+      const uint64_t* __restrict__ a_table = p.a_table;
+      const uint64_t* __restrict__ b_table = p.b_table;
+      const float* __restrict__ scale_table = p.scale_table;
+      const int u0 = u - s.first[2], per_e = p.rs_count * p.ns_count, inner = p.ns_count;
+#include "mlora_resident_body.inc"
+      break;
+    }
+    case 3: {
+      const GatherArgs& p = s.a[3];
+      const uint64_t* __restrict__ a_table = p.a_table;
+      const uint64_t* __restrict__ b_table = p.b_table;
+      const float* __restrict__ scale_table = p.scale_table;
+      const int u0 = u - s.first[3], per_e = p.rs_count * p.ns_count, inner = p.ns_count;
+#include "mlora_resident_body.inc"
+      break;
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // grouped (prefill) kernel
@@ -2303,6 +2163,18 @@ void launch_gather(const GatherArgs& a, int grid, hipStream_t s) {
 // per chunk, for slices that hold few rows of their expert (decode).
 // The decode fast path applies when every wave's k steps and column steps fit
 // the resident register arrays.
+// The set form of the decode kernel also takes one rank block at up to 16 k
+// steps a wave (k_in up to 2048).
+constexpr int kResStepsWide = 16;
+
+bool resident_set_fits(const GatherArgs& a) {
+  const int nb = (a.R + 15) / 16;
+  const int nks = (a.K + 31) / 32;
+  const int ncs = (a.ns_cols + kColStep - 1) / kColStep;
+  return nb <= 2 && nks <= kWaves * (nb <= 1 ? kResStepsWide : kResSteps) &&
+         ncs <= kWaves * kResSteps;
+}
+
 bool gather_resident_fits(const GatherArgs& a) {
   const int nb = (a.R + 15) / 16;
   const int nks = (a.K + 31) / 32;
@@ -2732,6 +2604,40 @@ void launch_fold_set(const GatherSet& gs, int grid, hipStream_t s) {
                        s, gs);
 }
 
+template <int NB, bool FULL_R, int PER>
+void launch_resident_set_per(const GatherSet& gs, int grid, hipStream_t s, int k_max) {
+  const int nks = (k_max + 31) / 32;
+  if (nks <= kWaves * 6)
+    hipLaunchKernelGGL((gather_resident_set_kernel<NB, FULL_R, PER, 6>), dim3(grid),
+                       dim3(kThreads), 0, s, gs);
+  else if (NB > 1 || nks <= kWaves * kResSteps)
+    hipLaunchKernelGGL((gather_resident_set_kernel<NB, FULL_R, PER, kResSteps>), dim3(grid),
+                       dim3(kThreads), 0, s, gs);
+  else
+    hipLaunchKernelGGL((gather_resident_set_kernel<1, FULL_R, PER, kResStepsWide>), dim3(grid),
+                       dim3(kThreads), 0, s, gs);
+}
+
+// The set through the decode kernel: the routing rounds of the longest
+// member's slice (3, 4 or 8) and the k steps of the longest k_in.
+template <int NB, bool FULL_R>
+void launch_resident_set(const GatherSet& gs, int grid, hipStream_t s, int scan, int k_max) {
+  const int rounds = (scan + kThreads - 1) / kThreads;
+  if (rounds <= 3) return launch_resident_set_per<NB, FULL_R, 3>(gs, grid, s, k_max);
+  if (rounds <= 4) return launch_resident_set_per<NB, FULL_R, 4>(gs, grid, s, k_max);
+  launch_resident_set_per<NB, FULL_R, kScanMax / kThreads>(gs, grid, s, k_max);
+}
+
+void dispatch_resident_set(const GatherSet& gs, int grid, hipStream_t s, int nb, bool full,
+                           int scan, int k_max) {
+  if (nb <= 1) {
+    if (full) return launch_resident_set<1, true>(gs, grid, s, scan, k_max);
+    return launch_resident_set<1, false>(gs, grid, s, scan, k_max);
+  }
+  if (full) return launch_resident_set<2, true>(gs, grid, s, scan, k_max);
+  launch_resident_set<2, false>(gs, grid, s, scan, k_max);
+}
+
 template <bool FULL_R>
 void dispatch_set(const GatherSet& gs, int grid, hipStream_t s, int nb, bool small) {
   if (nb <= 1) {
@@ -2829,6 +2735,19 @@ extern "C" int32_t mlora_gather_bgmv_set(const mlora_projection* projs, int32_t 
   }
   gs.per_xcd = (int32_t)((total + kXcds - 1) / kXcds);
   const int grid = gs.per_xcd * kXcds;
+  // the decode kernel's unit where every member with rows asks for it and fits
+  bool resident = nb <= 2;
+  int scan = 0, k_max = 0;
+  for (int32_t i = 0; i < n_proj; ++i) {
+    if (gs.a[i].units == 0) continue;
+    resident = resident && plans[i].resident != 0 && resident_set_fits(gs.a[i]);
+    scan = gs.a[i].scan_len > scan ? gs.a[i].scan_len : scan;
+    k_max = gs.a[i].K > k_max ? gs.a[i].K : k_max;
+  }
+  if (resident) {
+    dispatch_resident_set(gs, grid, s, nb, full, scan, k_max);
+    return launched(who);
+  }
   if (full)
     dispatch_set<true>(gs, grid, s, nb, small);
   else

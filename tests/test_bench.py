@@ -179,12 +179,18 @@ def test_traffic_from_scales_counters_by_the_copy(tmp_path, monkeypatch):
 
 def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
+    inc = tmp_path / "k.inc"
     src.write_text("int a;  // one\n\n// two\nint b;\n")
-    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    inc.write_text("int d;\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src), str(inc)])
     h1 = bench.kernel_hash()
     src.write_text("int a;   // changed\n// more\n\nint b;\n")
     assert bench.kernel_hash() == h1
     src.write_text("int a;\nint c;\n")
+    assert bench.kernel_hash() != h1
+    # the included body counts too
+    src.write_text("int a;  // one\n\n// two\nint b;\n")
+    inc.write_text("int e;\n")
     assert bench.kernel_hash() != h1
 
 

@@ -209,3 +209,38 @@ def test_one_entry_route_dense_slices_with_strides(x_by_row, overrides):
     assert rel <= REL_L2_TOL and ex <= 1.0, (rel, mx, ex)
     live = view.live_rows()
     assert np.array_equal(got[~live, :case.n_out], case.base[~live])
+
+
+@pytest.mark.parametrize("k_ins,rank", [((512, 768), 16), ((904, 1024), 16),
+                                        ((1536, 2048), 16), ((640, 1024), 32)],
+                         ids=["ks6", "ks8", "ks16_one_rank_block", "ks8_two_rank_blocks"])
+def test_set_through_decode_kernel_equals_streaming_set(k_ins, rank, overrides):
+    """Sets whose members fit the decode kernel's registers run through its
+    body (6, 8 or, for one rank block, 16 k steps a wave): the oracle bound
+    on every member, and the bits of the streaming set kernel
+    (MLORA_GATHER_RESIDENT=0)."""
+    import moe_expert_lora_amd as ml
+    from staging import DeviceCase, from_torch
+    from tests.test_gpu_fold import check
+    _need_gpu()
+    cases = [workloads.make_gather_case(150 + i + k, n_seq=40, padded_n=44, top_k=8, n_route=64,
+                                        k_in=k, n_out=(768, 1032)[i], max_rank=rank,
+                                        n_adapted=48, skip_seqs=3, name=f"set_k{k}")
+             for i, k in enumerate(k_ins)]
+    devs = [DeviceCase(c, DEV) for c in cases]
+
+    def run_set():
+        outs = [d.base0.clone() for d in devs]
+        projs = [ml.make_projection(d.route, d.x, o, d.indices, d.row_adapter, c.top_k)
+                 for c, d, o in zip(cases, devs, outs)]
+        ml.mlora_gather_bgmv_set(projs)
+        torch.cuda.synchronize()
+        return [from_torch(o) for o in outs]
+
+    res = run_set()
+    for c, got in zip(cases, res):
+        check(OracleView(c), got, c.base, f"{c.name} set, decode kernel")
+    overrides.set("MLORA_GATHER_RESIDENT", "0")
+    stream = run_set()
+    for c, a, b in zip(cases, res, stream):
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), c.name
