@@ -2257,13 +2257,17 @@ void dispatch_gather_two(const GatherArgs& g1, const GatherArgs& g2, hipStream_t
 template <int NB, bool FULL_R, int PER, bool MULTI>
 void launch_resident_per(const GatherArgs& a, int grid, hipStream_t s) {
   // k steps per wave: 6 cover k_in up to 768 (4 waves x 6 steps of 32),
-  // else every step of the register arrays
-  if ((a.K + 31) / 32 <= kWaves * 6)
+  // 8 up to 1024, 16 (one rank block, single-adapter calls) up to 2048
+  const int nks = (a.K + 31) / 32;
+  if (nks <= kWaves * 6)
     hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER, 6, MULTI>), dim3(grid),
                        dim3(kThreads), 0, s, LEAD_ARGS(a, a.ns_count));
-  else
+  else if (NB > 1 || MULTI || nks <= kWaves * kResSteps)
     hipLaunchKernelGGL((gather_resident_kernel<NB, FULL_R, PER, kResSteps, MULTI>), dim3(grid),
                        dim3(kThreads), 0, s, LEAD_ARGS(a, a.ns_count));
+  else
+    hipLaunchKernelGGL((gather_resident_kernel<1, FULL_R, PER, kResStepsWide, false>),
+                       dim3(grid), dim3(kThreads), 0, s, LEAD_ARGS(a, a.ns_count));
 }
 
 // The routing rounds the slice needs (scan_len rows, kThreads a round),
@@ -2299,7 +2303,7 @@ void dispatch_gather(const GatherArgs& a, int grid, hipStream_t s, bool small, b
     else launch_dense<2, 1>(a, grid, s);
     return;
   }
-  if (resident && gather_resident_fits(a)) {
+  if (resident && (gather_resident_fits(a) || (nb <= 1 && resident_set_fits(a)))) {
     if (nb <= 1) {
       if (whole_chunks(a.R)) launch_resident<1, true>(a, grid, s);
       else launch_resident<1, false>(a, grid, s);
@@ -2456,8 +2460,17 @@ int32_t plan_gather(const char* who, const mlora_expert_route* route, const void
   plan->small = ov(overrides().gather_small, rows_with_headroom(rows_per_slice) <= 16 ? 1 : 0);
   // weights held in registers when a slice is expected to hold at most two
   // 16-row blocks (and the wave's share fits)
-  plan->resident = ov(overrides().gather_resident, rows_per_slice <= 32 ? 1 : 0);
-  plan->use_resident = plan->resident != 0 && gather_resident_fits(a);
+  // One rank block at k_in 1025..2048 takes the wide form (16 k steps a wave),
+  // by default only at up to 6 rows per expert: a decode batch's gate/up call
+  // (640 rows, k_in 2048, rank 16) measured 7.35 us against 8.9 for the
+  // streaming kernel, while at 16 rows per expert the two-kernel form stays
+  // ahead (14.5 against 14.9 us).
+  const bool wide = kernel_nb(R) == 1 && !gather_resident_fits(a) && resident_set_fits(a);
+  const bool wide_ok = !wide || rows_per_e <= 6;
+  plan->resident =
+      ov(overrides().gather_resident, (rows_per_slice <= 32 && wide_ok) ? 1 : 0);
+  plan->use_resident =
+      plan->resident != 0 && (gather_resident_fits(a) || (wide && resident_set_fits(a)));
   plan->dense_mb = dense ? dense_mb : 0;
   return MLORA_OK;
 }

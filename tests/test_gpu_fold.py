@@ -606,9 +606,10 @@ def test_resident_weights_path_equals_streaming_path(label, overrides):
 @pytest.mark.parametrize("n_seq,form", [(64, "one"), (96, "one"), (128, "two")])
 def test_gather_planner_default_form(n_seq, form, overrides):
     """With a workspace, a gather whose experts average at most 6 rows (k_in
-    2048, rank 16: no register-resident form) runs as one kernel, from 7 rows
-    on as the k-split pair. The two forms add the k ranges in different orders,
-    so the default call's bits show which one ran; both pass the oracle bar."""
+    2048, rank 16) runs as one kernel (the decode kernel's wide form, whose
+    bits are the streaming kernel's), from 7 rows on as the k-split pair. The
+    two forms add the k ranges in different orders, so the default call's bits
+    show which one ran; both pass the oracle bar."""
     _need_gpu()
     from staging import DeviceCase
     case = workloads.make_gather_case(90 + n_seq, n_seq=n_seq, padded_n=n_seq, top_k=8,
@@ -618,10 +619,12 @@ def test_gather_planner_default_form(n_seq, form, overrides):
     got = dev.run()
     check(view, got, case.base, f"{case.name} default")
     forced = {}
+    overrides.set("MLORA_GATHER_RESIDENT", "0")  # the one-kernel form is the streaming one
     for f, two in (("one", "0"), ("two", "1")):
         overrides.set("MLORA_GATHER_TWO", two)
         forced[f] = dev.run()
     overrides.delete("MLORA_GATHER_TWO")
+    overrides.delete("MLORA_GATHER_RESIDENT")
     assert not np.array_equal(forced["one"], forced["two"])
     assert np.array_equal(got.view(np.uint8), forced[form].view(np.uint8))
 
