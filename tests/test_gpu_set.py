@@ -244,3 +244,64 @@ def test_set_through_decode_kernel_equals_streaming_set(k_ins, rank, overrides):
     stream = run_set()
     for c, a, b in zip(cases, res, stream):
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), c.name
+
+
+def test_set_graph_replay_reads_routing_on_device():
+    """A projection set captured in a HIP graph (members through the decode
+    kernel's body): every replay equals the eager call bit for bit, and a
+    replay after the routing, the map and one table cell of a member are
+    rewritten in place folds by the new contents."""
+    import moe_expert_lora_amd as ml
+    from staging import DeviceCase, from_torch, to_torch
+    from tests.test_gpu_fold import check
+    _need_gpu()
+    cases = [workloads.make_gather_case(160 + i, n_seq=40, padded_n=44, top_k=8, n_route=64,
+                                        k_in=(768, 2048)[i], n_out=(1032, 768)[i], max_rank=16,
+                                        n_adapted=48, skip_seqs=3, name=f"graph_set_{i}")
+             for i in range(2)]
+    devs = [DeviceCase(c, DEV) for c in cases]
+    pristine = [to_torch(c.base, "bf16", DEV) for c in cases]
+    outs = [p.clone() for p in pristine]
+    projs = [ml.make_projection(d.route, d.x, o, d.indices, d.row_adapter, c.top_k)
+             for c, d, o in zip(cases, devs, outs)]
+    ml.mlora_gather_bgmv_set(projs)
+    torch.cuda.synchronize()
+    eager = [from_torch(o) for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            ml.mlora_gather_bgmv_set(projs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for o, p in zip(outs, pristine):
+            o.copy_(p)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert np.array_equal(from_torch(o).view(np.uint16), e.view(np.uint16))
+    # member 1: new routing, a new map and one live table cell cleared, in place
+    c, d = cases[1], devs[1]
+    rng = np.random.default_rng(161)
+    new_idx = rng.integers(0, 64, size=c.indices.shape, dtype=np.int64).astype(np.int32)
+    new_map = np.where(rng.random(d.row_adapter.numel()) < 0.3, -1, 1).astype(np.int32)
+    d.indices.copy_(torch.from_numpy(new_idx))
+    d.row_adapter.copy_(torch.from_numpy(new_map))
+    live_e = int(np.flatnonzero(d.tables_host[0])[0])
+    d.a_table[live_e] = 0
+    for o, p in zip(outs, pristine):
+        o.copy_(p)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(from_torch(outs[0]).view(np.uint16), eager[0].view(np.uint16))
+    c2 = workloads.FoldCase(**{k: getattr(c, k) for k in c.__dataclass_fields__})
+    c2.indices = new_idx
+    view = OracleView(c2)
+    view.row_adapter = new_map
+    view.a_table = list(view.a_table)
+    view.a_table[live_e] = 0
+    check(view, from_torch(outs[1]), c.base, "set graph replay, new routing")
